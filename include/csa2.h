@@ -1,0 +1,228 @@
+/*
+ * csa2.h -- C-ABI of the CSA2 decode hot path on AMD Instinct MI355X (gfx950).
+ *
+ * CSA2 is the compressed sparse attention of a DeepSeek-V4.1-Flash-style
+ * layer.  For every query row it
+ *   1. scores each visible cached position with the lightning indexer,
+ *      I_s = sum_h w_h * ReLU(q_h . K_s), over 128-channel MXFP4 keys
+ *      ['DeepSeek-V4' paper page, section 2.3.1, index-score equation;
+ *       section 2.3.4: indexer attention in FP4];
+ *   2. keeps the 2,048 best aligned 8-position blocks (ranked by their maximum
+ *      score) as a 16,384-position candidate pool, or re-scores a given pool
+ *      in a Reindex layer, and takes the top 512 positions
+ *      ['DeepSeek V4.1 Flash architecture analysis' page, hierarchical sparse
+ *       indexer section; 'DeepSeek-V4' page, section 2.3.1, top-k selector];
+ *   3. gathers those positions' 512-channel FP4 latent entries, dequantises
+ *      them and attends with the latent as key and value (shared-KV MQA,
+ *      absorbed-MLA style), jointly with a 128-token 8-bit sliding-window
+ *      branch and an optional sink ['DeepSeek-V4' page, sections 2.3.1
+ *      "Shared Key-Value MQA" and 2.3.3; MLA article, section 4].
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; descriptor
+ *     structs (csa2_kv, csa2_rows) are HOST memory read during the call.  The
+ *     library keeps no pointer after a call returns and allocates nothing.
+ *   - `stream` is a hipStream_t (NULL: the null stream).  Work is enqueued
+ *     and the call returns without synchronising.
+ *   - Arguments are validated on the host before any launch; on error the
+ *     call returns a non-zero csa2_status, enqueues nothing and leaves the
+ *     outputs untouched; csa2_last_error() gives a message (per thread).
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Data preconditions that are not checked: inputs are finite; pool
+ *     blocks of a row are distinct, ascending and visible; idx entries are
+ *     below the row's visible count; slot ids are distinct and in range.
+ *   - All outputs are bitwise reproducible run to run.
+ *
+ * Storage formats (one "entry" = one compressed KV position)
+ *   MAIN  (latent KV, 512 ch): codes [256 B] = E2M1 pairs, channel 2j in the
+ *         low nibble of byte j; scales [32 B] = one E4M3 per 16 channels,
+ *         s = E4M3(fl32(amax/6)) rounded to nearest even, saturating at 448;
+ *         code = E2M1(fl32(x/s)) nearest even, saturating at 6.  288 B.
+ *   INDEX (indexer keys / queries, 128 ch): codes [64 B] E2M1 as above;
+ *         scales [4 B] E8M0 per 32 channels, e = floor(log2 amax) - 2
+ *         clamped to [-127, 127], code = E2M1(x * 2^-e).  68 B.
+ *   SWA   (sliding-window KV, 512 ch): codes [512 B] E4M3; scales [32 B]
+ *         E8M0 per 16 channels, e = floor(log2 amax) - 8, code =
+ *         E4M3(x * 2^-e) nearest even, saturating.  544 B.
+ * Each kind is stored as two planes (codes, scales) indexed by entry id.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
+    CSA2_ERR_SHAPE = 2,       /* inconsistent sizes or strides */
+    CSA2_ERR_RANGE = 3,       /* a size or count outside its allowed range */
+    CSA2_ERR_ALIGN = 4,       /* a pointer or stride is not aligned as required */
+    CSA2_ERR_UNSUPPORTED = 5, /* a head count or dtype this build does not handle */
+    CSA2_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+    CSA2_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} csa2_status;
+
+typedef enum { CSA2_BF16 = 0, CSA2_F32 = 1 } csa2_dtype;
+typedef enum { CSA2_MAIN_FP4 = 0, CSA2_INDEX_MXFP4 = 1, CSA2_SWA_FP8 = 2 } csa2_kind;
+
+/* Fixed constants of the method: 'candidate_topk_blocks' 2,048,
+ * 'candidate_block_size' 8, 'index_topk' 512, sliding window 128. */
+#define CSA2_LATENT 512
+#define CSA2_INDEX_DIM 128
+#define CSA2_POOL_BLOCKS 2048
+#define CSA2_BLOCK 8
+#define CSA2_TOPK 512
+#define CSA2_WINDOW 128
+#define CSA2_MAX_SELECT 2048  /* largest k csa2_select_topk accepts */
+
+/* The global (compressed) KV cache: MAIN and INDEX planes indexed by entry id.
+ *   page_entries == 0: contiguous; entry(req, pos) = req * req_stride + pos.
+ *   page_entries  > 0: paged; entry(req, pos) =
+ *        page_table[req * max_pages + pos / page_entries] * page_entries
+ *        + pos % page_entries; page_entries must be a multiple of 16.
+ * Every plane pointer must be 256-byte aligned. */
+typedef struct csa2_kv {
+    const uint8_t* main_codes;   /* [n_slots][256] (may be NULL for scoring-only calls) */
+    const uint8_t* main_scales;  /* [n_slots][32]  */
+    const uint8_t* idx_codes;    /* [n_slots][64]  (may be NULL for attention-only calls) */
+    const uint8_t* idx_scales;   /* [n_slots][4]   */
+    int64_t n_slots;             /* entries held by each plane */
+    int32_t page_entries;        /* 0 = contiguous */
+    int32_t max_pages;           /* row length of page_table */
+    const int32_t* page_table;   /* device [n_req][max_pages], paged layout only */
+    int64_t req_stride;          /* contiguous layout only */
+} csa2_kv;
+
+/* Query rows.  For decode a row is a request; for chunked prefill a row is a
+ * query token of a request, with its own visible count. */
+typedef struct csa2_rows {
+    const int32_t* req;    /* device [n_rows]: request id of each row */
+    const int32_t* n_vis;  /* device [n_rows]: visible entries, positions [0, n_vis) */
+    int32_t n_rows;
+    int32_t max_vis;       /* host: an upper bound on every n_vis (sizes the grid) */
+} csa2_rows;
+
+int csa2_abi_version(void);
+const char* csa2_status_str(csa2_status s);
+const char* csa2_last_error(void);
+
+/* ---------------------------------------------------------------- packing
+ * Quantise n rows of `src` (bf16 or fp32; row r at src + r * src_row_stride
+ * elements; 512 channels for MAIN/SWA, 128 for INDEX) and write the codes and
+ * scales of row r to entry slots[r] (slots NULL: entry r).  The write path of
+ * the cache ('890 bytes/token' section of the V4.1-Flash architecture page;
+ * quantisation after RoPE, 'KV cache diet' page).  Not part of the decode step. */
+csa2_status csa2_pack_kv(csa2_kind kind, const void* src, csa2_dtype src_dtype, int64_t n,
+                         int64_t src_row_stride, uint8_t* codes, uint8_t* scales,
+                         const int64_t* slots, void* stream);
+
+/* ---------------------------------------------------------------- indexer
+ * Lightning-indexer scores ('DeepSeek-V4' page, section 2.3.1):
+ *   q_idx [n_rows][n_idx_heads][128] (bf16 or fp32) is quantised to MXFP4 per
+ *   (row, head, 32 channels) with the INDEX rule; w [n_rows][n_idx_heads] fp32.
+ *   d_h = q_h . K_s, exact, rounded once to fp32 (nearest even);
+ *   score_s = fma-fold over h = 0 .. n_idx_heads-1 of (w_h, max(d_h, +0)),
+ *   starting from +0; -0 is returned as +0.
+ * Full scan (pool_blocks == NULL): every position s < n_vis[row].
+ *   scores [n_rows][scores_stride]: columns [0, n_vis) hold scores, columns
+ *   [n_vis, roundup(n_vis, 8)) hold -inf; scores_stride >= roundup(max_vis, 8).
+ *   block_max [n_rows][block_max_stride]: column j < ceil(n_vis/8) holds the
+ *   max over positions [8j, min(8j+8, n_vis)).  Either output may be NULL.
+ * Pool mode (Reindex; pool_blocks != NULL): only the blocks
+ *   pool_blocks[row * pool_stride + j], j < pool_count[row] (<= 2,048), are
+ *   scored; column 8j+i of `scores` holds the score of position
+ *   8*pool_blocks[..j] + i, or -inf if that position is >= n_vis.
+ *   block_max must be NULL.
+ * n_idx_heads in 1..16.  Requires kv->idx_codes / idx_scales. */
+csa2_status csa2_index_score(const csa2_kv* kv, const csa2_rows* rows,
+                             const void* q_idx, csa2_dtype q_dtype, int32_t n_idx_heads,
+                             const float* w,
+                             const int32_t* pool_blocks, int64_t pool_stride,
+                             const int32_t* pool_count,
+                             float* scores, int64_t scores_stride,
+                             float* block_max, int64_t block_max_stride,
+                             void* stream);
+
+/* ---------------------------------------------------------------- top-k
+ * Exact row-wise top-k ('DeepSeek-V4' page, section 2.3.1, top-k selector;
+ * V4.1-Flash architecture page, hierarchical sparse indexer: blocks ranked by
+ * their maximum, ties to the lower position).
+ * Row r has c_r = ceil(n_cols[r] * cols_mul / cols_div) candidate columns
+ * (n_cols NULL: max_cols), c_r <= max_cols.  Column c has id
+ *   id(c) = c                                          (pool_blocks NULL)
+ *   id(c) = 8 * pool_blocks[r * pool_stride + c/8] + c%8   (otherwise)
+ * and key keys[r * key_stride + (keys_by_id ? id(c) : c)].  Keys equal to
+ * -inf are absent.  The min(k, present) columns first in (key descending,
+ * column ascending) are selected; column order must be id order (pool blocks
+ * ascending).  Their ids are written ascending to out_ids[r * out_stride ..],
+ * the rest of the k slots get -1, and out_count[r] the number selected.
+ * 1 <= k <= 2,048; max_cols <= 2^24; cols_mul, cols_div in 1..8. */
+csa2_status csa2_select_topk(const float* keys, int64_t key_stride,
+                             const int32_t* n_cols, int32_t cols_mul, int32_t cols_div,
+                             const int32_t* pool_blocks, int64_t pool_stride, int32_t keys_by_id,
+                             int32_t n_rows, int32_t max_cols, int32_t k,
+                             int32_t* out_ids, int64_t out_stride, int32_t* out_count,
+                             void* stream);
+
+/* ---------------------------------------------------------------- attention
+ * Sparse branch ('DeepSeek-V4' page, section 2.3.1, shared-KV MQA; MLA article
+ * section 4, absorbed query):  for each row and head h,
+ *   z_j = softmax_scale * q_h . K_j over the row's selected entries
+ *   K_j = dequantised MAIN entry of position idx[row * idx_stride + j],
+ *   j < idx_count[row] (<= 512), each K_j both key and value;
+ *   o_partial[row][h][:] = sum_j softmax(z)_j K_j   (fp32),
+ *   lse[row][h] = ln sum_j exp(z_j)   (-inf and o = 0 for an empty set).
+ * q [n_rows][n_heads][512] bf16 or fp32; n_heads a multiple of 16, at most 128.
+ * workspace: csa2_sparse_attn_workspace_size(n_rows, n_heads) bytes, 256-B
+ * aligned, contents need not be initialised. */
+size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads);
+csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows,
+                             const void* q, csa2_dtype q_dtype, int32_t n_heads,
+                             const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
+                             float softmax_scale, float* o_partial, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sliding-window branch and merge ('DeepSeek-V4' page, section 2.3.3: the
+ * window's uncompressed entries join the selected entries in the same core
+ * attention; attention sink adds exp(sink_h) to the denominator):
+ *   window of row r = SWA entries swa_first[r] .. swa_first[r]+swa_count[r]-1
+ *   (swa_count <= 128) of the planes swa_codes [.][512] / swa_scales [.][32];
+ *   out[r][h][:] = joint softmax over {sparse set} + {window} (+ sink) of the
+ *   entries, obtained by merging (o_partial, lse) with the window's own
+ *   attention through their log-sum-exp.  o_partial / lse NULL: window only.
+ *   sink [n_heads] fp32 or NULL.  out may alias o_partial. */
+csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                           const int64_t* swa_first, const int32_t* swa_count, int32_t n_rows,
+                           const void* q, csa2_dtype q_dtype, int32_t n_heads, float softmax_scale,
+                           const float* sink, const float* o_partial, const float* lse,
+                           float* out, void* stream);
+
+/* ---------------------------------------------------------------- synthetic inputs
+ * Counter-based generator for seeded synthetic inputs (SplitMix64; Steele,
+ * Lea & Flood 2014): base = mix64(seed * 0x9E3779B97F4A7C15 + tensor_id),
+ * word(i) = mix64(base + (i+1) * 0x9E3779B97F4A7C15).
+ * normal: element i = bf16 (nearest even) of (sum of the twelve 16-bit
+ *   fields of words 3i..3i+2 - 393210) * 2^-16 (Irwin-Hall N(0,1)), for
+ *   elements first .. first+n-1, written as bf16 or as the same value in fp32.
+ * uniform: element i = (word(i) >> 40) * 2^-24, fp32. */
+csa2_status csa2_synth_normal(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n,
+                              csa2_dtype out_dtype, void* out, void* stream);
+csa2_status csa2_synth_uniform(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n,
+                               float* out, void* stream);
+/* Multiply rows [0, n_rows) of x [n_rows][width] fp32 by 3 where the row's
+ * position first_pos + r is boosted: word(pos) of stream (seed, boost_tensor)
+ * below 0.05 * 2^64 (about 5% of positions). */
+csa2_status csa2_synth_boost(uint64_t seed, uint32_t boost_tensor, int64_t first_pos, int64_t n_rows,
+                             int32_t width, float* x, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,197 @@
+"""Python binding of libcsa2 -- the CSA2 decode hot path on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libcsa2.so`` (see ``include/csa2.h`` for the contract of each call).
+PyTorch tensors serve as owners of device memory and as the source of the
+current HIP stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcsa2.so")
+
+BF16, F32 = 0, 1
+MAIN_FP4, INDEX_MXFP4, SWA_FP8 = 0, 1, 2
+LATENT, INDEX_DIM, POOL_BLOCKS, BLOCK, TOPK, WINDOW = 512, 128, 2048, 8, 512, 128
+
+# bytes per entry of each plane: (codes, scales)
+PLANE_BYTES = {MAIN_FP4: (256, 32), INDEX_MXFP4: (64, 4), SWA_FP8: (512, 32)}
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+class KV(ctypes.Structure):
+    _fields_ = [
+        ("main_codes", ctypes.c_void_p), ("main_scales", ctypes.c_void_p),
+        ("idx_codes", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p),
+        ("n_slots", ctypes.c_int64), ("page_entries", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32), ("page_table", ctypes.c_void_p),
+        ("req_stride", ctypes.c_int64),
+    ]
+
+
+class Rows(ctypes.Structure):
+    _fields_ = [("req", ctypes.c_void_p), ("n_vis", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int32), ("max_vis", ctypes.c_int32)]
+
+
+_lib = None
+EXPORTS = (
+    "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
+    "csa2_select_topk", "csa2_sparse_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
+    "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost",
+)
+
+
+def lib():
+    """Load libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libcsa2.so not built at {LIB_PATH}: run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.csa2_abi_version.restype = ctypes.c_int
+    L.csa2_status_str.restype = ctypes.c_char_p
+    L.csa2_status_str.argtypes = [ctypes.c_int]
+    L.csa2_last_error.restype = ctypes.c_char_p
+    L.csa2_pack_kv.argtypes = [ctypes.c_int, P, ctypes.c_int, i64, i64, P, P, P, P]
+    L.csa2_index_score.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P,
+                                   P, i64, P, P, i64, P, i64, P]
+    L.csa2_select_topk.argtypes = [P, i64, P, i32, i32, P, i64, i32, i32, i32, i32, P, i64, P, P]
+    L.csa2_sparse_attn_workspace_size.restype = ctypes.c_size_t
+    L.csa2_sparse_attn_workspace_size.argtypes = [i32, i32]
+    L.csa2_sparse_attn.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P, i64, P,
+                                   f32, P, P, P, ctypes.c_size_t, P]
+    L.csa2_swa_merge.argtypes = [P, P, i64, P, P, i32, P, ctypes.c_int, i32, f32, P, P, P, P, P]
+    L.csa2_synth_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, ctypes.c_int, P, P]
+    L.csa2_synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, P, P]
+    L.csa2_synth_boost.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, i32, P, P]
+    for name in EXPORTS:
+        if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error",
+                        "csa2_sparse_attn_workspace_size"):
+            getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != 0:
+        L = lib()
+        raise Csa2Error(fn, status, (L.csa2_last_error() or b"").decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_kv(main_codes=None, main_scales=None, idx_codes=None, idx_scales=None, n_slots=0,
+            page_entries=0, page_table=None, req_stride=0):
+    """Host descriptor of a KV cache.  It keeps references to the tensors whose
+    device pointers it holds, so they live as long as the descriptor."""
+    max_pages = 0 if page_table is None else int(page_table.shape[-1])
+    kv = KV(_ptr(main_codes), _ptr(main_scales), _ptr(idx_codes), _ptr(idx_scales), int(n_slots),
+            int(page_entries), max_pages, _ptr(page_table), int(req_stride))
+    kv._refs = (main_codes, main_scales, idx_codes, idx_scales, page_table)
+    return kv
+
+
+def make_rows(req, n_vis, max_vis):
+    """Host descriptor of the query rows (keeps its tensors alive)."""
+    rows = Rows(_ptr(req), _ptr(n_vis), int(req.shape[0]), int(max_vis))
+    rows._refs = (req, n_vis)
+    return rows
+
+
+# ------------------------------------------------------------------ entry points
+def abi_version() -> int:
+    return lib().csa2_abi_version()
+
+
+def csa2_pack_kv(kind, src, codes, scales, slots=None, stream=None):
+    n = int(src.shape[0])
+    _check("csa2_pack_kv", lib().csa2_pack_kv(kind, _ptr(src), _dtype(src), n, int(src.stride(0)),
+                                             _ptr(codes), _ptr(scales), _ptr(slots), _stream(stream)))
+
+
+def csa2_index_score(kv, rows, q_idx, w, scores=None, block_max=None, pool_blocks=None, pool_count=None,
+                     stream=None):
+    Hi = int(q_idx.shape[1])
+    _check("csa2_index_score", lib().csa2_index_score(
+        ctypes.byref(kv), ctypes.byref(rows), _ptr(q_idx), _dtype(q_idx), Hi, _ptr(w),
+        _ptr(pool_blocks), 0 if pool_blocks is None else int(pool_blocks.stride(0)), _ptr(pool_count),
+        _ptr(scores), 0 if scores is None else int(scores.stride(0)),
+        _ptr(block_max), 0 if block_max is None else int(block_max.stride(0)), _stream(stream)))
+
+
+def csa2_select_topk(keys, k, out_ids, out_count, n_cols=None, cols_mul=1, cols_div=1, pool_blocks=None,
+                     keys_by_id=False, max_cols=None, stream=None):
+    n_rows = int(out_ids.shape[0])
+    if max_cols is None:
+        max_cols = int(keys.shape[1]) if not keys_by_id else 8 * int(pool_blocks.shape[1])
+    _check("csa2_select_topk", lib().csa2_select_topk(
+        _ptr(keys), int(keys.stride(0)), _ptr(n_cols), cols_mul, cols_div, _ptr(pool_blocks),
+        0 if pool_blocks is None else int(pool_blocks.stride(0)), int(bool(keys_by_id)), n_rows,
+        int(max_cols), int(k), _ptr(out_ids), int(out_ids.stride(0)), _ptr(out_count), _stream(stream)))
+
+
+def csa2_sparse_attn_workspace_size(n_rows, n_heads) -> int:
+    return int(lib().csa2_sparse_attn_workspace_size(int(n_rows), int(n_heads)))
+
+
+def csa2_sparse_attn(kv, rows, q, idx, idx_count, softmax_scale, o_partial, lse, workspace, stream=None):
+    H = int(q.shape[1])
+    _check("csa2_sparse_attn", lib().csa2_sparse_attn(
+        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), int(idx.stride(0)),
+        _ptr(idx_count), float(softmax_scale), _ptr(o_partial), _ptr(lse), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def csa2_swa_merge(swa_codes, swa_scales, swa_first, swa_count, q, softmax_scale, out, sink=None,
+                   o_partial=None, lse=None, stream=None):
+    n_rows, H = int(q.shape[0]), int(q.shape[1])
+    _check("csa2_swa_merge", lib().csa2_swa_merge(
+        _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first), _ptr(swa_count), n_rows,
+        _ptr(q), _dtype(q), H, float(softmax_scale), _ptr(sink), _ptr(o_partial), _ptr(lse), _ptr(out),
+        _stream(stream)))
+
+
+def csa2_synth_normal(seed, tensor_id, first, out, stream=None):
+    n = int(out.numel())
+    _check("csa2_synth_normal", lib().csa2_synth_normal(int(seed), int(tensor_id), int(first), n,
+                                                        _dtype(out), _ptr(out), _stream(stream)))
+
+
+def csa2_synth_uniform(seed, tensor_id, first, out, stream=None):
+    _check("csa2_synth_uniform", lib().csa2_synth_uniform(int(seed), int(tensor_id), int(first),
+                                                          int(out.numel()), _ptr(out), _stream(stream)))
+
+
+def csa2_synth_boost(seed, tensor_id, first_pos, x, stream=None):
+    _check("csa2_synth_boost", lib().csa2_synth_boost(int(seed), int(tensor_id), int(first_pos),
+                                                      int(x.shape[0]), int(x.shape[1]), _ptr(x), _stream(stream)))

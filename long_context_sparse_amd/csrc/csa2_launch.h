@@ -1,0 +1,90 @@
+// csa2_launch.h -- internal launchers of the CSA2 kernels, called by the
+// C-ABI layer (api.cpp) after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct KvView;
+
+hipError_t launch_pack(int kind, const void* src, bool bf16, int64_t n, int64_t stride,
+                       uint8_t* codes, uint8_t* scales, const int64_t* slots, hipStream_t st);
+
+struct IndexScoreArgs {
+    const void* q_idx;
+    bool q_bf16;
+    int n_heads;
+    const float* w;
+    const int32_t* req;
+    const int32_t* n_vis;
+    int n_rows;
+    int max_vis;
+    const int32_t* pool;      // NULL: full scan
+    int64_t pool_stride;
+    const int32_t* pool_count;
+    float* scores;
+    int64_t scores_stride;
+    float* block_max;
+    int64_t block_max_stride;
+};
+hipError_t launch_index_score(const KvView& kv, const IndexScoreArgs& a, hipStream_t st);
+
+struct TopkArgs {
+    const float* keys;
+    int64_t key_stride;
+    const int32_t* n_cols;
+    int cols_mul, cols_div;
+    const int32_t* pool;
+    int64_t pool_stride;
+    bool keys_by_id;
+    int n_rows, max_cols, k;
+    int32_t* out_ids;
+    int64_t out_stride;
+    int32_t* out_count;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+struct SparseAttnArgs {
+    const void* q;
+    bool q_bf16;
+    int n_heads;
+    const int32_t* req;
+    int n_rows;
+    const int32_t* idx;
+    int64_t idx_stride;
+    const int32_t* idx_count;
+    float scale;
+    float* o;
+    float* lse;
+    float* ws;
+};
+size_t sparse_attn_workspace_bytes(int n_rows, int n_heads);
+hipError_t launch_sparse_attn(const KvView& kv, const SparseAttnArgs& a, hipStream_t st);
+
+struct SwaArgs {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const int64_t* first;
+    const int32_t* count;
+    int n_rows;
+    const void* q;
+    bool q_bf16;
+    int n_heads;
+    float scale;
+    const float* sink;
+    const float* o_in;
+    const float* lse_in;
+    float* out;
+};
+hipError_t launch_swa_merge(const SwaArgs& a, hipStream_t st);
+
+hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,
+                               void* out, hipStream_t st);
+hipError_t launch_synth_uniform(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, float* out,
+                                hipStream_t st);
+hipError_t launch_synth_boost(uint64_t seed, uint32_t tensor, int64_t first_pos, int64_t n_rows, int width,
+                              float* x, hipStream_t st);
+
+}  // namespace csa2

@@ -1,0 +1,241 @@
+"""Device-resident synthetic workloads and the decode step that runs them.
+
+Builds the caches of a configuration (synth.configs) on the GPU with the
+library's own generator and packer, then strings the five entry points
+together as one step of the hot path:
+
+  Full layer    csa2_index_score (full scan + block max)
+                -> csa2_select_topk (2,048 blocks) -> csa2_select_topk (512 positions)
+                -> csa2_sparse_attn -> csa2_swa_merge
+  Reindex layer csa2_index_score (pool) -> csa2_select_topk (512)
+                -> csa2_sparse_attn -> csa2_swa_merge
+
+('DeepSeek V4.1 Flash architecture analysis' page, hierarchical sparse
+indexer: the first Full layer scores every position and builds the pool that
+later Reindex layers re-score; 'KV cache diet' page, figure 2: layer roles.)
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import synth
+from synth.configs import Config
+
+from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_index_score, csa2_pack_kv,
+               csa2_select_topk, csa2_sparse_attn, csa2_sparse_attn_workspace_size, csa2_swa_merge,
+               csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform, make_kv, make_rows)
+
+GEN_CHUNK = 1 << 20   # entries generated per chunk
+
+
+def _planes(n, kind, dev):
+    cb, sb = {MAIN_FP4: (256, 32), INDEX_MXFP4: (64, 4), SWA_FP8: (512, 32)}[kind]
+    return (torch.empty((n, cb), dtype=torch.uint8, device=dev),
+            torch.empty((n, sb), dtype=torch.uint8, device=dev))
+
+
+def _fill_packed(kind, seed, tensor, width, logical_first, n, codes, scales, slots=None, boost=False,
+                 dev="cuda"):
+    """Generate rows logical_first .. +n of stream (seed, tensor) and pack them.
+    Row i goes to entry slots[i] (or to row i of codes/scales)."""
+    for c0 in range(0, n, GEN_CHUNK):
+        m = min(GEN_CHUNK, n - c0)
+        buf = torch.empty((m, width), dtype=torch.float32 if boost else torch.bfloat16, device=dev)
+        csa2_synth_normal(seed, tensor, (logical_first + c0) * width, buf)
+        if boost:
+            csa2_synth_boost(seed, synth.T_BOOST, logical_first + c0, buf)
+        if slots is None:
+            csa2_pack_kv(kind, buf, codes[c0:c0 + m], scales[c0:c0 + m])
+        else:
+            csa2_pack_kv(kind, buf, codes, scales, slots=slots[c0:c0 + m])
+        del buf
+
+
+class Layer:
+    """Per-layer query-side inputs and outputs of one step."""
+
+    def __init__(self, cfg: Config, n_rows: int, layer: int, swa_first_tok, dev):
+        H, Hi = cfg.heads, cfg.idx_heads
+        off = 16 * layer
+        s = cfg.seed
+        self.q = torch.empty((n_rows, H, 512), dtype=torch.bfloat16, device=dev)
+        csa2_synth_normal(s, synth.T_Q + off, 0, self.q)
+        self.q_idx = torch.empty((n_rows, Hi, 128), dtype=torch.bfloat16, device=dev)
+        csa2_synth_normal(s, synth.T_QIDX + off, 0, self.q_idx)
+        self.w = torch.empty((n_rows, Hi), dtype=torch.float32, device=dev)
+        csa2_synth_uniform(s, synth.T_W + off, 0, self.w)
+        # sliding window: the row's own 128 8-bit entries
+        n_swa = int(swa_first_tok[-1] + cfg.window) if n_rows else 0
+        self.swa_codes, self.swa_scales = _planes(max(n_swa, 1), SWA_FP8, dev)
+        _fill_packed(SWA_FP8, s, synth.T_SWA + off, 512, 0, n_swa, self.swa_codes, self.swa_scales, dev=dev)
+        self.swa_first = torch.as_tensor(np.asarray(swa_first_tok, np.int64), device=dev)
+        self.swa_count = torch.full((n_rows,), cfg.window, dtype=torch.int32, device=dev)
+        self.idx = torch.empty((n_rows, 512), dtype=torch.int32, device=dev)
+        self.idx_count = torch.empty((n_rows,), dtype=torch.int32, device=dev)
+        self.o_partial = torch.empty((n_rows, H, 512), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((n_rows, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=dev)
+
+
+class Workload:
+    """All device buffers of one configuration; ``step()`` runs the hot path."""
+
+    def __init__(self, cfg: Config, copies: int = 1, dev="cuda"):
+        self.cfg = cfg
+        self.dev = dev
+        L = cfg.lens
+        base = cfg.req_base
+        self.n_entries = int(L.sum())
+        self.sigma = 512 ** -0.5
+        # ---- rows
+        if cfg.mode == "prefill":
+            t = np.arange(cfg.prefill_tokens - cfg.prefill_rows, cfg.prefill_tokens, dtype=np.int64)
+            n_vis = t // cfg.tokens_per_entry
+            req = np.zeros(cfg.prefill_rows, np.int32)
+            swa_first = t - (cfg.window - 1) - (t[0] - (cfg.window - 1))   # row i: tokens t-127 .. t
+        else:
+            n_vis = L.copy()
+            req = np.arange(cfg.n_req, dtype=np.int32)
+            swa_first = np.arange(cfg.n_req, dtype=np.int64) * cfg.window
+        self.n_rows = len(req)
+        self.n_vis_host = n_vis.astype(np.int64)
+        self.max_vis = int(n_vis.max())
+        self.req = torch.as_tensor(req, device=dev)
+        self.n_vis = torch.as_tensor(n_vis.astype(np.int32), device=dev)
+        self.rows = make_rows(self.req, self.n_vis, self.max_vis)
+        # ---- global KV (MAIN + INDEX planes), logical entry = base[req] + pos
+        if cfg.page_entries:
+            P = cfg.page_entries
+            pages_per_req = (L + P - 1) // P
+            n_pages = int(pages_per_req.sum())
+            perm = synth.page_permutation(cfg.seed, n_pages)
+            max_pages = int(pages_per_req.max())
+            table = np.zeros((cfg.n_req, max_pages), np.int32)
+            k = 0
+            for r in range(cfg.n_req):
+                table[r, :pages_per_req[r]] = perm[k:k + pages_per_req[r]]
+                k += pages_per_req[r]
+            self.page_table_host = table
+            self.page_table = torch.as_tensor(table, device=dev)
+            n_slots = n_pages * P
+        else:
+            self.page_table_host = None
+            self.page_table = None
+            n_slots = self.n_entries
+        self.n_slots = n_slots
+        main0 = _planes(n_slots, MAIN_FP4, dev)
+        idx0 = _planes(n_slots, INDEX_MXFP4, dev)
+        self._fill_kv(main0, idx0)
+        self.kv_copies = [(main0, idx0)]
+        for _ in range(1, copies):
+            self.kv_copies.append(((main0[0].clone(), main0[1].clone()), (idx0[0].clone(), idx0[1].clone())))
+        stride = int(L.max()) if cfg.page_entries == 0 else 0
+        self.kvs = [make_kv(m[0], m[1], i[0], i[1], n_slots, cfg.page_entries, self.page_table,
+                            req_stride=stride if len(set(L.tolist())) == 1 else 0)
+                    for (m, i) in self.kv_copies]
+        if cfg.page_entries == 0 and len(set(L.tolist())) != 1:
+            raise ValueError("contiguous layout needs equal contexts")
+        # ---- layers
+        n_layers = 1 + cfg.reindex_layers
+        self.layers = [Layer(cfg, self.n_rows, li, swa_first, dev) for li in range(n_layers)]
+        # ---- intermediates
+        self.nv8 = (self.max_vis + 7) // 8 * 8
+        mode = cfg.mode
+        self.full = mode in ("full", "prefill", "mixed")
+        if self.full:
+            self.scores = torch.empty((self.n_rows, self.nv8), dtype=torch.float32, device=dev)
+            self.block_max = torch.empty((self.n_rows, self.nv8 // 8), dtype=torch.float32, device=dev)
+        if mode in ("full", "mixed", "reindex"):
+            self.pool = torch.empty((self.n_rows, 2048), dtype=torch.int32, device=dev)
+            self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
+            self.pool_scores = torch.empty((self.n_rows, 16384), dtype=torch.float32, device=dev)
+        if mode == "reindex":
+            pools = np.stack([synth.given_pool(cfg.seed, r, int(L[r]) // 8, 2048) for r in range(self.n_rows)])
+            self.pool.copy_(torch.as_tensor(pools))
+            self.pool_count.fill_(2048)
+        ws = csa2_sparse_attn_workspace_size(self.n_rows, cfg.heads)
+        self.workspace = torch.empty((ws + 255) // 256 * 256, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # --------------------------------------------------------------- setup
+    def _fill_kv(self, main, idx):
+        cfg = self.cfg
+        L = cfg.lens
+        base = cfg.req_base
+        if cfg.page_entries == 0:
+            _fill_packed(MAIN_FP4, cfg.seed, synth.T_LATENT, 512, 0, self.n_entries, main[0], main[1], dev=self.dev)
+            _fill_packed(INDEX_MXFP4, cfg.seed, synth.T_IDXKEY, 128, 0, self.n_entries, idx[0], idx[1],
+                         boost=cfg.boost, dev=self.dev)
+            return
+        P = cfg.page_entries
+        for r in range(cfg.n_req):
+            pos = np.arange(L[r], dtype=np.int64)
+            slots = self.page_table_host[r, pos // P].astype(np.int64) * P + pos % P
+            sl = torch.as_tensor(slots, device=self.dev)
+            _fill_packed(MAIN_FP4, cfg.seed, synth.T_LATENT, 512, int(base[r]), int(L[r]), main[0], main[1],
+                         slots=sl, dev=self.dev)
+            _fill_packed(INDEX_MXFP4, cfg.seed, synth.T_IDXKEY, 128, int(base[r]), int(L[r]), idx[0], idx[1],
+                         slots=sl, boost=cfg.boost, dev=self.dev)
+
+    # --------------------------------------------------------------- the step
+    def run_full(self, layer: "Layer", kv, stream=None):
+        csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.scores, block_max=self.block_max,
+                         stream=stream)
+        if self.cfg.mode == "prefill":
+            csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.n_vis,
+                             max_cols=self.max_vis, stream=stream)
+        else:
+            csa2_select_topk(self.block_max, 2048, self.pool, self.pool_count, n_cols=self.n_vis, cols_div=8,
+                             max_cols=self.nv8 // 8, stream=stream)
+            csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.pool_count, cols_mul=8,
+                             pool_blocks=self.pool, keys_by_id=True, max_cols=16384, stream=stream)
+        self._attend(layer, kv, stream)
+
+    def run_reindex(self, layer: "Layer", kv, stream=None):
+        csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.pool_scores,
+                         pool_blocks=self.pool, pool_count=self.pool_count, stream=stream)
+        csa2_select_topk(self.pool_scores, 512, layer.idx, layer.idx_count, n_cols=self.pool_count, cols_mul=8,
+                         pool_blocks=self.pool, keys_by_id=False, max_cols=16384, stream=stream)
+        self._attend(layer, kv, stream)
+
+    def _attend(self, layer, kv, stream):
+        csa2_sparse_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, self.sigma, layer.o_partial,
+                         layer.lse, self.workspace, stream=stream)
+        csa2_swa_merge(layer.swa_codes, layer.swa_scales, layer.swa_first, layer.swa_count, layer.q, self.sigma,
+                       layer.out, o_partial=layer.o_partial, lse=layer.lse, stream=stream)
+
+    def step(self, copy: int = 0, stream=None):
+        kv = self.kvs[copy % len(self.kvs)]
+        mode = self.cfg.mode
+        if mode == "reindex":
+            self.run_reindex(self.layers[0], kv, stream)
+            return
+        self.run_full(self.layers[0], kv, stream)
+        for layer in self.layers[1:]:
+            self.run_reindex(layer, kv, stream)
+
+    # --------------------------------------------------------------- bytes
+    def algorithmic_bytes(self) -> dict:
+        """Bytes the method must move per step: indexer keys scored, selected
+        main entries gathered, window entries, queries in, outputs out."""
+        cfg = self.cfg
+        H = cfg.heads
+        n_layers = len(self.layers)
+        rows = self.n_rows
+        d = {}
+        if self.full:
+            d["index_keys_full"] = int(self.n_vis_host.sum()) * 68
+        reindex_layers = n_layers - 1 if cfg.mode != "reindex" else 1
+        if reindex_layers:
+            pool_pos = int(np.minimum(self.n_vis_host, 16384).sum()) if cfg.mode != "reindex" else rows * 16384
+            d["index_keys_pool"] = reindex_layers * pool_pos * 68
+        sel = int(np.minimum(self.n_vis_host, 512).sum())
+        d["gathered_main"] = n_layers * sel * 288
+        d["swa"] = n_layers * rows * cfg.window * 544
+        d["q"] = n_layers * rows * (H * 512 * 2 + cfg.idx_heads * 128 * 2 + cfg.idx_heads * 4)
+        d["out"] = n_layers * rows * H * 512 * 4
+        d["total"] = sum(d.values())
+        return d

@@ -82,13 +82,26 @@ def uniform(seed: int, tensor_id: int, idx) -> np.ndarray:
 
 def normal(seed: int, tensor_id: int, idx) -> np.ndarray:
     """fp32 Irwin-Hall normals for element indices ``idx``."""
-    i = _u64(idx) * np.uint64(3)
-    total = np.zeros(np.shape(idx), dtype=np.int64)
-    for k in range(3):
-        w = words(seed, tensor_id, i + np.uint64(k))
-        for f in range(4):
-            total += ((w >> np.uint64(16 * f)) & np.uint64(0xFFFF)).astype(np.int64)
-    return ((total - 393210).astype(np.float64) * 2.0 ** -16).astype(np.float32)
+    base = stream_base(seed, tensor_id)
+    flat = _u64(idx).reshape(-1)
+    out = np.empty(flat.shape[0], np.float32)
+    step = 1 << 16                      # chunks stay in cache
+    with np.errstate(over="ignore"):
+        for c0 in range(0, flat.shape[0], step):
+            i3 = flat[c0:c0 + step] * np.uint64(3)
+            tot = np.zeros(i3.shape[0], np.int64)
+            for k in range(3):
+                z = (i3 + np.uint64(k + 1)) * GAMMA
+                z += base
+                z ^= z >> np.uint64(30)
+                z *= _M1
+                z ^= z >> np.uint64(27)
+                z *= _M2
+                z ^= z >> np.uint64(31)
+                # the four 16-bit fields of each word (their order does not matter)
+                tot += z.view(np.uint16).reshape(-1, 4).astype(np.int64).sum(axis=1)
+            out[c0:c0 + step] = (tot - 393210).astype(np.float64) * 2.0 ** -16
+    return out.reshape(np.shape(idx))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

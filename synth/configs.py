@@ -1,0 +1,90 @@
+"""The five synthetic workloads (shapes, seeds, structure) -- data only.
+
+Element numbering shared by every consumer (host generator, GPU generator,
+oracle): a cache entry has a *logical* id ``req_base[req] + pos`` (requests
+laid end to end); element c of a tensor row r is element ``r * width + c`` of
+that tensor's stream.  Per-layer streams add 16 * layer to the tensor id.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import ragged_lengths
+
+
+@dataclass
+class Config:
+    name: str
+    seed: int
+    n_req: int
+    heads: int = 64
+    idx_heads: int = 8
+    mode: str = "full"            # "full" | "reindex" | "prefill" | "mixed"
+    ctx: int = 0                  # entries per request (uniform contexts)
+    lengths: np.ndarray | None = None   # ragged contexts (entries)
+    page_entries: int = 0         # 0 = contiguous
+    reindex_layers: int = 0
+    boost: bool = False
+    prefill_rows: int = 0         # chunked prefill: query rows (tokens)
+    prefill_tokens: int = 0       # total tokens of the prefill context
+    tokens_per_entry: int = 1
+    window: int = 128
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def lens(self) -> np.ndarray:
+        if self.lengths is not None:
+            return np.asarray(self.lengths, np.int64)
+        return np.full(self.n_req, self.ctx, np.int64)
+
+    @property
+    def total_entries(self) -> int:
+        return int(self.lens.sum())
+
+    @property
+    def req_base(self) -> np.ndarray:
+        L = self.lens
+        return np.concatenate([[0], np.cumsum(L)[:-1]]).astype(np.int64)
+
+
+def tiny_full_decode(**kw) -> Config:
+    return Config("tiny_full_decode_4k", seed=0, n_req=1, heads=16, ctx=4096, mode="full",
+                  description="1 request, 4,096 cached entries, 16 heads, Full layer", **kw)
+
+
+def full_decode_128k(**kw) -> Config:
+    return Config("full_decode_16x128k", seed=1, n_req=16, heads=64, ctx=131072, mode="full",
+                  description="16 requests x 131,072 entries, 64 heads, Full layer", **kw)
+
+
+def reindex_decode_1m(**kw) -> Config:
+    return Config("reindex_decode_64x1m", seed=2, n_req=64, heads=64, ctx=1048576, mode="reindex",
+                  boost=True, description="64 requests x 1,048,576 entries, given 2,048-block pools, "
+                  "5% of indexer keys x3, 64 heads, Reindex layer", **kw)
+
+
+def chunked_prefill_256k(**kw) -> Config:
+    return Config("chunked_prefill_4096x131k", seed=3, n_req=1, heads=64, ctx=131072, mode="prefill",
+                  prefill_rows=4096, prefill_tokens=262144, tokens_per_entry=2,
+                  description="262,144 tokens at 2 per entry (131,072 entries); the last 4,096 tokens "
+                  "as causal query rows, 64 heads", **kw)
+
+
+def mixed_serving(**kw) -> Config:
+    seed = 4
+    return Config("mixed_serving_256req", seed=seed, n_req=256, heads=64, mode="mixed",
+                  lengths=ragged_lengths(seed, 256), page_entries=64, reindex_layers=4,
+                  description="256 requests, log-uniform contexts in [4,096, 1,048,576), 64-entry pages "
+                  "in a random page order, 1 Full + 4 Reindex layers, 64 heads", **kw)
+
+
+ALL = {
+    "c0": tiny_full_decode,
+    "c1": full_decode_128k,
+    "c2": reindex_decode_1m,
+    "c3": chunked_prefill_256k,
+    "c4": mixed_serving,
+}

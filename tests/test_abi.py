@@ -1,0 +1,112 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every entry
+point include/csa2.h declares, and rejects bad arguments on the host before
+any launch (status code + message, nothing enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_amd as lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "csa2.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = lib.lib()
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lib.EXPORTS)
+    assert L.csa2_abi_version() == 1
+
+
+def _kv(**over):
+    kv = lib.KV(256, 256, 256, 256, 1000, 0, 0, None, 1000)
+    for k, v in over.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def _rows(n=2, max_vis=100):
+    return lib.Rows(256, 512, n, max_vis)
+
+
+def test_status_strings():
+    L = lib.lib()
+    for s in range(8):
+        assert L.csa2_status_str(s)
+
+
+@pytest.mark.parametrize("k,expect", [(0, 3), (2049, 3)])
+def test_topk_rejects_k(k, expect):
+    L = lib.lib()
+    assert L.csa2_select_topk(256, 100, None, 1, 1, None, 0, 0, 4, 100, k, 256, 2048, 256, None) == expect
+    assert b"k must be" in L.csa2_last_error()
+
+
+def test_topk_rejects_shapes():
+    L = lib.lib()
+    assert L.csa2_select_topk(None, 100, None, 1, 1, None, 0, 0, 4, 100, 10, 256, 16, 256, None) == 1
+    assert L.csa2_select_topk(256, 100, None, 1, 1, None, 0, 0, 4, 100, 10, 256, 5, 256, None) == 2
+    assert L.csa2_select_topk(256, 100, None, 1, 1, None, 0, 1, 4, 100, 10, 256, 16, 256, None) == 2
+    assert L.csa2_select_topk(256, 50, None, 1, 1, None, 0, 0, 4, 100, 10, 256, 16, 256, None) == 2
+    assert L.csa2_select_topk(256, 100, None, 9, 1, None, 0, 0, 4, 100, 10, 256, 16, 256, None) == 3
+    # zero rows: nothing to do
+    assert L.csa2_select_topk(None, 0, None, 1, 1, None, 0, 0, 0, 0, 10, None, 0, None, None) == 0
+
+
+def test_pack_rejects():
+    L = lib.lib()
+    assert L.csa2_pack_kv(7, 256, 0, 4, 512, 256, 256, None, None) == 5
+    assert L.csa2_pack_kv(0, 256, 5, 4, 512, 256, 256, None, None) == 5
+    assert L.csa2_pack_kv(0, None, 0, 4, 512, 256, 256, None, None) == 1
+    assert L.csa2_pack_kv(0, 256, 0, 4, 100, 256, 256, None, None) == 2
+    assert L.csa2_pack_kv(0, 258, 0, 4, 512, 256, 256, None, None) == 4
+    assert L.csa2_pack_kv(0, 256, 0, 4, 512, 272, 256, None, None) == 4
+    assert L.csa2_pack_kv(0, 256, 0, -1, 512, 256, 256, None, None) == 3
+    assert L.csa2_pack_kv(0, None, 0, 0, 512, None, None, None, None) == 0
+
+
+def test_index_score_rejects():
+    L = lib.lib()
+    kv, rows = _kv(), _rows()
+    f = L.csa2_index_score
+    B = ctypes.byref
+    assert f(None, B(rows), 256, 0, 8, 256, None, 0, None, 256, 104, None, 0, None) == 1
+    assert f(B(kv), B(rows), 256, 0, 17, 256, None, 0, None, 256, 104, None, 0, None) == 5
+    assert f(B(kv), B(rows), 256, 0, 0, 256, None, 0, None, 256, 104, None, 0, None) == 5
+    assert f(B(kv), B(rows), 256, 0, 8, 256, None, 0, None, 256, 99, None, 0, None) == 2
+    assert f(B(kv), B(rows), 256, 0, 8, 256, None, 0, None, None, 0, None, 0, None) == 1
+    assert f(B(_kv(idx_codes=300)), B(rows), 256, 0, 8, 256, None, 0, None, 256, 104, None, 0, None) == 4
+    assert f(B(_kv(page_entries=48, page_table=256, max_pages=4)), B(rows), 256, 0, 8, 256, None, 0, None,
+             256, 104, None, 0, None) == 3
+    assert f(B(_kv(page_entries=64)), B(rows), 256, 0, 8, 256, None, 0, None, 256, 104, None, 0, None) == 1
+    # pool mode needs pool_count and forbids block_max
+    assert f(B(kv), B(rows), 256, 0, 8, 256, 256, 2048, None, 256, 16384, None, 0, None) == 1
+    assert f(B(kv), B(rows), 256, 0, 8, 256, 256, 2048, 256, 256, 16384, 256, 2048, None) == 2
+
+
+def test_attn_rejects():
+    L = lib.lib()
+    kv, rows = _kv(), _rows()
+    B = ctypes.byref
+    f = L.csa2_sparse_attn
+    ws = L.csa2_sparse_attn_workspace_size(2, 64)
+    assert ws > 0
+    assert f(B(kv), B(rows), 256, 0, 40, 256, 512, 256, ctypes.c_float(0.04), 256, 256, 256, ws, None) == 5
+    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(0.04), 256, 256, 256, ws - 1, None) == 6
+    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(-1.0), 256, 256, 256, ws, None) == 3
+    assert f(B(_kv(main_codes=None)), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(0.04), 256, 256,
+             256, ws, None) == 1
+    g = L.csa2_swa_merge
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, ctypes.c_float(0.04), None, 256, None, 256, None) == 1
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 200, ctypes.c_float(0.04), None, None, None, 256, None) == 5
+    assert g(264, 256, 10, 256, 256, 2, 256, 0, 64, ctypes.c_float(0.04), None, None, None, 256, None) == 4

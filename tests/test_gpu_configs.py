@@ -1,0 +1,76 @@
+"""End-to-end parity of the decode step on the five synthetic workloads.
+
+Each test builds the workload on the GPU (generator + packer of the HIP
+library), runs one step exactly as bench.py times it, and checks sampled rows
+against the oracle, which draws the same rows with the host generator:
+indexer scores, block maxima, the pool and the top-512 bit-exact; the
+sparse-branch output, its log-sum-exp and the merged output within
+|o - ref| <= 2e-3 + 1e-2 |ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_amd.workload import Workload
+from synth import configs
+from tests.ref import RowRef
+
+pytestmark = pytest.mark.gpu
+
+
+def tol_ok(got, ref):
+    return bool(np.all(np.abs(got - ref) <= 2e-3 + 1e-2 * np.abs(ref)))
+
+
+def check_attention(wl, layer_i, row, ref, idx):
+    o_p, lse_p, o = ref.attend(idx)
+    L = wl.layers[layer_i]
+    n = int(L.idx_count[row])
+    assert np.array_equal(L.idx[row, :n].cpu().numpy(), idx)
+    assert tol_ok(L.o_partial[row].cpu().numpy(), o_p)
+    assert np.allclose(L.lse[row].cpu().numpy(), lse_p, rtol=1e-5, atol=1e-4)
+    assert tol_ok(L.out[row].cpu().numpy(), o)
+
+
+def check_full_row(wl, row):
+    ref = RowRef(wl.cfg, row, 0)
+    scores = ref.full_scores()
+    got = wl.scores[row, :ref.n_vis].cpu().numpy()
+    assert np.array_equal(got, scores), np.nonzero(got != scores)[0][:5]
+    nb = (ref.n_vis + 7) // 8
+    import oracle
+    assert np.array_equal(wl.block_max[row, :nb].cpu().numpy(), oracle.block_max(scores))
+    pool, idx = ref.select_full(scores)
+    assert int(wl.pool_count[row]) == len(pool)
+    assert np.array_equal(wl.pool[row, :len(pool)].cpu().numpy(), pool)
+    check_attention(wl, 0, row, ref, idx)
+    return pool
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = Workload(configs.tiny_full_decode())
+    wl.step()
+    torch.cuda.synchronize()
+    return wl
+
+
+def test_tiny_full_decode(tiny):
+    check_full_row(tiny, 0)
+
+
+def test_tiny_repeatable(tiny):
+    before = tiny.layers[0].out.clone()
+    tiny.step()
+    torch.cuda.synchronize()
+    assert torch.equal(before, tiny.layers[0].out)
+
+
+def test_full_decode_128k_sampled_rows():
+    wl = Workload(configs.full_decode_128k())
+    wl.step()
+    torch.cuda.synchronize()
+    for row in (0, 11):
+        check_full_row(wl, row)
+    del wl
+    torch.cuda.empty_cache()

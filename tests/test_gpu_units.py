@@ -1,0 +1,334 @@
+"""Parity of each HIP entry point against the CPU oracle (needs the GPU).
+
+Bit-exact: packed codes/scales, generator output, indexer scores, block
+maxima, selected ids and counts.  Attention outputs: |o - ref| <= 2e-3 +
+1e-2 |ref| elementwise (the tolerance the task sets for fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_amd as lib
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+RNG = np.random.default_rng(123)
+SIG = 512 ** -0.5
+
+
+def T(a, dtype=None):
+    t = torch.as_tensor(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def bf16(x):
+    return torch.as_tensor(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+
+
+def tolerance_ok(got, ref):
+    return np.all(np.abs(got - ref) <= 2e-3 + 1e-2 * np.abs(ref))
+
+
+def planes(n, kind):
+    cb, sb = lib.PLANE_BYTES[kind]
+    return (torch.zeros((n, cb), dtype=torch.uint8, device=DEV), torch.zeros((n, sb), dtype=torch.uint8, device=DEV))
+
+
+def edge_values(width, n):
+    x = RNG.standard_normal((n, width)).astype(np.float32)
+    x *= (2.0 ** RNG.integers(-30, 20, (n, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, :16] = np.linspace(-2688, 2688, 16, dtype=np.float32)
+    x[3] = 2.0 ** -14
+    x[4, :] = -1e-30
+    # E2M1 midpoints after the main scale: group amax 6 -> scale 1 -> ties exactly
+    x[5, :16] = np.array([6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, -1.25, -1.75, -2.5, -3.5, -5, 0], np.float32)
+    x[6, :] = 3.0e38
+    x[7, :] = 1.0e-40       # fp32 subnormal
+    return x
+
+
+# ---------------------------------------------------------------- K1 packing
+@pytest.mark.parametrize("kind,width", [(lib.MAIN_FP4, 512), (lib.INDEX_MXFP4, 128), (lib.SWA_FP8, 512)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_pack_bit_exact(kind, width, dt):
+    n = 333
+    x = edge_values(width, n)
+    if dt == "bf16":
+        src = bf16(x).to(DEV)
+        xref = src.float().cpu().numpy()
+    else:
+        src = T(x)
+        xref = x
+    codes, scales = planes(n, kind)
+    lib.csa2_pack_kv(kind, src, codes, scales)
+    torch.cuda.synchronize()
+    pk = {lib.MAIN_FP4: oracle.pack_main, lib.INDEX_MXFP4: oracle.pack_index, lib.SWA_FP8: oracle.pack_swa}[kind]
+    rc, rs = pk(xref)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_pack_slots_and_stride():
+    n = 100
+    x = RNG.standard_normal((n, 640)).astype(np.float32)   # row stride 640 > 512
+    src = T(x)
+    slots = RNG.permutation(300)[:n].astype(np.int64)
+    codes, scales = planes(300, lib.MAIN_FP4)
+    lib.csa2_pack_kv(lib.MAIN_FP4, src[:, :512], codes, scales, slots=T(slots))
+    torch.cuda.synchronize()
+    rc, rs = oracle.pack_main(x[:, :512])
+    assert np.array_equal(codes.cpu().numpy()[slots], rc)
+    assert np.array_equal(scales.cpu().numpy()[slots], rs)
+
+
+# ---------------------------------------------------------------- generator
+def test_synth_matches_host():
+    out = torch.empty(50000, dtype=torch.bfloat16, device=DEV)
+    lib.csa2_synth_normal(7, synth.T_LATENT, 12345, out)
+    ref = synth.normal_bf16(7, synth.T_LATENT, (50000,), offset=12345)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+    out32 = torch.empty(50000, dtype=torch.float32, device=DEV)
+    lib.csa2_synth_normal(7, synth.T_LATENT, 12345, out32)
+    assert np.array_equal(out32.cpu().numpy(), synth.bf16_bits_to_f32(ref))
+    u = torch.empty(50000, dtype=torch.float32, device=DEV)
+    lib.csa2_synth_uniform(9, synth.T_W, 77, u)
+    assert np.array_equal(u.cpu().numpy(), synth.uniform(9, synth.T_W, np.arange(77, 50077, dtype=np.uint64)))
+    x = torch.ones((5000, 16), dtype=torch.float32, device=DEV)
+    lib.csa2_synth_boost(2, synth.T_BOOST, 1000, x)
+    m = synth.boost_mask(2, np.arange(1000, 6000))
+    assert np.array_equal(x.cpu().numpy(), np.where(m[:, None], 3.0, 1.0).astype(np.float32) * np.ones((1, 16)))
+
+
+# ---------------------------------------------------------------- K2 indexer
+def _score_setup(n_rows, n, Hi, spread=False, zero_groups=False):
+    keys = RNG.standard_normal((n_rows * n, 128)).astype(np.float32)
+    q = RNG.standard_normal((n_rows, Hi, 128)).astype(np.float32)
+    if spread:
+        keys *= (2.0 ** RNG.integers(-12, 12, (n_rows * n, 4))).repeat(32, axis=1).astype(np.float32)
+        q *= (2.0 ** RNG.integers(-8, 8, (n_rows, Hi, 4))).repeat(32, axis=2).astype(np.float32)
+    if zero_groups:
+        keys[::7, 32:64] = 0
+    keys = bf16(keys).float().numpy()
+    q = bf16(q).float().numpy()
+    w = RNG.random((n_rows, Hi)).astype(np.float32)
+    w[:, ::3] *= -1
+    kc, ks = oracle.pack_index(keys)
+    return keys, q, w, kc, ks
+
+
+@pytest.mark.parametrize("Hi", [1, 3, 8, 16])
+@pytest.mark.parametrize("spread", [False, True])
+def test_index_score_full_exact(Hi, spread):
+    n_rows, n = 3, 5000
+    keys, q, w, kc, ks = _score_setup(n_rows, n, Hi, spread=spread, zero_groups=spread)
+    n_vis = np.array([n, 4093, 17], np.int32)
+    kv = lib.make_kv(idx_codes=T(kc), idx_scales=T(ks), n_slots=n_rows * n, req_stride=n)
+    req = T(np.arange(n_rows, dtype=np.int32))
+    nv = T(n_vis)
+    rows = lib.make_rows(req, nv, int(n_vis.max()))
+    nv8 = (n + 7) // 8 * 8
+    scores = torch.full((n_rows, nv8 + 8), 7.0, dtype=torch.float32, device=DEV)
+    bmax = torch.full((n_rows, nv8 // 8 + 4), 7.0, dtype=torch.float32, device=DEV)
+    lib.csa2_index_score(kv, rows, T(q), T(w), scores=scores, block_max=bmax)
+    torch.cuda.synchronize()
+    S, Bm = scores.cpu().numpy(), bmax.cpu().numpy()
+    qc, qs = oracle.quant_query(q.reshape(-1, 128))
+    for r in range(n_rows):
+        m = int(n_vis[r])
+        ref = oracle.index_score(qc[r * Hi:(r + 1) * Hi], qs[r * Hi:(r + 1) * Hi], w[r],
+                                 kc[r * n:r * n + m], ks[r * n:r * n + m])
+        assert np.array_equal(S[r, :m], ref), (r, np.nonzero(S[r, :m] != ref)[0][:5])
+        m8 = (m + 7) // 8 * 8
+        assert np.all(np.isneginf(S[r, m:m8])) and np.all(S[r, m8:] == 7.0)
+        nb = (m + 7) // 8
+        assert np.array_equal(Bm[r, :nb], oracle.block_max(ref))
+        assert np.all(Bm[r, nb:] == 7.0)
+
+
+def test_index_score_bf16_query_and_fp32_agree():
+    keys, q, w, kc, ks = _score_setup(1, 2048, 8)
+    kv = lib.make_kv(idx_codes=T(kc), idx_scales=T(ks), n_slots=2048, req_stride=2048)
+    rows = lib.make_rows(T(np.zeros(1, np.int32)), T(np.array([2048], np.int32)), 2048)
+    a = torch.empty((1, 2048), dtype=torch.float32, device=DEV)
+    b = torch.empty((1, 2048), dtype=torch.float32, device=DEV)
+    lib.csa2_index_score(kv, rows, T(q), T(w), scores=a)
+    lib.csa2_index_score(kv, rows, bf16(q).to(DEV), T(w), scores=b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_index_score_pool_exact(paged):
+    n_rows, n, Hi = 2, 9000, 8
+    keys, q, w, kc, ks = _score_setup(n_rows, n, Hi, spread=True)
+    n_vis = np.array([9000, 8997], np.int32)
+    pools = np.full((n_rows, 2048), -1, np.int32)
+    counts = np.array([1125, 700], np.int32)
+    for r in range(n_rows):
+        nb = (int(n_vis[r]) + 7) // 8
+        pools[r, :counts[r]] = np.sort(RNG.permutation(nb)[:counts[r]])
+    last = (int(n_vis[1]) + 7) // 8 - 1                        # a partial last block
+    pools[1, :counts[1]] = np.sort(np.concatenate([RNG.permutation(last)[:counts[1] - 1], [last]]))
+    if paged:
+        P = 64
+        npg = (n + P - 1) // P
+        perm = RNG.permutation(n_rows * npg).astype(np.int32)
+        table = perm.reshape(n_rows, npg)
+        n_slots = n_rows * npg * P
+        kc2 = np.zeros((n_slots, 64), np.uint8)
+        ks2 = np.zeros((n_slots, 4), np.uint8)
+        for r in range(n_rows):
+            pos = np.arange(n)
+            sl = table[r, pos // P].astype(np.int64) * P + pos % P
+            kc2[sl] = kc[r * n:(r + 1) * n]
+            ks2[sl] = ks[r * n:(r + 1) * n]
+        kv = lib.make_kv(idx_codes=T(kc2), idx_scales=T(ks2), n_slots=n_slots, page_entries=P, page_table=T(table))
+    else:
+        kv = lib.make_kv(idx_codes=T(kc), idx_scales=T(ks), n_slots=n_rows * n, req_stride=n)
+    rows = lib.make_rows(T(np.arange(n_rows, dtype=np.int32)), T(n_vis), n)
+    pb = T(pools)
+    pc = T(counts)
+    scores = torch.full((n_rows, 16384), 7.0, dtype=torch.float32, device=DEV)
+    lib.csa2_index_score(kv, rows, T(q), T(w), scores=scores, pool_blocks=pb, pool_count=pc)
+    torch.cuda.synchronize()
+    S = scores.cpu().numpy()
+    qc, qs = oracle.quant_query(q.reshape(-1, 128))
+    for r in range(n_rows):
+        pos = 8 * pools[r, :counts[r]].astype(np.int64).repeat(8) + np.tile(np.arange(8), counts[r])
+        vis = pos < n_vis[r]
+        ref = np.full(len(pos), -np.inf, np.float32)
+        ref[vis] = oracle.index_score(qc[r * Hi:(r + 1) * Hi], qs[r * Hi:(r + 1) * Hi], w[r],
+                                      kc[r * n + pos[vis]], ks[r * n + pos[vis]])
+        assert np.array_equal(S[r, :8 * counts[r]], ref)
+
+
+# ---------------------------------------------------------------- K3 top-k
+@pytest.mark.parametrize("n,k", [(1, 1), (100, 512), (512, 512), (513, 512), (4096, 512), (16384, 2048),
+                                 (16384, 512), (20000, 2048), (131071, 512)])
+def test_topk_exact(n, k):
+    n_rows = 3
+    keys = (RNG.integers(0, 50, (n_rows, n)) * 0.125).astype(np.float32)   # heavy ties
+    keys[0, ::5] = -np.inf                                                  # absent
+    keys[1] = RNG.standard_normal(n).astype(np.float32)
+    keys[2, : n // 2] = -0.0
+    n_cols = np.array([n, max(n - 3, 0), n // 2 + 1], np.int32)
+    out = torch.full((n_rows, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
+    lib.csa2_select_topk(T(keys), k, out, cnt, n_cols=T(n_cols), max_cols=n)
+    torch.cuda.synchronize()
+    O, C = out.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(n_rows):
+        kk = keys[r, :n_cols[r]]
+        present = np.nonzero(~np.isneginf(kk))[0]
+        ref = present[oracle.topk(kk[present], k)] if len(present) else np.zeros(0, np.int64)
+        ref = np.sort(ref)
+        assert C[r] == len(ref)
+        assert np.array_equal(O[r, :C[r]], ref)
+        assert np.all(O[r, C[r]:] == -1)
+
+
+def test_topk_block_counts_and_pool_ids():
+    n_rows, nb = 2, 3000
+    bm = RNG.standard_normal((n_rows, nb)).astype(np.float32)
+    n_vis = np.array([8 * nb, 8 * 1500 - 3], np.int32)
+    out = torch.empty((n_rows, 2048), dtype=torch.int32, device=DEV)
+    cnt = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+    lib.csa2_select_topk(T(bm), 2048, out, cnt, n_cols=T(n_vis), cols_div=8, max_cols=nb)
+    torch.cuda.synchronize()
+    for r in range(n_rows):
+        nbr = (int(n_vis[r]) + 7) // 8
+        ref = oracle.topk(bm[r, :nbr], 2048)
+        assert int(cnt[r]) == len(ref) and np.array_equal(out[r, :len(ref)].cpu().numpy(), ref)
+    # pool-mapped ids, keys addressed by id (the Full layer's second selection)
+    scores = RNG.standard_normal((n_rows, 8 * nb)).astype(np.float32)
+    idx = torch.empty((n_rows, 512), dtype=torch.int32, device=DEV)
+    icnt = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+    lib.csa2_select_topk(T(scores), 512, idx, icnt, n_cols=cnt, cols_mul=8, pool_blocks=out, keys_by_id=True,
+                         max_cols=16384)
+    # pool-mapped ids, keys by column (the Reindex layer)
+    pscores = RNG.standard_normal((n_rows, 16384)).astype(np.float32)
+    idx2 = torch.empty((n_rows, 512), dtype=torch.int32, device=DEV)
+    icnt2 = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+    lib.csa2_select_topk(T(pscores), 512, idx2, icnt2, n_cols=cnt, cols_mul=8, pool_blocks=out,
+                         keys_by_id=False, max_cols=16384)
+    torch.cuda.synchronize()
+    for r in range(n_rows):
+        pool = out[r, :int(cnt[r])].cpu().numpy()
+        pos = (8 * pool.astype(np.int64)[:, None] + np.arange(8)).reshape(-1)
+        ref = oracle.topk(scores[r, pos], 512, ids=pos)
+        assert int(icnt[r]) == len(ref) and np.array_equal(idx[r, :len(ref)].cpu().numpy(), ref)
+        ref2 = oracle.topk(pscores[r, :len(pos)], 512, ids=pos)
+        assert int(icnt2[r]) == len(ref2) and np.array_equal(idx2[r, :len(ref2)].cpu().numpy(), ref2)
+
+
+# ---------------------------------------------------------------- K4 / K5 attention
+def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=torch.bfloat16):
+    lat = bf16(RNG.standard_normal((n_rows * n_entries, 512)).astype(np.float32)).float().numpy()
+    mc, ms = oracle.pack_main(lat)
+    K = oracle.dequant_main(mc, ms)
+    swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
+    wc, wsc = oracle.pack_swa(swa)
+    W = oracle.dequant_swa(wc, wsc)
+    q = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32) * 2).float().numpy()
+    idx = np.full((n_rows, 512), -1, np.int32)
+    for r in range(n_rows):
+        idx[r, :counts[r]] = np.sort(RNG.permutation(n_entries)[:counts[r]])
+    sk = (RNG.standard_normal(H) * 3).astype(np.float32) if sink else None
+    kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), n_slots=n_rows * n_entries, req_stride=n_entries)
+    rows = lib.make_rows(T(np.arange(n_rows, dtype=np.int32)), T(np.full(n_rows, n_entries, np.int32)), n_entries)
+    qd = torch.as_tensor(q).to(qdt).to(DEV)
+    o_p = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
+    ws = torch.empty(lib.csa2_sparse_attn_workspace_size(n_rows, H), dtype=torch.uint8, device=DEV)
+    lib.csa2_sparse_attn(kv, rows, qd, T(idx), T(np.asarray(counts, np.int32)), SIG, o_p, lse, ws)
+    out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
+    first = np.arange(n_rows, dtype=np.int64) * 128
+    lib.csa2_swa_merge(T(wc), T(wsc), T(first), T(np.asarray(swa_counts, np.int32)), qd, SIG, out,
+                       sink=None if sk is None else T(sk), o_partial=o_p, lse=lse)
+    torch.cuda.synchronize()
+    O_p, L_p, Out = o_p.cpu().numpy(), lse.cpu().numpy(), out.cpu().numpy()
+    for r in range(n_rows):
+        Kr = K[r * n_entries + idx[r, :counts[r]]]
+        Wr = W[r * 128:r * 128 + swa_counts[r]]
+        ro, rl = oracle.attention(q[r], Kr, None, sigma=SIG)
+        assert tolerance_ok(O_p[r], ro), (r, np.abs(O_p[r] - ro).max())
+        if counts[r]:
+            assert np.allclose(L_p[r], rl, rtol=1e-5, atol=1e-5)
+        else:
+            assert np.all(np.isneginf(L_p[r])) and not O_p[r].any()
+        fo, _ = oracle.attention(q[r], Kr, Wr, sink=sk, sigma=SIG)
+        assert tolerance_ok(Out[r], fo), (r, np.abs(Out[r] - fo).max())
+
+
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_attention_counts(H):
+    _attn_case(4, H, [512, 1, 65, 0], [128, 128, 1, 100])
+
+
+def test_attention_sink_and_empty_window():
+    _attn_case(3, 32, [300, 0, 64], [0, 128, 0], sink=True)
+
+
+def test_attention_fp32_query():
+    _attn_case(2, 16, [200, 512], [128, 128], qdt=torch.float32)
+
+
+def test_swa_only_and_alias():
+    n_rows, H = 2, 16
+    swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
+    wc, wsc = oracle.pack_swa(swa)
+    W = oracle.dequant_swa(wc, wsc)
+    q = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32)).float().numpy()
+    out = torch.full((n_rows, H, 512), 5.0, dtype=torch.float32, device=DEV)
+    lib.csa2_swa_merge(T(wc), T(wsc), T(np.array([0, 128], np.int64)), T(np.array([128, 37], np.int32)),
+                       bf16(q).to(DEV), SIG, out)
+    torch.cuda.synchronize()
+    for r, c in enumerate([128, 37]):
+        ref, _ = oracle.attention(q[r], None, W[r * 128:r * 128 + c], sigma=SIG)
+        assert tolerance_ok(out[r].cpu().numpy(), ref)
