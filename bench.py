@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+One step = the whole hot path over one batch: for the default workload (16
+requests x 131,072 cached entries, 64 heads, Full layer) that is the MXFP4
+indexer scan with block maxima, the 2,048-block pool, the top-512 positions,
+the sparse attention and the sliding-window merge, for all 16 requests.
+
+Inputs are resident in HBM before the timed region; the KV caches rotate
+over several identical copies so that the 256 MB Infinity Cache cannot serve
+the 143 MB key stream from one step to the next.
+
+Prints one JSON line (see the README of the repository for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "CSA2 decode steps/s (batch×heads) at 128K ctx; achieved HBM GB/s vs peak"
+DOMINANT = "index_score"          # the kernel the roofline object describes
+DOMINANT_SRC = os.path.join(ROOT, "long_context_sparse_amd", "csrc", "index_score.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_full_decode_16x128k_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c1", help="c0..c4 (the JSON line is for c1 by default)")
+    ap.add_argument("--copies", type=int, default=4, help="rotated KV-cache copies")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8, help="rows of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run a 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from committed counter runs,
+    only while the kernel source is the one they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256_16") != source_hash(DOMINANT_SRC):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, rows, threads):
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    first `rows` requests, full rows (scoring every position, the pool, the
+    top-512, attention over 512 + 128 entries for all heads).  Inputs are drawn
+    and packed before the clock starts, as on the GPU."""
+    import numpy as np
+    import oracle
+    from tests.ref import RowRef
+
+    refs = [RowRef(cfg, r) for r in range(rows)]
+    packed = [r.packed_index(np.arange(r.n_vis)) for r in refs]
+
+    def run(i):
+        r = refs[i]
+        kc, ks = packed[i]
+        sc = oracle.index_score(r.qc, r.qs, r.w, kc, ks)
+        _, idx = oracle.full_select(sc)
+        return r.attend(idx)
+
+    t0 = time.perf_counter()
+    oracle.map_rows(run, list(range(rows)), threads=threads)
+    dt = time.perf_counter() - t0
+    return dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); requests are independent, so "
+              f"N GPUs would each run this same step on their own requests.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import long_context_sparse_amd as lib
+    from long_context_sparse_amd.workload import Workload
+    from synth import configs
+
+    lib.lib()        # raises if the HIP library is missing: there is no other path
+    cfg = configs.ALL[args.workload]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = Workload(cfg, copies=args.copies)
+    B, H = wl.n_rows, cfg.heads
+    algo = wl.algorithmic_bytes()
+
+    for i in range(args.warmup):
+        wl.step(copy=i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, dominant kernel bracketed by events
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(copy=args.warmup + i, marks={"index_score": ev[i]})
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    k2_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- per-kernel breakdown (separate, untimed pass)
+    names = ["index_score", "select_blocks", "select_positions", "sparse_attn", "swa_merge"]
+    if cfg.mode == "reindex":
+        names = ["index_score", "select_positions", "sparse_attn", "swa_merge"]
+    per = {n: [] for n in names}
+    for i in range(20):
+        marks = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+        wl.step(copy=i, marks=marks)
+        torch.cuda.synchronize()
+        for n, (a, b) in marks.items():
+            per[n].append(a.elapsed_time(b) * 1e3)
+    kernels_us = {n: round(float(np.median(v)), 2) for n, v in per.items()}
+
+    ms = dt * 1e3 / args.steps
+    steps_s = args.steps / dt
+    k2_bytes = algo.get("index_keys_full", algo.get("index_keys_pool", 0))
+    k2_gbs = k2_bytes / (k2_ms * 1e-3) / 1e9
+    step_gbs = algo["total"] / (ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(steps_s * B * H, 1),
+        "unit": "(request x head) decodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (indexer MFMA, exact) + bf16/fp16 (attention MFMA), fp32 accumulate",
+        "data": "synthetic (seeded counter-based N(0,1)/U(0,1), packed on the GPU)",
+        "config": {"workload": cfg.name, "requests": B, "context_entries": int(wl.max_vis), "heads": H,
+                   "idx_heads": cfg.idx_heads, "pool_blocks": 2048, "topk": 512, "window": cfg.window,
+                   "kv_copies_rotated": args.copies},
+        "steps_per_s": round(steps_s, 2),
+        "step_algorithmic_bytes": algo["total"],
+        "step_gbs": round(step_gbs, 1),
+        "step_frac_of_hbm_peak": round(step_gbs / PEAK_HBM_GBS, 4),
+        "kernels_us": kernels_us,
+        "roofline": {
+            "kernel": DOMINANT,
+            "bound": "hbm",
+            "achieved": round(k2_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(k2_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": k2_bytes,
+            "avg_launch_us": round(k2_ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu:
+        rows = min(args.cpu_rows, B)
+        threads = min(rows, os.cpu_count() or 1, 16)
+        cdt = cpu_baseline(cfg, rows, threads)
+        out["cpu_baseline"] = {
+            "value": round(rows * H / cdt, 3),
+            "unit": "(request x head) decodes/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} of {B} requests of the same workload, whole rows ({int(wl.max_vis)} entries "
+                      f"scored, pool, top-512, {H}-head attention), {cdt:.1f} s",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

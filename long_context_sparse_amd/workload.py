@@ -181,39 +181,64 @@ class Workload:
                          slots=sl, boost=cfg.boost, dev=self.dev)
 
     # --------------------------------------------------------------- the step
-    def run_full(self, layer: "Layer", kv, stream=None):
+    @staticmethod
+    def _mark(marks, name, which):
+        if marks and name in marks:
+            marks[name][which].record()
+
+    def run_full(self, layer: "Layer", kv, stream=None, marks=None):
+        m = self._mark
+        m(marks, "index_score", 0)
         csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.scores, block_max=self.block_max,
                          stream=stream)
+        m(marks, "index_score", 1)
         if self.cfg.mode == "prefill":
+            m(marks, "select_positions", 0)
             csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.n_vis,
                              max_cols=self.max_vis, stream=stream)
+            m(marks, "select_positions", 1)
         else:
+            m(marks, "select_blocks", 0)
             csa2_select_topk(self.block_max, 2048, self.pool, self.pool_count, n_cols=self.n_vis, cols_div=8,
                              max_cols=self.nv8 // 8, stream=stream)
+            m(marks, "select_blocks", 1)
+            m(marks, "select_positions", 0)
             csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.pool_count, cols_mul=8,
                              pool_blocks=self.pool, keys_by_id=True, max_cols=16384, stream=stream)
-        self._attend(layer, kv, stream)
+            m(marks, "select_positions", 1)
+        self._attend(layer, kv, stream, marks)
 
-    def run_reindex(self, layer: "Layer", kv, stream=None):
+    def run_reindex(self, layer: "Layer", kv, stream=None, marks=None):
+        m = self._mark
+        m(marks, "index_score", 0)
         csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.pool_scores,
                          pool_blocks=self.pool, pool_count=self.pool_count, stream=stream)
+        m(marks, "index_score", 1)
+        m(marks, "select_positions", 0)
         csa2_select_topk(self.pool_scores, 512, layer.idx, layer.idx_count, n_cols=self.pool_count, cols_mul=8,
                          pool_blocks=self.pool, keys_by_id=False, max_cols=16384, stream=stream)
-        self._attend(layer, kv, stream)
+        m(marks, "select_positions", 1)
+        self._attend(layer, kv, stream, marks)
 
-    def _attend(self, layer, kv, stream):
+    def _attend(self, layer, kv, stream, marks=None):
+        m = self._mark
+        m(marks, "sparse_attn", 0)
         csa2_sparse_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, self.sigma, layer.o_partial,
                          layer.lse, self.workspace, stream=stream)
+        m(marks, "sparse_attn", 1)
+        m(marks, "swa_merge", 0)
         csa2_swa_merge(layer.swa_codes, layer.swa_scales, layer.swa_first, layer.swa_count, layer.q, self.sigma,
                        layer.out, o_partial=layer.o_partial, lse=layer.lse, stream=stream)
+        m(marks, "swa_merge", 1)
 
-    def step(self, copy: int = 0, stream=None):
+    def step(self, copy: int = 0, stream=None, marks=None):
+        """One pass of the hot path.  `marks` maps step names to (start, end)
+        events recorded around that call (first layer only)."""
         kv = self.kvs[copy % len(self.kvs)]
-        mode = self.cfg.mode
-        if mode == "reindex":
-            self.run_reindex(self.layers[0], kv, stream)
+        if self.cfg.mode == "reindex":
+            self.run_reindex(self.layers[0], kv, stream, marks)
             return
-        self.run_full(self.layers[0], kv, stream)
+        self.run_full(self.layers[0], kv, stream, marks)
         for layer in self.layers[1:]:
             self.run_reindex(layer, kv, stream)
 
