@@ -130,9 +130,9 @@ def main():
         torch.cuda.synchronize()
 
     # ---- per-kernel breakdown (separate, untimed pass)
-    names = ["index_score", "select_blocks", "select_positions", "sparse_attn", "swa_merge"]
-    if cfg.mode == "reindex":
-        names = ["index_score", "select_positions", "sparse_attn", "swa_merge"]
+    names = ["index_score", "select_blocks", "select_positions", "attention"]
+    if cfg.mode != "full" and cfg.mode != "mixed":
+        names = ["index_score", "select_positions", "attention"]
     per = {n: [] for n in names}
     for i in range(20):
         marks = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}

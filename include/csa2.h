@@ -172,37 +172,52 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride,
                              void* stream);
 
 /* ---------------------------------------------------------------- attention
- * Sparse branch ('DeepSeek-V4' page, section 2.3.1, shared-KV MQA; MLA article
- * section 4, absorbed query):  for each row and head h,
- *   z_j = softmax_scale * q_h . K_j over the row's selected entries
- *   K_j = dequantised MAIN entry of position idx[row * idx_stride + j],
- *   j < idx_count[row] (<= 512), each K_j both key and value;
- *   o_partial[row][h][:] = sum_j softmax(z)_j K_j   (fp32),
- *   lse[row][h] = ln sum_j exp(z_j)   (-inf and o = 0 for an empty set).
- * q [n_rows][n_heads][512] bf16 or fp32; n_heads a multiple of 16, at most 128.
- * workspace: csa2_sparse_attn_workspace_size(n_rows, n_heads) bytes, 256-B
- * aligned, contents need not be initialised. */
-size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads);
+ * Core attention of CSA2 ('DeepSeek-V4' page, section 2.3.1 "Shared Key-Value
+ * MQA": each selected compressed entry is both key and value; section 2.3.3:
+ * the sliding-window entries join the selected ones in the same softmax, and
+ * a per-head sink logit adds exp(sink_h) to its denominator; MLA article,
+ * section 4: the query is the absorbed query in the 512-channel latent space).
+ * For a row and head h, with z_j = softmax_scale * q_h . E_j over the row's
+ * entries E_j (dequantised, exact):
+ *   o[row][h][:] = sum_j e^(z_j) E_j / (sum_j e^(z_j) [+ e^(sink_h)]),
+ *   lse[row][h]  = ln(sum_j e^(z_j) [+ e^(sink_h)]), -inf (o = 0) if empty.
+ * Entry sets: the SELECTED entries are the MAIN entries of positions
+ * idx[row * idx_stride + j], j < idx_count[row] (<= 512, positions < n_vis);
+ * the WINDOW entries are SWA entries swa_first[row] .. + swa_count[row] - 1
+ * (<= 128) of the planes swa_codes [swa_slots][512] / swa_scales [.][32].
+ * q [n_rows][n_heads][512] bf16 (fp32 is rounded to bf16 on the way in);
+ * n_heads 16, 32, 48, 64 or 128; outputs fp32.  q, o/out 16-B aligned.
+ * workspace: csa2_attn_workspace_size(n_rows, n_heads) bytes, 256-B aligned,
+ * no initialisation needed, not kept between calls. */
+size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads);
+
+/* Selected entries only: o_partial / lse of the sparse branch. */
 csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows,
                              const void* q, csa2_dtype q_dtype, int32_t n_heads,
                              const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
                              float softmax_scale, float* o_partial, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Sliding-window branch and merge ('DeepSeek-V4' page, section 2.3.3: the
- * window's uncompressed entries join the selected entries in the same core
- * attention; attention sink adds exp(sink_h) to the denominator):
- *   window of row r = SWA entries swa_first[r] .. swa_first[r]+swa_count[r]-1
- *   (swa_count <= 128) of the planes swa_codes [.][512] / swa_scales [.][32];
- *   out[r][h][:] = joint softmax over {sparse set} + {window} (+ sink) of the
- *   entries, obtained by merging (o_partial, lse) with the window's own
- *   attention through their log-sum-exp.  o_partial / lse NULL: window only.
- *   sink [n_heads] fp32 or NULL.  out may alias o_partial. */
+/* Window branch merged with a sparse-branch result through its log-sum-exp:
+ * out = joint softmax over {the entries behind (o_partial, lse)} + {window}
+ * (+ sink).  o_partial / lse NULL: window only.  sink [n_heads] or NULL.
+ * out may alias o_partial. */
 csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
                            const int64_t* swa_first, const int32_t* swa_count, int32_t n_rows,
                            const void* q, csa2_dtype q_dtype, int32_t n_heads, float softmax_scale,
                            const float* sink, const float* o_partial, const float* lse,
-                           float* out, void* stream);
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Both branches in one pass (the decode step's form): out = joint softmax
+ * over selected + window entries (+ sink); lse (may be NULL) of that joint
+ * denominator. */
+csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
+                                 const void* q, csa2_dtype q_dtype, int32_t n_heads,
+                                 const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
+                                 const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                                 const int64_t* swa_first, const int32_t* swa_count, const float* sink,
+                                 float softmax_scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- synthetic inputs
  * Counter-based generator for seeded synthetic inputs (SplitMix64; Steele,

@@ -194,14 +194,50 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_
     return hip_status(csa2::launch_topk(a, (hipStream_t)stream), "csa2_select_topk launch");
 }
 
-size_t csa2_sparse_attn_workspace_size(int32_t n_rows, int32_t n_heads) {
+size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads) {
     if (n_rows <= 0 || n_heads <= 0) return 0;
-    return csa2::sparse_attn_workspace_bytes(n_rows, n_heads);
+    return csa2::attn_workspace_bytes(n_rows, n_heads);
 }
 
 static csa2_status check_heads(int32_t h) {
-    if (h < 16 || h > 128 || (h % 16)) return fail(CSA2_ERR_UNSUPPORTED, "n_heads must be a multiple of 16 in 16..128 (got %d)", h);
+    if (!(h == 16 || h == 32 || h == 48 || h == 64 || h == 128))
+        return fail(CSA2_ERR_UNSUPPORTED, "n_heads must be 16, 32, 48, 64 or 128 (got %d)", h);
     return CSA2_OK;
+}
+
+static csa2_status check_common(int32_t n_rows, const void* q, csa2_dtype q_dtype, int32_t n_heads, float scale,
+                                void* workspace, size_t workspace_bytes) {
+    csa2_status s = check_heads(n_heads);
+    if (s != CSA2_OK) return s;
+    if (n_rows < 0 || n_rows > 65535) return fail(CSA2_ERR_RANGE, "n_rows out of range");
+    if (q_dtype != CSA2_BF16 && q_dtype != CSA2_F32) return fail(CSA2_ERR_UNSUPPORTED, "unknown q dtype");
+    if (n_rows == 0) return CSA2_OK;
+    if (!q) return fail(CSA2_ERR_NULL, "q is NULL");
+    if (!aligned(q, 16)) return fail(CSA2_ERR_ALIGN, "q must be 16-byte aligned");
+    if (!(scale > 0.0f) || scale > 1e30f) return fail(CSA2_ERR_RANGE, "softmax_scale must be positive and finite");
+    const size_t need = csa2::attn_workspace_bytes(n_rows, n_heads);
+    if (!workspace || workspace_bytes < need) return fail(CSA2_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(workspace, 256)) return fail(CSA2_ERR_ALIGN, "workspace must be 256-byte aligned");
+    return CSA2_OK;
+}
+
+static csa2_status check_swa(const uint8_t* codes, const uint8_t* scales, int64_t slots, const int64_t* first,
+                             const int32_t* count) {
+    if (!codes || !scales || !first || !count) return fail(CSA2_ERR_NULL, "SWA planes / swa_first / swa_count is NULL");
+    if (!aligned(codes, 256) || !aligned(scales, 256)) return fail(CSA2_ERR_ALIGN, "SWA planes must be 256-byte aligned");
+    if (slots <= 0) return fail(CSA2_ERR_RANGE, "swa_slots must be positive");
+    return CSA2_OK;
+}
+
+static void fill_q(csa2::AttnArgs& a, const void* q, csa2_dtype q_dtype, int32_t n_heads, int32_t n_rows, float scale,
+                   void* workspace) {
+    memset(&a, 0, sizeof a);
+    a.q = q;
+    a.q_bf16 = q_dtype == CSA2_BF16;
+    a.n_heads = n_heads;
+    a.n_rows = n_rows;
+    a.scale = scale;
+    a.ws = (float*)workspace;
 }
 
 csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
@@ -212,64 +248,82 @@ csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows, const voi
     csa2_status s = make_view(kv, true, false, &v);
     if (s != CSA2_OK) return s;
     if ((s = check_rows(rows)) != CSA2_OK) return s;
-    if ((s = check_heads(n_heads)) != CSA2_OK) return s;
-    if (q_dtype != CSA2_BF16 && q_dtype != CSA2_F32) return fail(CSA2_ERR_UNSUPPORTED, "unknown q dtype");
+    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale, workspace, workspace_bytes)) != CSA2_OK) return s;
     if (rows->n_rows == 0) return CSA2_OK;
-    if (!q || !idx || !idx_count || !o_partial || !lse) return fail(CSA2_ERR_NULL, "q / idx / idx_count / o_partial / lse is NULL");
-    if (!aligned(q, 16) || !aligned(o_partial, 16)) return fail(CSA2_ERR_ALIGN, "q and o_partial must be 16-byte aligned");
+    if (!idx || !idx_count || !o_partial || !lse) return fail(CSA2_ERR_NULL, "idx / idx_count / o_partial / lse is NULL");
+    if (!aligned(o_partial, 16)) return fail(CSA2_ERR_ALIGN, "o_partial must be 16-byte aligned");
     if (idx_stride < 1) return fail(CSA2_ERR_SHAPE, "idx_stride must be >= 1");
-    const size_t need = csa2::sparse_attn_workspace_bytes(rows->n_rows, n_heads);
-    if (!workspace || workspace_bytes < need) return fail(CSA2_ERR_WORKSPACE, "workspace needs %zu bytes", need);
-    if (!aligned(workspace, 256)) return fail(CSA2_ERR_ALIGN, "workspace must be 256-byte aligned");
-    if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return fail(CSA2_ERR_RANGE, "softmax_scale must be positive and finite");
-    csa2::SparseAttnArgs a;
-    a.q = q;
-    a.q_bf16 = q_dtype == CSA2_BF16;
-    a.n_heads = n_heads;
+    csa2::AttnArgs a;
+    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
     a.req = rows->req;
-    a.n_rows = rows->n_rows;
     a.idx = idx;
     a.idx_stride = idx_stride;
     a.idx_count = idx_count;
-    a.scale = softmax_scale;
-    a.o = o_partial;
-    a.lse = lse;
-    a.ws = (float*)workspace;
-    return hip_status(csa2::launch_sparse_attn(v, a, (hipStream_t)stream), "csa2_sparse_attn launch");
+    a.out = o_partial;
+    a.lse_out = lse;
+    a.max_chunks = 8;
+    return hip_status(csa2::launch_attn(v, a, (hipStream_t)stream), "csa2_sparse_attn launch");
 }
 
 csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
                            const int64_t* swa_first, const int32_t* swa_count, int32_t n_rows, const void* q,
                            csa2_dtype q_dtype, int32_t n_heads, float softmax_scale, const float* sink,
-                           const float* o_partial, const float* lse, float* out, void* stream) {
-    csa2_status s = check_heads(n_heads);
+                           const float* o_partial, const float* lse, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    csa2_status s = check_common(n_rows, q, q_dtype, n_heads, softmax_scale, workspace, workspace_bytes);
     if (s != CSA2_OK) return s;
-    if (n_rows < 0 || n_rows > 65535) return fail(CSA2_ERR_RANGE, "n_rows out of range");
-    if (q_dtype != CSA2_BF16 && q_dtype != CSA2_F32) return fail(CSA2_ERR_UNSUPPORTED, "unknown q dtype");
     if (n_rows == 0) return CSA2_OK;
-    if (!swa_codes || !swa_scales || !swa_first || !swa_count || !q || !out)
-        return fail(CSA2_ERR_NULL, "swa planes / swa_first / swa_count / q / out is NULL");
+    if ((s = check_swa(swa_codes, swa_scales, swa_slots, swa_first, swa_count)) != CSA2_OK) return s;
+    if (!out) return fail(CSA2_ERR_NULL, "out is NULL");
     if ((o_partial == nullptr) != (lse == nullptr)) return fail(CSA2_ERR_NULL, "o_partial and lse must be both set or both NULL");
-    if (!aligned(swa_codes, 256) || !aligned(swa_scales, 256)) return fail(CSA2_ERR_ALIGN, "SWA planes must be 256-byte aligned");
-    if (!aligned(q, 16) || !aligned(out, 16) || (o_partial && !aligned(o_partial, 16)))
-        return fail(CSA2_ERR_ALIGN, "q, out and o_partial must be 16-byte aligned");
-    if (swa_slots <= 0) return fail(CSA2_ERR_RANGE, "swa_slots must be positive");
-    if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return fail(CSA2_ERR_RANGE, "softmax_scale must be positive and finite");
-    csa2::SwaArgs a;
-    a.codes = swa_codes;
-    a.scales = swa_scales;
-    a.first = swa_first;
-    a.count = swa_count;
-    a.n_rows = n_rows;
-    a.q = q;
-    a.q_bf16 = q_dtype == CSA2_BF16;
-    a.n_heads = n_heads;
-    a.scale = softmax_scale;
+    if (!aligned(out, 16) || (o_partial && !aligned(o_partial, 16))) return fail(CSA2_ERR_ALIGN, "out and o_partial must be 16-byte aligned");
+    csa2::AttnArgs a;
+    fill_q(a, q, q_dtype, n_heads, n_rows, softmax_scale, workspace);
+    a.swa_codes = swa_codes;
+    a.swa_scales = swa_scales;
+    a.swa_first = swa_first;
+    a.swa_count = swa_count;
     a.sink = sink;
     a.o_in = o_partial;
     a.lse_in = lse;
     a.out = out;
-    return hip_status(csa2::launch_swa_merge(a, (hipStream_t)stream), "csa2_swa_merge launch");
+    a.max_chunks = 2;
+    csa2::KvView none;
+    memset(&none, 0, sizeof none);
+    return hip_status(csa2::launch_attn(none, a, (hipStream_t)stream), "csa2_swa_merge launch");
+}
+
+csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
+                                 int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
+                                 const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                                 const int64_t* swa_first, const int32_t* swa_count, const float* sink,
+                                 float softmax_scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    csa2::KvView v;
+    csa2_status s = make_view(kv, true, false, &v);
+    if (s != CSA2_OK) return s;
+    if ((s = check_rows(rows)) != CSA2_OK) return s;
+    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale, workspace, workspace_bytes)) != CSA2_OK) return s;
+    if (rows->n_rows == 0) return CSA2_OK;
+    if ((s = check_swa(swa_codes, swa_scales, swa_slots, swa_first, swa_count)) != CSA2_OK) return s;
+    if (!idx || !idx_count || !out) return fail(CSA2_ERR_NULL, "idx / idx_count / out is NULL");
+    if (!aligned(out, 16)) return fail(CSA2_ERR_ALIGN, "out must be 16-byte aligned");
+    if (idx_stride < 1) return fail(CSA2_ERR_SHAPE, "idx_stride must be >= 1");
+    csa2::AttnArgs a;
+    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
+    a.req = rows->req;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.idx_count = idx_count;
+    a.swa_codes = swa_codes;
+    a.swa_scales = swa_scales;
+    a.swa_first = swa_first;
+    a.swa_count = swa_count;
+    a.sink = sink;
+    a.out = out;
+    a.lse_out = lse;
+    a.max_chunks = 10;
+    return hip_status(csa2::launch_attn(v, a, (hipStream_t)stream), "csa2_sparse_swa_attn launch");
 }
 
 csa2_status csa2_synth_normal(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n, csa2_dtype out_dtype,

@@ -1,4 +1,5 @@
-// attn.hip -- K4 sparse attention and K5 sliding-window branch + merge (gfx950).
+// attn.hip -- K4/K5: sparse attention over the selected FP4 entries, jointly
+// with the 8-bit sliding window and an optional sink (gfx950).
 //
 // Shared-KV MQA: every selected compressed entry is both key and value, and
 // the query heads attend in the 512-channel latent space (absorbed query)
@@ -9,42 +10,49 @@
 // optional per-head sink adds exp(z'_h) to the denominator [section 2.3.3].
 //
 // MI355X mapping
-//   * Sparse branch: one workgroup per (row, split of 64 selected entries),
-//     one wave per 16 heads.  The workgroup gathers its 64 entries (256 B codes
-//     + 32 B scales each), dequantises them once into LDS -- as bf16 rows
-//     [entry][channel] for Q.K and as fp16 columns [channel][entry] for P.V
-//     (FP4 x E4M3 values have at most 6 significant bits and lie in
-//     [2^-10, 2688], so both conversions are exact).
+//   * A row's entries form one virtual list: its selected FP4 entries, padded
+//     to a multiple of 64, then its window entries.  A workgroup walks a
+//     contiguous range of 64-entry chunks with an online softmax, one wave per
+//     16 heads.  Few rows (decode): each chunk gets its own workgroup and a
+//     merge kernel combines the partials; many rows (prefill): one
+//     workgroup per row writes the final output itself.
+//   * Per chunk the workgroup gathers the 64 entries once and dequantises them
+//     into LDS -- bf16 rows [entry][channel] for Q.K, and columns
+//     [channel][entry] for P.V.  FP4 x E4M3 values have at most 6
+//     significant bits and lie in [2^-10, 2688]: exact in bf16 and in fp16.
+//     Window values E4M3 x 2^e are exact in bf16.
 //   * S^T = K q^T on V_MFMA_F32_16X16X32_BF16 (A = 16 entries from LDS, B = the
 //     wave's 16 query heads held in registers).  The MFMA output layout puts
 //     4 consecutive entries of one head in a lane, which is exactly the
-//     B-operand layout P^T needs for O^T = V^T P^T (V_MFMA_F32_16X16X32_F16)
-//     once the contraction slots are mapped to entries {4g..4g+3, 16+4g..}:
-//     the softmax never leaves registers.
-//   * Split partials (max, sum, unnormalised O) go to a workspace and a
-//     second kernel merges them through their log-sum-exp.
-//   * Window branch: one workgroup per row, chunks of 64 window entries with
-//     an online softmax; the window KV is 8-bit E4M3 x 2^e, exact in bf16, so
-//     P.V uses bf16 with P split into a bf16 head and tail (16 bits of P).
-//     Its epilogue merges the sparse branch's (o, lse) and the sink.
+//     B-operand layout P^T needs for O^T = V^T P^T once the contraction slots
+//     are mapped to entries {4g..4g+3, 16+4g..16+4g+3}: P never leaves
+//     registers.  Selected chunks use V_MFMA_F32_16X16X32_F16 with P in fp16;
+//     window chunks use bf16 with P split into a bf16 head and tail.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
 namespace csa2 {
 
-constexpr int AT_ENT = 64;            // entries per split / chunk
-constexpr int AT_SPLITS = 512 / AT_ENT;
+constexpr int AT_ENT = 64;            // entries per chunk
 constexpr int KT_LD = 512 + 8;        // bf16 elements per K row in LDS (padded)
 constexpr int VT_LD = AT_ENT + 4;     // 16-bit elements per V^T row in LDS (padded)
 constexpr size_t AT_LDS = (size_t)AT_ENT * KT_LD * 2 + (size_t)512 * VT_LD * 2;
+constexpr int AT_MAX_SPLITS = 10;     // 512 selected + 128 window entries, 64 per chunk
 
-size_t sparse_attn_workspace_bytes(int n_rows, int n_heads) {
-    const size_t per = (size_t)AT_SPLITS * n_heads;
-    return (size_t)n_rows * per * (512 + 2) * sizeof(float);
+int attn_splits(int n_rows) {
+    if (n_rows <= 0) return 1;
+    const int s = (2560 + n_rows - 1) / n_rows;   // aim at ~2,560 workgroups
+    return s < 1 ? 1 : (s > AT_MAX_SPLITS ? AT_MAX_SPLITS : s);
+}
+
+size_t attn_workspace_bytes(int n_rows, int n_heads) {
+    const int s = attn_splits(n_rows);
+    if (s == 1) return 256;
+    return (size_t)n_rows * s * n_heads * (512 + 2) * sizeof(float);
 }
 
 // q B-operand of one wave: lane holds head (h0 + l%16), channels
-// 32*ks + 8*(l/16) .. +8 for ks = 0..15, as bf16.
+// 32*ks + 8*(l/16) .. +8 for ks = 0..15, as bf16 (fp32 input rounded to nearest even).
 template <bool QBF16>
 __device__ __forceinline__ void load_q_operand(const void* q, int64_t row_head0, int n, int g, bf16x8* qv) {
     if (QBF16) {
@@ -66,21 +74,6 @@ __device__ __forceinline__ void load_q_operand(const void* q, int64_t row_head0,
     }
 }
 
-// S^T tiles: acc[et][i] = K[16et + 4g + i] . q[head l%16] for 64 entries.
-__device__ __forceinline__ void qk_tiles(const uint16_t* Kt, const bf16x8* qv, int n, int g, f32x4* acc) {
-#pragma unroll
-    for (int et = 0; et < 4; ++et) {
-        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-        const uint16_t* base = Kt + (16 * et + n) * KT_LD + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const bf16x8 a = *(const bf16x8*)(base + 32 * ks);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[ks], c, 0, 0, 0);
-        }
-        acc[et] = c;
-    }
-}
-
 // V^T A-operand for channel tile ct, contraction step u: channel 16ct + n,
 // entries {32u + 4g .. +3} and {32u + 16 + 4g .. +3}.
 __device__ __forceinline__ uint4 vt_operand(const uint16_t* Vt, int ct, int u, int n, int g) {
@@ -90,204 +83,119 @@ __device__ __forceinline__ uint4 vt_operand(const uint16_t* Vt, int ct, int u, i
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// --------------------------------------------------------------- sparse split
+// Gather + dequantise one chunk of selected FP4 entries (lane = entry).
+__device__ __forceinline__ void dequant_main_chunk(const KvView& kv, const AttnArgs& a, int row, int e0, int nent,
+                                                   uint16_t* Kt, uint16_t* Vt, int wave, int W, int l) {
+    const int j = l;
+    const bool valid = j < nent;
+    int64_t ent = 0;
+    if (valid) ent = entry_of(kv, a.req[row], a.idx[(int64_t)row * a.idx_stride + e0 + j]);
+    for (int grp = wave; grp < 32; grp += W) {
+        uint2 c = make_uint2(0u, 0u);
+        uint32_t sc = 0u;
+        if (valid) {
+            c = *(const uint2*)(kv.main_codes + ent * 256 + 8 * grp);
+            sc = kv.main_scales[ent * 32 + grp];
+        }
+        const float s = e4m3_to_f32(sc);
+        uint32_t kb[8];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t word = i < 8 ? c.x : c.y;
+            const float v = e2m1_to_f32((word >> (4 * (i & 7))) & 15u) * s;
+            const uint32_t bb = __float_as_uint(v) >> 16;          // exact bf16
+            if (i & 1) kb[i >> 1] |= bb << 16; else kb[i >> 1] = bb;
+            const _Float16 hv = (_Float16)v;                         // exact fp16
+            Vt[(16 * grp + i) * VT_LD + j] = __builtin_bit_cast(uint16_t, hv);
+        }
+        uint4* kd = (uint4*)(Kt + j * KT_LD + 16 * grp);
+        kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
+        kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
+    }
+}
+
+// Load + dequantise one chunk of window entries (8-bit E4M3 x 2^e).
+__device__ __forceinline__ void dequant_swa_chunk(const AttnArgs& a, int64_t first, int nent,
+                                                  uint16_t* Kt, uint16_t* Vt, int wave, int W, int l) {
+    const int j = l;
+    const bool valid = j < nent;
+    const int64_t ent = first + j;
+    for (int grp = wave; grp < 32; grp += W) {
+        uint4 c = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t sc = 127u;
+        if (valid) {
+            c = *(const uint4*)(a.swa_codes + ent * 512 + 16 * grp);
+            sc = a.swa_scales[ent * 32 + grp];
+        }
+        const float s = e8m0_to_f32(sc);
+        const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+        uint32_t kb[8];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float v = e4m3_to_f32((words[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
+            const uint32_t bb = __float_as_uint(v) >> 16;          // exact bf16
+            if (i & 1) kb[i >> 1] |= bb << 16; else kb[i >> 1] = bb;
+            Vt[(16 * grp + i) * VT_LD + j] = (uint16_t)bb;
+        }
+        uint4* kd = (uint4*)(Kt + j * KT_LD + 16 * grp);
+        kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
+        kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
+    }
+}
+
+// Workgroup = (split, row, group of up to 64 heads); one wave per 16 heads, at
+// most 4 waves so that a wave may hold its accumulators in the full register
+// file (VGPRs + AGPRs) at one wave per SIMD.
 template <bool QBF16>
-__global__ __launch_bounds__(512) void sparse_split_kernel(KvView kv, SparseAttnArgs a) {
+__global__ __launch_bounds__(256) void attn_kernel(KvView kv, AttnArgs a) {
     extern __shared__ __align__(16) uint8_t at_smem[];
     uint16_t* Kt = (uint16_t*)at_smem;
     uint16_t* Vt = Kt + AT_ENT * KT_LD;
     const int row = blockIdx.y, split = blockIdx.x;
-    const int H = a.n_heads, W = H >> 4;
+    const int H = a.n_heads, W = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int n = l & 15, g = l >> 4;
-    const int cnt = a.idx_count[row];
-    const int e0 = split * AT_ENT;
-    const int nent = min(max(cnt - e0, 0), AT_ENT);
-    const size_t pbase = ((size_t)row * AT_SPLITS + split) * H;
-    float* wsO = a.ws;
-    float* wsM = a.ws + (size_t)a.n_rows * AT_SPLITS * H * 512;
-    float* wsL = wsM + (size_t)a.n_rows * AT_SPLITS * H;
-    if (nent == 0) {
-        for (int h = threadIdx.x; h < H; h += blockDim.x) { wsM[pbase + h] = -INFINITY; wsL[pbase + h] = 0.0f; }
-        return;
-    }
-    // ---- gather + dequantise: lane = entry, groups strided over waves
-    {
-        const int j = l;
-        const bool valid = j < nent;
-        int64_t ent = 0;
-        if (valid) ent = entry_of(kv, a.req[row], a.idx[(int64_t)row * a.idx_stride + e0 + j]);
-        for (int grp = wave; grp < 32; grp += W) {
-            uint2 c = make_uint2(0u, 0u);
-            uint32_t sc = 0u;
-            if (valid) {
-                c = *(const uint2*)(kv.main_codes + ent * 256 + 8 * grp);
-                sc = kv.main_scales[ent * 32 + grp];
-            }
-            const float s = e4m3_to_f32(sc);
-            uint32_t kb[8];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t word = i < 8 ? c.x : c.y;
-                const float v = e2m1_to_f32((word >> (4 * (i & 7))) & 15u) * s;
-                const uint32_t bb = __float_as_uint(v) >> 16;          // exact bf16
-                if (i & 1) kb[i >> 1] |= bb << 16; else kb[i >> 1] = bb;
-                const _Float16 hv = (_Float16)v;                         // exact fp16
-                Vt[(16 * grp + i) * VT_LD + j] = *(const uint16_t*)&hv;
-            }
-            uint4* kd = (uint4*)(Kt + j * KT_LD + 16 * grp);
-            kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
-            kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
-        }
-    }
-    __syncthreads();
-    const int h0 = wave * 16;
-    bf16x8 qv[16];
-    load_q_operand<QBF16>(a.q, (int64_t)row * H + h0, n, g, qv);
-    f32x4 acc[4];
-    qk_tiles(Kt, qv, n, g, acc);
-    // ---- softmax over the 64 entries of this split (column = head n)
-    float m = -INFINITY;
-#pragma unroll
-    for (int et = 0; et < 4; ++et)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 16 * et + 4 * g + i;
-            const float z = e < nent ? acc[et][i] * a.scale : -INFINITY;
-            acc[et][i] = z;
-            m = fmaxf(m, z);
-        }
-    m = fmaxf(m, shfl_xor_f(m, 16));
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    float lsum = 0.0f;
-#pragma unroll
-    for (int et = 0; et < 4; ++et)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = expf(acc[et][i] - m);
-            acc[et][i] = p;
-            lsum += p;
-        }
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
-    f16x8 pb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pb[u][i] = (_Float16)acc[2 * u][i];
-            pb[u][4 + i] = (_Float16)acc[2 * u + 1][i];
-        }
-    // ---- O^T = V^T P^T, 32 channel tiles
-    float* orow = wsO + (pbase + h0 + n) * 512;
-#pragma unroll 4
-    for (int ct = 0; ct < 32; ++ct) {
-        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint4 av = vt_operand(Vt, ct, u, n, g);
-            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const f16x8*)&av, pb[u], o, 0, 0, 0);
-        }
-        *(float4*)(orow + 16 * ct + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
-    }
-    if (g == 0) { wsM[pbase + h0 + n] = m; wsL[pbase + h0 + n] = lsum; }
-}
+    const int h0 = blockIdx.z * 64 + wave * 16;
+    const int nsp = a.idx ? min(a.idx_count[row], 512) : 0;
+    const int nsw = a.swa_codes ? min(a.swa_count[row], 128) : 0;
+    const int csp = (nsp + AT_ENT - 1) / AT_ENT;
+    const int ctot = csp + (nsw + AT_ENT - 1) / AT_ENT;
+    const int per = (ctot + a.n_splits - 1) / a.n_splits;
+    const int cb = min(split * per, ctot), ce = min(cb + per, ctot);
 
-// --------------------------------------------------------------- split merge
-// o[row][h][c] = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s; lse = M + ln(.)
-__global__ __launch_bounds__(256) void sparse_merge_kernel(SparseAttnArgs a) {
-    const int H = a.n_heads;
-    const int row = blockIdx.y;
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;   // (head, 4-channel group)
-    if (t >= H * 128) return;
-    const int h = t >> 7, c4 = t & 127;
-    const float* wsO = a.ws;
-    const float* wsM = a.ws + (size_t)a.n_rows * AT_SPLITS * H * 512;
-    const float* wsL = wsM + (size_t)a.n_rows * AT_SPLITS * H;
-    float ms[AT_SPLITS];
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < AT_SPLITS; ++s) {
-        ms[s] = wsM[((size_t)row * AT_SPLITS + s) * H + h];
-        M = fmaxf(M, ms[s]);
-    }
-    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float L = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int s = 0; s < AT_SPLITS; ++s) {
-            if (ms[s] == -INFINITY) continue;
-            const size_t ps = ((size_t)row * AT_SPLITS + s) * H + h;
-            const float wgt = expf(ms[s] - M);
-            L += wgt * wsL[ps];
-            const float4 v = *(const float4*)(wsO + ps * 512 + 4 * c4);
-            o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
-        }
-        const float inv = 1.0f / L;
-        o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-    }
-    *(float4*)(a.o + ((size_t)row * H + h) * 512 + 4 * c4) = o;
-    if (c4 == 0) a.lse[(size_t)row * H + h] = (M == -INFINITY) ? -INFINITY : M + logf(L);
-}
-
-// --------------------------------------------------------------- window + merge
-template <bool QBF16>
-__global__ __launch_bounds__(512) void swa_merge_kernel(SwaArgs a) {
-    extern __shared__ __align__(16) uint8_t at_smem[];
-    uint16_t* Kt = (uint16_t*)at_smem;
-    uint16_t* Vt = Kt + AT_ENT * KT_LD;
-    const int row = blockIdx.x;
-    const int H = a.n_heads, W = H >> 4;
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int n = l & 15, g = l >> 4;
-    const int h0 = wave * 16;
-    const int cnt = min(a.count[row], 128);
-    const int64_t first = a.first[row];
     bf16x8 qv[16];
     load_q_operand<QBF16>(a.q, (int64_t)row * H + h0, n, g, qv);
     f32x4 oacc[32];
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;
-    for (int c0 = 0; c0 < cnt; c0 += AT_ENT) {
-        const int nent = min(cnt - c0, AT_ENT);
+
+    for (int c = cb; c < ce; ++c) {
+        const bool is_sw = c >= csp;
+        const int e0 = is_sw ? (c - csp) * AT_ENT : c * AT_ENT;
+        const int nent = min((is_sw ? nsw : nsp) - e0, AT_ENT);
         __syncthreads();                               // previous chunk fully consumed
-        {
-            const int j = l;
-            const bool valid = j < nent;
-            const int64_t ent = first + c0 + j;
-            for (int grp = wave; grp < 32; grp += W) {
-                uint4 c = make_uint4(0u, 0u, 0u, 0u);
-                uint32_t sc = 127u;
-                if (valid) {
-                    c = *(const uint4*)(a.codes + ent * 512 + 16 * grp);
-                    sc = a.scales[ent * 32 + grp];
-                }
-                const float s = e8m0_to_f32(sc);
-                const uint32_t words[4] = {c.x, c.y, c.z, c.w};
-                uint32_t kb[8];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float v = e4m3_to_f32((words[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
-                    const uint32_t bb = __float_as_uint(v) >> 16;      // exact bf16
-                    if (i & 1) kb[i >> 1] |= bb << 16; else kb[i >> 1] = bb;
-                    Vt[(16 * grp + i) * VT_LD + j] = (uint16_t)bb;
-                }
-                uint4* kd = (uint4*)(Kt + j * KT_LD + 16 * grp);
-                kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
-                kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
-            }
-        }
+        if (is_sw) dequant_swa_chunk(a, a.swa_first[row] + e0, nent, Kt, Vt, wave, W, l);
+        else dequant_main_chunk(kv, a, row, e0, nent, Kt, Vt, wave, W, l);
         __syncthreads();
+        // ---- S^T tiles: acc[et][i] = K[16et + 4g + i] . q[head n]
         f32x4 acc[4];
-        qk_tiles(Kt, qv, n, g, acc);
+#pragma unroll
+        for (int et = 0; et < 4; ++et) {
+            f32x4 cc = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint16_t* base = Kt + (16 * et + n) * KT_LD + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks)
+                cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(base + 32 * ks), qv[ks], cc, 0, 0, 0);
+            acc[et] = cc;
+        }
+        // ---- online softmax (column = head)
         float m = -INFINITY;
 #pragma unroll
         for (int et = 0; et < 4; ++et)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = 16 * et + 4 * g + i;
-                const float z = e < nent ? acc[et][i] * a.scale : -INFINITY;
+                const float z = (16 * et + 4 * g + i) < nent ? acc[et][i] * a.scale : -INFINITY;
                 acc[et][i] = z;
                 m = fmaxf(m, z);
             }
@@ -308,53 +216,132 @@ __global__ __launch_bounds__(512) void swa_merge_kernel(SwaArgs a) {
         lsum += shfl_xor_f(lsum, 32);
         l_run = l_run * alpha + lsum;
         m_run = m_new;
-        bf16x8 phi[2], plo[2];
+        // ---- O^T += V^T P^T
+        if (!is_sw) {
+            f16x8 pb[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = acc[2 * u + (i >> 2)][i & 3];
-                const uint32_t hb = f32_to_bf16_rne(p);
-                const float rest = p - __uint_as_float(hb << 16);
-                const uint32_t lb = f32_to_bf16_rne(rest);
-                phi[u][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-                plo[u][i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
+                for (int i = 0; i < 8; ++i) pb[u][i] = (_Float16)acc[2 * u + (i >> 2)][i & 3];
+#pragma unroll
+            for (int ct = 0; ct < 32; ++ct) {
+                f32x4 o = oacc[ct] * alpha;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint4 av = vt_operand(Vt, ct, u, n, g);
+                    o = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const f16x8*)&av, pb[u], o, 0, 0, 0);
+                }
+                oacc[ct] = o;
             }
+        } else {
+            bf16x8 phi[2], plo[2];
 #pragma unroll
-        for (int ct = 0; ct < 32; ++ct) {
-            f32x4 o = oacc[ct] * alpha;
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint4 av = vt_operand(Vt, ct, u, n, g);
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&av, phi[u], o, 0, 0, 0);
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&av, plo[u], o, 0, 0, 0);
+                for (int i = 0; i < 8; ++i) {
+                    const float p = acc[2 * u + (i >> 2)][i & 3];
+                    const uint32_t hb = f32_to_bf16_rne(p);
+                    const uint32_t lb = f32_to_bf16_rne(p - __uint_as_float(hb << 16));
+                    phi[u][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+                    plo[u][i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
+                }
+#pragma unroll
+            for (int ct = 0; ct < 32; ++ct) {
+                f32x4 o = oacc[ct] * alpha;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint4 av = vt_operand(Vt, ct, u, n, g);
+                    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&av, phi[u], o, 0, 0, 0);
+                    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&av, plo[u], o, 0, 0, 0);
+                }
+                oacc[ct] = o;
             }
-            oacc[ct] = o;
         }
     }
-    // ---- merge with the sparse branch and the sink (column = head h0 + n)
+
     const int h = h0 + n;
+    if (a.n_splits > 1) {
+        // partial (max, sum, unnormalised O) of this split
+        const size_t ps = ((size_t)row * a.n_splits + split) * H + h;
+        float* wsO = a.ws;
+        float* wsM = a.ws + (size_t)a.n_rows * a.n_splits * H * 512;
+        float* wsL = wsM + (size_t)a.n_rows * a.n_splits * H;
+        if (cb < ce) {
+            float* orow = wsO + ps * 512;
+#pragma unroll
+            for (int ct = 0; ct < 32; ++ct)
+                *(float4*)(orow + 16 * ct + 4 * g) = make_float4(oacc[ct][0], oacc[ct][1], oacc[ct][2], oacc[ct][3]);
+        }
+        if (g == 0) { wsM[ps] = m_run; wsL[ps] = l_run; }
+        return;
+    }
+    // ---- single split: merge with the external partial and the sink here
     const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * H + h] : -INFINITY;
     const float sk = a.sink ? a.sink[h] : -INFINITY;
     const float M = fmaxf(fmaxf(m_run, lse_p), sk);
-    const float w_sw = (m_run == -INFINITY) ? 0.0f : expf(m_run - M);
+    const float w_run = (m_run == -INFINITY) ? 0.0f : expf(m_run - M);
     const float w_p = (lse_p == -INFINITY) ? 0.0f : expf(lse_p - M);
     const float w_s = (sk == -INFINITY) ? 0.0f : expf(sk - M);
-    const float den = w_sw * l_run + w_p + w_s;
+    const float den = w_run * l_run + w_p + w_s;
     const float inv = (M == -INFINITY || den == 0.0f) ? 0.0f : 1.0f / den;
     const float* oin = a.o_in ? a.o_in + ((int64_t)row * H + h) * 512 : nullptr;
     float* orow = a.out + ((int64_t)row * H + h) * 512;
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct) {
         const int c = 16 * ct + 4 * g;
+        const float4 pin = oin ? *(const float4*)(oin + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         float4 r;
-        float4 pin = oin ? *(const float4*)(oin + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        r.x = (w_sw * oacc[ct][0] + w_p * pin.x) * inv;
-        r.y = (w_sw * oacc[ct][1] + w_p * pin.y) * inv;
-        r.z = (w_sw * oacc[ct][2] + w_p * pin.z) * inv;
-        r.w = (w_sw * oacc[ct][3] + w_p * pin.w) * inv;
+        r.x = (w_run * oacc[ct][0] + w_p * pin.x) * inv;
+        r.y = (w_run * oacc[ct][1] + w_p * pin.y) * inv;
+        r.z = (w_run * oacc[ct][2] + w_p * pin.z) * inv;
+        r.w = (w_run * oacc[ct][3] + w_p * pin.w) * inv;
         *(float4*)(orow + c) = r;
     }
+    if (a.lse_out && g == 0) a.lse_out[(int64_t)row * H + h] = (M == -INFINITY || den == 0.0f) ? -INFINITY : M + logf(den);
+}
+
+// out = (sum_s e^(m_s - M) O_s + e^(lse_in - M) o_in) / (sum_s e^(m_s - M) l_s + e^(lse_in - M) + e^(sink - M))
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    const int H = a.n_heads, S = a.n_splits;
+    const int row = blockIdx.y;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;   // (head, 4-channel group)
+    if (t >= H * 128) return;
+    const int h = t >> 7, c4 = t & 127;
+    const float* wsO = a.ws;
+    const float* wsM = a.ws + (size_t)a.n_rows * S * H * 512;
+    const float* wsL = wsM + (size_t)a.n_rows * S * H;
+    float ms[AT_MAX_SPLITS];
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) {
+        ms[s] = wsM[((size_t)row * S + s) * H + h];
+        M = fmaxf(M, ms[s]);
+    }
+    const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * H + h] : -INFINITY;
+    const float sk = a.sink ? a.sink[h] : -INFINITY;
+    M = fmaxf(fmaxf(M, lse_p), sk);
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float den = 0.0f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < S; ++s) {
+            if (ms[s] == -INFINITY) continue;
+            const size_t ps = ((size_t)row * S + s) * H + h;
+            const float wgt = expf(ms[s] - M);
+            den += wgt * wsL[ps];
+            const float4 v = *(const float4*)(wsO + ps * 512 + 4 * c4);
+            o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
+        }
+        if (lse_p != -INFINITY) {
+            const float wgt = expf(lse_p - M);
+            den += wgt;
+            const float4 v = *(const float4*)(a.o_in + ((int64_t)row * H + h) * 512 + 4 * c4);
+            o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
+        }
+        if (sk != -INFINITY) den += expf(sk - M);
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+    *(float4*)(a.out + ((int64_t)row * H + h) * 512 + 4 * c4) = o;
+    if (a.lse_out && c4 == 0) a.lse_out[(int64_t)row * H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
 }
 
 static bool g_attr_set = false;
@@ -362,33 +349,30 @@ static bool g_attr_set = false;
 static hipError_t set_lds_attrs() {
     if (g_attr_set) return hipSuccess;
     hipError_t e;
-    if ((e = hipFuncSetAttribute((const void*)sparse_split_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void*)sparse_split_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void*)swa_merge_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void*)swa_merge_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void*)attn_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void*)attn_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
     g_attr_set = true;
     return hipSuccess;
 }
 
-hipError_t launch_sparse_attn(const KvView& kv, const SparseAttnArgs& a, hipStream_t st) {
+hipError_t launch_attn(const KvView& kv, const AttnArgs& a_in, hipStream_t st) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
-    const dim3 grid(AT_SPLITS, (unsigned)a.n_rows), block((unsigned)(4 * a.n_heads));
-    if (a.q_bf16) hipLaunchKernelGGL(sparse_split_kernel<true>, grid, block, AT_LDS, st, kv, a);
-    else hipLaunchKernelGGL(sparse_split_kernel<false>, grid, block, AT_LDS, st, kv, a);
+    AttnArgs a = a_in;
+    a.n_splits = attn_splits(a.n_rows);
+    if (a.n_splits > a.max_chunks) a.n_splits = a.max_chunks > 0 ? a.max_chunks : 1;
+    const int hg = (a.n_heads + 63) / 64;
+    const dim3 grid((unsigned)a.n_splits, (unsigned)a.n_rows, (unsigned)hg);
+    const dim3 block((unsigned)(4 * (a.n_heads < 64 ? a.n_heads : 64)));
+    if (a.q_bf16) hipLaunchKernelGGL(attn_kernel<true>, grid, block, AT_LDS, st, kv, a);
+    else hipLaunchKernelGGL(attn_kernel<false>, grid, block, AT_LDS, st, kv, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 mgrid((unsigned)((a.n_heads * 128 + 255) / 256), (unsigned)a.n_rows);
-    hipLaunchKernelGGL(sparse_merge_kernel, mgrid, dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_swa_merge(const SwaArgs& a, hipStream_t st) {
-    hipError_t e = set_lds_attrs();
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)a.n_rows), block((unsigned)(4 * a.n_heads));
-    if (a.q_bf16) hipLaunchKernelGGL(swa_merge_kernel<true>, grid, block, AT_LDS, st, a);
-    else hipLaunchKernelGGL(swa_merge_kernel<false>, grid, block, AT_LDS, st, a);
-    return hipGetLastError();
+    if (a.n_splits > 1) {
+        const dim3 mgrid((unsigned)((a.n_heads * 128 + 255) / 256), (unsigned)a.n_rows);
+        hipLaunchKernelGGL(attn_merge_kernel, mgrid, dim3(256), 0, st, a);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace csa2

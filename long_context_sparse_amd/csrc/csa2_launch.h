@@ -46,39 +46,33 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
-struct SparseAttnArgs {
+// Joint attention over a row's selected FP4 entries (idx) and its 8-bit
+// window (swa_*), plus an optional external partial (o_in, lse_in) and sink.
+struct AttnArgs {
     const void* q;
     bool q_bf16;
     int n_heads;
     const int32_t* req;
     int n_rows;
-    const int32_t* idx;
+    const int32_t* idx;          // NULL: no selected entries
     int64_t idx_stride;
     const int32_t* idx_count;
-    float scale;
-    float* o;
-    float* lse;
-    float* ws;
-};
-size_t sparse_attn_workspace_bytes(int n_rows, int n_heads);
-hipError_t launch_sparse_attn(const KvView& kv, const SparseAttnArgs& a, hipStream_t st);
-
-struct SwaArgs {
-    const uint8_t* codes;
-    const uint8_t* scales;
-    const int64_t* first;
-    const int32_t* count;
-    int n_rows;
-    const void* q;
-    bool q_bf16;
-    int n_heads;
+    const uint8_t* swa_codes;    // NULL: no window
+    const uint8_t* swa_scales;
+    const int64_t* swa_first;
+    const int32_t* swa_count;
     float scale;
     const float* sink;
     const float* o_in;
     const float* lse_in;
     float* out;
+    float* lse_out;
+    float* ws;
+    int n_splits;                // set by launch_attn
+    int max_chunks;              // upper bound on 64-entry chunks per row
 };
-hipError_t launch_swa_merge(const SwaArgs& a, hipStream_t st);
+size_t attn_workspace_bytes(int n_rows, int n_heads);
+hipError_t launch_attn(const KvView& kv, const AttnArgs& a, hipStream_t st);
 
 hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,
                                void* out, hipStream_t st);

@@ -24,19 +24,22 @@
 //     every partial sum is a multiple of 2^Emin below 2^(Emin+24), so fp32
 //     accumulation in any order is exact and the MFMA result is the exactly
 //     rounded value.  A per-key guard checks this (plus a range that keeps
-//     every term a normal fp32); keys outside it are re-scored by an exact
-//     integer path on the VALU.
-//   * The fma fold follows the MFMA output layout: lanes 16g..16g+15 hold
-//     heads 4g..4g+3 of the 16 keys; each lane group continues the chain
-//     handed over by the previous one.
+//     every term a normal fp32); the 8-blocks of keys outside it are queued in
+//     LDS and re-scored after the main loop by an exact integer path.
+//   * Each MFMA row group (rows 4g..4g+3) is given the same 4 query heads, so
+//     every lane receives those 4 heads of its key; ceil(n_heads/4) MFMAs per
+//     16 keys hand each lane all heads of its key, and the sequential fma fold
+//     runs inside the lane with no cross-lane traffic.  The block maximum over
+//     8 aligned keys uses DPP row shifts.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
 namespace csa2 {
 
 constexpr int IS_WAVES = 4;
-constexpr int IS_TILES = 8;                          // 16-key tiles per wave
-constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16;   // columns per workgroup
+constexpr int IS_TILES = 4;                          // 16-key tiles per batch
+constexpr int IS_ITERS = 4;                          // batches per wave (even)
+constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16 * IS_ITERS;   // columns per workgroup
 
 struct QShared {
     uint8_t codes[16][64];
@@ -45,6 +48,8 @@ struct QShared {
     int spread;   // max over real heads of (max - min) block scale code
     int smin;     // min block scale code over real heads
     int smax;     // max block scale code over real heads
+    int n_fix;    // queued 8-blocks that need the exact path
+    int fix[IS_CHUNK];
 };
 
 // Doubled E2M1 value of a code, as an integer in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}.
@@ -56,7 +61,7 @@ __device__ __forceinline__ int e2m1_x2(uint32_t nib) {
 
 // Round-to-nearest-even fp32 of sum_t S[t] * 2^E[t] (4 terms, |S| < 2^20,
 // -256 <= E <= 252), through a 576-bit two's-complement fixed point.
-__device__ __noinline__ float round_pow2_sum4(const int* S, const int* E) {
+__device__ float round_pow2_sum4(const int* S, const int* E) {
     constexpr int NW = 9, OFF = 264;
     uint64_t L[NW];
 #pragma unroll
@@ -111,7 +116,7 @@ __device__ __noinline__ float round_pow2_sum4(const int* S, const int* E) {
 }
 
 // Exact score of one key (used where the MFMA exactness guard fails).
-__device__ __noinline__ float exact_key_score(const QShared& qs, int n_heads, const uint8_t* kc, const uint8_t* ks) {
+__device__ float exact_key_score(const QShared& qs, int n_heads, const uint8_t* kc, const uint8_t* ks) {
     uint8_t key[64];
     for (int i = 0; i < 64; ++i) key[i] = kc[i];
     int kscale[4];
@@ -188,7 +193,47 @@ __device__ void prep_query(QShared& qs, const void* q_idx, const float* w, int r
     if (l == 0) { qs.spread = spread; qs.smin = smin; qs.smax = smax; }
 }
 
-template <bool QBF16, bool POOL>
+// Keys of one batch (IS_TILES tiles of 16) for one lane: 16 code bytes and the
+// key's scale dword per tile.
+struct KeyBatch {
+    uint4 code[IS_TILES];
+    uint32_t scl[IS_TILES];
+};
+
+template <bool POOL>
+__device__ __forceinline__ int col_pos(const int32_t* pool, int col) {
+    return POOL ? 8 * pool[col >> 3] + (col & 7) : col;
+}
+
+// Issue the loads of one batch of this wave (columns clamped into range).
+template <bool POOL>
+__device__ __forceinline__ void load_batch(const KvView& kv, int req, const int32_t* pool, int nv, int ncols,
+                                           int col_base, int n, int lg, KeyBatch& kb) {
+#pragma unroll
+    for (int t = 0; t < IS_TILES; ++t) {
+        const int col0 = col_base + 16 * t;
+        const int c0 = col0 < ncols ? col0 : 0;         // column 0 is always valid when ncols > 0
+        const int col = col0 + n < ncols ? col0 + n : c0;
+        int ld = col_pos<POOL>(pool, col);
+        if (POOL && ld >= nv) ld = 8 * pool[col >> 3];   // a visible position of the same block
+        const int64_t e = entry_of(kv, req, ld);
+        kb.code[t] = *(const uint4*)(kv.idx_codes + e * 64 + 16 * lg);
+        kb.scl[t] = *(const uint32_t*)(kv.idx_scales + e * 4);
+    }
+}
+
+__device__ __forceinline__ float dpp_row_shr_max(float v, int shift) {
+    int src = __builtin_bit_cast(int, v);
+    int sh;
+    switch (shift) {   // DPP control must be a constant
+        case 1: sh = __builtin_amdgcn_update_dpp(src, src, 0x111, 0xF, 0xF, false); break;
+        case 2: sh = __builtin_amdgcn_update_dpp(src, src, 0x112, 0xF, 0xF, false); break;
+        default: sh = __builtin_amdgcn_update_dpp(src, src, 0x114, 0xF, 0xF, false); break;
+    }
+    return fmaxf(v, __builtin_bit_cast(float, sh));
+}
+
+template <bool QBF16, bool POOL, int NM>
 __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, IndexScoreArgs a) {
     __shared__ QShared qs;
     const int row = blockIdx.y;
@@ -199,109 +244,136 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     if (chunk0 >= ncols) return;                       // uniform over the workgroup
     const int req = a.req[row];
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int n = l & 15, lg = l >> 4;
+    const int32_t* pool = POOL ? a.pool + (int64_t)row * a.pool_stride : nullptr;
+    // a wave's batch b covers columns wbase + b * BSTRIDE + [0, 16 * IS_TILES)
+    const int wbase = chunk0 + wave * IS_TILES * 16;
+    constexpr int BSTRIDE = IS_WAVES * IS_TILES * 16;
+
+    KeyBatch A, B;
+    load_batch<POOL>(kv, req, pool, nv, ncols, wbase, n, lg, A);   // in flight during the query prep
     if (wave == 0) prep_query<QBF16>(qs, a.q_idx, a.w, row, a.n_heads);
+    if (threadIdx.x == 0) qs.n_fix = 0;
     __syncthreads();
 
-    const int n = l & 15, lg = l >> 4;
-    const int NG = (a.n_heads + 3) >> 2;               // lane groups holding real heads
-    i32x8 A = {0, 0, 0, 0, 0, 0, 0, 0};
-    {
-        const uint4 v = *(const uint4*)&qs.codes[n][16 * lg];
-        A[0] = (int)v.x; A[1] = (int)v.y; A[2] = (int)v.z; A[3] = (int)v.w;
-    }
-    const int sa = qs.scales[n][lg];
-    float wl[4];
+    // MFMA k takes heads 4k .. 4k+3 on every row group: row n carries head 4k + (n & 3)
+    i32x8 Aq[NM];
+    int sa[NM];
+    float wl[4 * NM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wl[i] = qs.w[min(4 * lg + i, 15)] * (4 * lg + i < a.n_heads ? 1.0f : 0.0f);
+    for (int k = 0; k < NM; ++k) {
+        const int h = 4 * k + (n & 3);
+        const uint4 v = *(const uint4*)&qs.codes[h][16 * lg];
+        Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sa[k] = qs.scales[h][lg];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.w[4 * k + i];   // 0 above n_heads
+    }
     const int qspread = qs.spread, qmin = qs.smin, qmax = qs.smax;
-    const int32_t* pool = POOL ? a.pool + (int64_t)row * a.pool_stride : nullptr;
     float* srow = a.scores ? a.scores + (int64_t)row * a.scores_stride : nullptr;
     float* brow = (!POOL && a.block_max) ? a.block_max + (int64_t)row * a.block_max_stride : nullptr;
     const int nv8 = (nv + 7) & ~7;
+    const bool writer = lg == 0;                       // the 4 row groups hold identical results
 
-    // ---- issue the loads of all tiles first
-    uint4 kcode[IS_TILES];
-    uint32_t kscl[IS_TILES];
-    int kpos[IS_TILES];
-    int64_t kent[IS_TILES];
+    auto compute = [&](const KeyBatch& kb, int col_base) {
 #pragma unroll
-    for (int t = 0; t < IS_TILES; ++t) {
-        const int col0 = chunk0 + (wave * IS_TILES + t) * 16;
-        const int col = col0 + n;
-        const int c0 = col0 < ncols ? col0 : chunk0;
-        int pos, ld;
-        if (POOL) {
-            const int cc = col < ncols ? col : c0;
-            pos = col < ncols ? 8 * pool[col >> 3] + (col & 7) : 0x7FFFFFFF;
-            ld = 8 * pool[cc >> 3] + (cc & 7);
-            if (ld >= nv) ld = 8 * pool[cc >> 3];      // a visible position of the same block
-        } else {
-            pos = col;
-            ld = col < nv ? col : c0;
+        for (int t = 0; t < IS_TILES; ++t) {
+            const int col0 = col_base + 16 * t;
+            if (col0 >= ncols) break;
+            const i32x8 Bk = {(int)kb.code[t].x, (int)kb.code[t].y, (int)kb.code[t].z, (int)kb.code[t].w, 0, 0, 0, 0};
+            const uint32_t sd = kb.scl[t];
+            const int sb = (int)((sd >> (8 * lg)) & 0xFFu);
+            f32x4 d[NM];
+#pragma unroll
+            for (int k = 0; k < NM; ++k) {
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[k], Bk, z, 4, 4, 0, sa[k], 0, sb);
+            }
+            const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
+            const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
+            const bool ok = (kmax - kmin + qspread <= 9) && (qmin + kmin >= 136) && (qmax + kmax <= 356);
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NM; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = fmaf(wl[4 * k + i], d[k][i] > 0.0f ? d[k][i] : 0.0f, acc);
+            acc = (acc == 0.0f) ? 0.0f : acc;
+            const int col = col0 + n;
+            const bool in_cols = col < ncols;
+            // full scan: the position is the column (padding up to a multiple of 8 gets -inf)
+            const int pos = POOL ? (in_cols ? col_pos<POOL>(pool, col) : 0x7FFFFFFF) : col;
+            if (__builtin_expect(__any(!ok), 0)) {
+                if (writer && !ok && in_cols && pos < nv) qs.fix[atomicAdd(&qs.n_fix, 1)] = col & ~7;
+            }
+            const float val = (in_cols && pos < nv) ? acc : -INFINITY;
+            if (srow && writer) {
+                if (POOL) { if (in_cols) srow[col] = val; }
+                else if (pos < nv8) srow[pos] = val;
+            }
+            if (!POOL && brow) {
+                float bm = dpp_row_shr_max(val, 1);
+                bm = dpp_row_shr_max(bm, 2);
+                bm = dpp_row_shr_max(bm, 4);
+                // lanes 7 and 15 of the row now hold the maxima of keys 0..7 and 8..15
+                if (writer && (n & 7) == 7 && (pos & ~7) < nv) brow[pos >> 3] = bm;
+            }
         }
-        kpos[t] = pos;
-        const int64_t e = entry_of(kv, req, ld);
-        kent[t] = e;
-        kcode[t] = *(const uint4*)(kv.idx_codes + e * 64 + 16 * lg);
-        kscl[t] = *(const uint32_t*)(kv.idx_scales + e * 4);
+    };
+
+    for (int b = 0; b < IS_ITERS; b += 2) {
+        const int c_a = wbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
+        if (c_b < ncols) load_batch<POOL>(kv, req, pool, nv, ncols, c_b, n, lg, B);
+        compute(A, c_a);
+        if (c_b >= ncols) break;
+        const int c_n = c_b + BSTRIDE;
+        if (b + 2 < IS_ITERS && c_n < ncols) load_batch<POOL>(kv, req, pool, nv, ncols, c_n, n, lg, A);
+        compute(B, c_b);
+        if (c_n >= ncols) break;
     }
 
-    // ---- contraction, exactness guard, head fold, outputs
-#pragma unroll
-    for (int t = 0; t < IS_TILES; ++t) {
-        const int col0 = chunk0 + (wave * IS_TILES + t) * 16;
-        if (col0 >= ncols) break;
-        i32x8 B = {(int)kcode[t].x, (int)kcode[t].y, (int)kcode[t].z, (int)kcode[t].w, 0, 0, 0, 0};
-        const int sb = (int)((kscl[t] >> (8 * lg)) & 0xFFu);
-        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-        d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, d, 4, 4, 0, sa, 0, sb);
+    // ---- exact path for the queued 8-blocks (first column of each)
+    __syncthreads();
+    const int nfix = qs.n_fix;
+    for (int i = threadIdx.x; i < nfix; i += blockDim.x) {
+        const int c8 = qs.fix[i];
+        float bm = -INFINITY;
+        for (int j = 0; j < 8; ++j) {
+            const int col = c8 + j;
+            if (col >= ncols) break;
+            const int pos = col_pos<POOL>(pool, col);
+            float v = -INFINITY;
+            if (pos < nv) {
+                const int64_t e = entry_of(kv, req, pos);
+                v = exact_key_score(qs, a.n_heads, kv.idx_codes + e * 64, kv.idx_scales + e * 4);
+            }
+            if (srow) srow[col] = v;                   // col == pos in a full scan
+            bm = fmaxf(bm, v);
+        }
+        if (brow) brow[c8 >> 3] = bm;
+    }
+}
 
-        const int b0 = kscl[t] & 0xFF, b1 = (kscl[t] >> 8) & 0xFF, b2 = (kscl[t] >> 16) & 0xFF, b3 = kscl[t] >> 24;
-        const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
-        const bool ok = (kmax - kmin + qspread <= 9) && (qmin + kmin >= 136) && (qmax + kmax <= 356);
-
-        float acc = 0.0f;
-        for (int grp = 0; grp < NG; ++grp) {
-            const float prev = shfl_up_f(acc, 16);
-            float tt = grp == 0 ? 0.0f : prev;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tt = fmaf(wl[i], d[i] > 0.0f ? d[i] : 0.0f, tt);
-            acc = (lg == grp) ? tt : acc;
-        }
-        acc = (acc == 0.0f) ? 0.0f : acc;
-        const bool final_grp = (lg == NG - 1);
-        if (__builtin_expect(__any(!ok), 0)) {
-            if (final_grp && !ok)
-                acc = exact_key_score(qs, a.n_heads, kv.idx_codes + kent[t] * 64, kv.idx_scales + kent[t] * 4);
-        }
-        const int col = col0 + n;
-        const int pos = kpos[t];
-        const bool vis = POOL ? (col < ncols && pos < nv) : (pos < nv);
-        const float val = vis ? acc : -INFINITY;
-        if (srow && final_grp) {
-            if (POOL) { if (col < ncols) srow[col] = val; }
-            else if (pos < nv8) srow[pos] = val;
-        }
-        if (!POOL && brow) {
-            float bm = val;
-            bm = fmaxf(bm, shfl_xor_f(bm, 1));
-            bm = fmaxf(bm, shfl_xor_f(bm, 2));
-            bm = fmaxf(bm, shfl_xor_f(bm, 4));
-            if (final_grp && (n & 7) == 0 && pos < nv) brow[pos >> 3] = bm;
-        }
+template <bool QBF16, bool POOL>
+static void launch_nm(int nm, dim3 grid, dim3 block, hipStream_t st, const KvView& kv, const IndexScoreArgs& a) {
+    switch (nm) {
+        case 1: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 1>), grid, block, 0, st, kv, a); break;
+        case 2: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 2>), grid, block, 0, st, kv, a); break;
+        case 3: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 3>), grid, block, 0, st, kv, a); break;
+        default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4>), grid, block, 0, st, kv, a); break;
     }
 }
 
 hipError_t launch_index_score(const KvView& kv, const IndexScoreArgs& a, hipStream_t st) {
     const bool pool = a.pool != nullptr;
     const int cols = pool ? 8 * 2048 : a.max_vis;
+    const int nm = (a.n_heads + 3) / 4;
     const dim3 grid((unsigned)((cols + IS_CHUNK - 1) / IS_CHUNK), (unsigned)a.n_rows), block(IS_WAVES * 64);
     if (a.q_bf16) {
-        if (pool) hipLaunchKernelGGL((index_score_kernel<true, true>), grid, block, 0, st, kv, a);
-        else hipLaunchKernelGGL((index_score_kernel<true, false>), grid, block, 0, st, kv, a);
+        if (pool) launch_nm<true, true>(nm, grid, block, st, kv, a);
+        else launch_nm<true, false>(nm, grid, block, st, kv, a);
     } else {
-        if (pool) hipLaunchKernelGGL((index_score_kernel<false, true>), grid, block, 0, st, kv, a);
-        else hipLaunchKernelGGL((index_score_kernel<false, false>), grid, block, 0, st, kv, a);
+        if (pool) launch_nm<false, true>(nm, grid, block, st, kv, a);
+        else launch_nm<false, false>(nm, grid, block, st, kv, a);
     }
     return hipGetLastError();
 }

@@ -7,12 +7,16 @@
 // are in id order, so ties go to the lower position / block.
 //
 // One 1024-thread workgroup per row.  Keys become order-preserving 32-bit
-// integers; an MSB-first radix select (four 8-bit digit passes over an LDS
-// histogram) finds the k-th key T and how many items equal to T are needed;
-// a block-wide scan in column order then writes the selected ids ascending.
-// Thread t owns columns [16t, 16t+16) of each 16,384-column sweep, so
-// "column order" is "thread order, then item order".  A row of at most
-// 16,384 columns stays in registers; longer rows are re-read per pass.
+// integers.  The bits above the highest bit in which the smallest and the
+// largest present key differ are common to every key and are skipped; an
+// MSB-first radix select then resolves 12, 10 and 10 bits per pass with an
+// LDS histogram of 4,096 bins (scores of one row share few exponent values,
+// so a digit that covers only exponent bits would send most atomics to one
+// bin; 12 bits reach into the mantissa), and stops as soon as the bin
+// holding the k-th key is taken whole.  A block-wide scan in column order
+// writes the selected ids ascending.  Thread t owns columns [16t, 16t+16) of
+// each 16,384-column sweep, so column order is thread order, then item order.
+// Rows of at most 16,384 columns stay in registers; longer rows are re-read.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -23,10 +27,13 @@ constexpr int TK_ITEMS = 16;
 constexpr int TK_SWEEP = TK_THREADS * TK_ITEMS;
 constexpr int TK_WAVES = TK_THREADS / 64;
 
+constexpr int TK_BINS = 4096;
+
 struct TkShared {
-    uint32_t hist[256];
+    uint32_t hist[TK_BINS];
     uint32_t part[TK_WAVES];
-    uint32_t digit, above;
+    uint32_t red[3][TK_WAVES];
+    uint32_t digit, above, count;
 };
 
 // Exclusive scan of v over the workgroup in thread order; `total` gets the sum.
@@ -56,18 +63,26 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
     return base + x - v;
 }
 
-__device__ __forceinline__ int col_id(const TopkArgs& a, const int32_t* pool, int c) {
+__device__ __forceinline__ int col_id(const int32_t* pool, int c) {
     return pool ? 8 * pool[c >> 3] + (c & 7) : c;
 }
 
 __device__ __forceinline__ void load_sweep(const TopkArgs& a, const float* krow, const int32_t* pool,
                                            int ncols, int sweep, uint32_t* u) {
     const int c0 = sweep * TK_SWEEP + threadIdx.x * TK_ITEMS;
+    if (!a.keys_by_id && c0 + TK_ITEMS <= ncols && ((uintptr_t)(krow + c0) & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; i += 4) {
+            const float4 v = *(const float4*)(krow + c0 + i);
+            u[i] = order_key(v.x); u[i + 1] = order_key(v.y); u[i + 2] = order_key(v.z); u[i + 3] = order_key(v.w);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TK_ITEMS; ++i) {
         const int c = c0 + i;
         uint32_t key = 0u;
-        if (c < ncols) key = order_key(krow[a.keys_by_id ? col_id(a, pool, c) : c]);
+        if (c < ncols) key = order_key(krow[a.keys_by_id ? col_id(pool, c) : c]);
         u[i] = key;
     }
 }
@@ -75,6 +90,7 @@ __device__ __forceinline__ void load_sweep(const TopkArgs& a, const float* krow,
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     __shared__ TkShared sh;
     const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int ncols = a.max_cols;
     if (a.n_cols) {
         const int64_t v = ((int64_t)a.n_cols[row] * a.cols_mul + a.cols_div - 1) / a.cols_div;
@@ -86,69 +102,106 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     int32_t* orow = a.out_ids + (int64_t)row * a.out_stride;
 
     uint32_t u[TK_ITEMS];
-    if (nsweep >= 1) load_sweep(a, krow, pool, ncols, 0, u);
-    else {
 #pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
-    }
+    for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
 
-    // number of present keys
-    uint32_t present = 0;
+    // ---- count, min and max of the present keys
+    uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
     for (int s = 0; s < nsweep; ++s) {
-        if (s > 0) load_sweep(a, krow, pool, ncols, s, u);
+        load_sweep(a, krow, pool, ncols, s, u);
 #pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i) present += u[i] != 0u;
+        for (int i = 0; i < TK_ITEMS; ++i)
+            if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
     }
-    uint32_t n_present;
-    block_excl_scan(present, sh.part, n_present);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        cnt += __shfl_xor(cnt, d, 64);
+        umin = min(umin, (uint32_t)__shfl_xor(umin, d, 64));
+        umax = max(umax, (uint32_t)__shfl_xor(umax, d, 64));
+    }
+    if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = umin; sh.red[2][wave] = umax; }
+    __syncthreads();
+    uint32_t n_present = 0;
+    umin = 0xFFFFFFFFu; umax = 0u;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+        n_present += sh.red[0][w];
+        umin = min(umin, sh.red[1][w]);
+        umax = max(umax, sh.red[2][w]);
+    }
 
-    uint32_t T = 0u, need_eq = 0u;
+    // ---- radix select: prefix/mask describe the bits decided so far
+    uint32_t prefix = 0u, mask = 0u, need = 0u;   // select (u & mask) > prefix, or == prefix for the first `need`
     if (n_present > (uint32_t)a.k) {
-        uint32_t prefix = 0u, mask = 0u, rem = (uint32_t)a.k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0u;
+        const uint32_t diff = umin ^ umax;
+        int hb = diff ? 31 - __clz(diff) : -1;   // highest bit that is not common to all keys
+        mask = hb < 0 ? 0xFFFFFFFFu : (hb >= 31 ? 0u : ~((2u << hb) - 1u));
+        prefix = umin & mask;
+        uint32_t rem = (uint32_t)a.k;
+        uint32_t in_bin = n_present;
+        int pass = 0;
+        while (hb >= 0 && in_bin != rem) {
+            const int wbits = pass == 0 ? 12 : 10;
+            const int shift = hb >= wbits - 1 ? hb - (wbits - 1) : 0;
+            const int width = hb - shift + 1;
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
             __syncthreads();
             for (int s = 0; s < nsweep; ++s) {
                 if (nsweep > 1) load_sweep(a, krow, pool, ncols, s, u);
 #pragma unroll
                 for (int i = 0; i < TK_ITEMS; ++i)
-                    if (u[i] != 0u && (u[i] & mask) == prefix) atomicAdd(&sh.hist[(u[i] >> shift) & 255u], 1u);
+                    if (u[i] != 0u && (u[i] & mask) == prefix) atomicAdd(&sh.hist[(u[i] >> shift) & dmask], 1u);
             }
             __syncthreads();
-            // digits in descending order: thread t looks at digit 255 - t
-            const uint32_t h = threadIdx.x < 256 ? sh.hist[255 - threadIdx.x] : 0u;
+            // thread t owns the 4 bins 4095-4t .. 4092-4t (descending digits)
+            uint32_t hb4[4], h = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { hb4[j] = sh.hist[TK_BINS - 1 - 4 * threadIdx.x - j]; h += hb4[j]; }
             uint32_t tot;
-            const uint32_t before = block_excl_scan(h, sh.part, tot);
-            if (threadIdx.x < 256 && before < rem && rem <= before + h) {
-                sh.digit = 255u - threadIdx.x;
-                sh.above = before;
+            uint32_t before = block_excl_scan(h, sh.part, tot);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (hb4[j] != 0u && before < rem && rem <= before + hb4[j]) {
+                    sh.digit = (uint32_t)(TK_BINS - 1 - 4 * threadIdx.x - j);
+                    sh.above = before;
+                    sh.count = hb4[j];
+                }
+                before += hb4[j];
             }
             __syncthreads();
             prefix |= sh.digit << shift;
-            mask |= 0xFFu << shift;
+            mask |= dmask << shift;
             rem -= sh.above;
+            in_bin = sh.count;
+            hb = shift - 1;
+            ++pass;
             __syncthreads();
         }
-        T = prefix;
-        need_eq = rem;
+        need = rem;
     }
+    const bool take_all = n_present <= (uint32_t)a.k;
 
-    // selection in column order
+    // ---- selection in column order
     uint32_t eq_base = 0u, out_base = 0u;
     for (int s = 0; s < nsweep; ++s) {
         if (nsweep > 1) load_sweep(a, krow, pool, ncols, s, u);
         uint32_t n_eq = 0u;
+        if (!take_all) {
 #pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i) n_eq += (T != 0u && u[i] == T);
+            for (int i = 0; i < TK_ITEMS; ++i) n_eq += (u[i] != 0u && (u[i] & mask) == prefix);
+        }
         uint32_t eq_tot;
         uint32_t eq_rank = eq_base + block_excl_scan(n_eq, sh.part, eq_tot);
         uint32_t sel_mask = 0u, n_sel = 0u;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
-            bool sel = u[i] > T;
-            if (T != 0u && u[i] == T) {
-                sel = eq_rank < need_eq;
-                eq_rank++;
+            bool sel;
+            if (take_all) sel = u[i] != 0u;
+            else {
+                const uint32_t hi = u[i] & mask;
+                sel = u[i] != 0u && hi > prefix;
+                if (u[i] != 0u && hi == prefix) { sel = eq_rank < need; eq_rank++; }
             }
             if (sel) { sel_mask |= 1u << i; n_sel++; }
         }
@@ -157,7 +210,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i)
-            if (sel_mask & (1u << i)) orow[pos++] = col_id(a, pool, c0 + i);
+            if (sel_mask & (1u << i)) orow[pos++] = col_id(pool, c0 + i);
         eq_base += eq_tot;
         out_base += sel_tot;
     }

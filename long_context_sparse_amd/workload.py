@@ -24,8 +24,8 @@ import torch
 import synth
 from synth.configs import Config
 
-from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_index_score, csa2_pack_kv,
-               csa2_select_topk, csa2_sparse_attn, csa2_sparse_attn_workspace_size, csa2_swa_merge,
+from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_attn_workspace_size, csa2_index_score,
+               csa2_pack_kv, csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge,
                csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform, make_kv, make_rows)
 
 GEN_CHUNK = 1 << 20   # entries generated per chunk
@@ -83,8 +83,9 @@ class Layer:
 class Workload:
     """All device buffers of one configuration; ``step()`` runs the hot path."""
 
-    def __init__(self, cfg: Config, copies: int = 1, dev="cuda"):
+    def __init__(self, cfg: Config, copies: int = 1, dev="cuda", separate: bool = False):
         self.cfg = cfg
+        self.separate = separate
         self.dev = dev
         L = cfg.lens
         base = cfg.req_base
@@ -156,7 +157,7 @@ class Workload:
             pools = np.stack([synth.given_pool(cfg.seed, r, int(L[r]) // 8, 2048) for r in range(self.n_rows)])
             self.pool.copy_(torch.as_tensor(pools))
             self.pool_count.fill_(2048)
-        ws = csa2_sparse_attn_workspace_size(self.n_rows, cfg.heads)
+        ws = csa2_attn_workspace_size(self.n_rows, cfg.heads)
         self.workspace = torch.empty((ws + 255) // 256 * 256, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -221,15 +222,25 @@ class Workload:
         self._attend(layer, kv, stream, marks)
 
     def _attend(self, layer, kv, stream, marks=None):
+        """Sparse + window attention in one pass (csa2_sparse_swa_attn); with
+        separate=True the two-call form csa2_sparse_attn -> csa2_swa_merge."""
         m = self._mark
-        m(marks, "sparse_attn", 0)
-        csa2_sparse_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, self.sigma, layer.o_partial,
-                         layer.lse, self.workspace, stream=stream)
-        m(marks, "sparse_attn", 1)
-        m(marks, "swa_merge", 0)
-        csa2_swa_merge(layer.swa_codes, layer.swa_scales, layer.swa_first, layer.swa_count, layer.q, self.sigma,
-                       layer.out, o_partial=layer.o_partial, lse=layer.lse, stream=stream)
-        m(marks, "swa_merge", 1)
+        if self.separate:
+            m(marks, "sparse_attn", 0)
+            csa2_sparse_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, self.sigma, layer.o_partial,
+                             layer.lse, self.workspace, stream=stream)
+            m(marks, "sparse_attn", 1)
+            m(marks, "swa_merge", 0)
+            csa2_swa_merge(layer.swa_codes, layer.swa_scales, layer.swa_first, layer.swa_count, layer.q,
+                           self.sigma, layer.out, self.workspace, o_partial=layer.o_partial, lse=layer.lse,
+                           stream=stream)
+            m(marks, "swa_merge", 1)
+        else:
+            m(marks, "attention", 0)
+            csa2_sparse_swa_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, layer.swa_codes,
+                                 layer.swa_scales, layer.swa_first, layer.swa_count, self.sigma, layer.out,
+                                 self.workspace, stream=stream)
+            m(marks, "attention", 1)
 
     def step(self, copy: int = 0, stream=None, marks=None):
         """One pass of the hot path.  `marks` maps step names to (start, end)

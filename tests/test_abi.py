@@ -99,7 +99,7 @@ def test_attn_rejects():
     kv, rows = _kv(), _rows()
     B = ctypes.byref
     f = L.csa2_sparse_attn
-    ws = L.csa2_sparse_attn_workspace_size(2, 64)
+    ws = L.csa2_attn_workspace_size(2, 64)
     assert ws > 0
     assert f(B(kv), B(rows), 256, 0, 40, 256, 512, 256, ctypes.c_float(0.04), 256, 256, 256, ws, None) == 5
     assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(0.04), 256, 256, 256, ws - 1, None) == 6
@@ -107,6 +107,15 @@ def test_attn_rejects():
     assert f(B(_kv(main_codes=None)), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(0.04), 256, 256,
              256, ws, None) == 1
     g = L.csa2_swa_merge
-    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, ctypes.c_float(0.04), None, 256, None, 256, None) == 1
-    assert g(256, 256, 10, 256, 256, 2, 256, 0, 200, ctypes.c_float(0.04), None, None, None, 256, None) == 5
-    assert g(264, 256, 10, 256, 256, 2, 256, 0, 64, ctypes.c_float(0.04), None, None, None, 256, None) == 4
+    F = ctypes.c_float(0.04)
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, F, None, 256, None, 256, 256, ws, None) == 1
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 200, F, None, None, None, 256, 256, ws, None) == 5
+    assert g(264, 256, 10, 256, 256, 2, 256, 0, 64, F, None, None, None, 256, 256, ws, None) == 4
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, F, None, None, None, 256, None, 0, None) == 6
+    h = L.csa2_sparse_swa_attn
+    assert h(B(kv), B(rows), 256, 0, 64, 256, 512, 256, None, 256, 10, 256, 256, None, F, 256, None, 256, ws,
+             None) == 1
+    assert h(B(kv), B(rows), 256, 0, 64, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 260, None, 256, ws,
+             None) == 4
+    assert h(B(kv), B(rows), 256, 0, 24, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 256, None, 256, ws,
+             None) == 5

@@ -268,7 +268,7 @@ def test_topk_block_counts_and_pool_ids():
 
 
 # ---------------------------------------------------------------- K4 / K5 attention
-def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=torch.bfloat16):
+def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=torch.bfloat16, check_rows=None):
     lat = bf16(RNG.standard_normal((n_rows * n_entries, 512)).astype(np.float32)).float().numpy()
     mc, ms = oracle.pack_main(lat)
     K = oracle.dequant_main(mc, ms)
@@ -283,17 +283,25 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
     kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), n_slots=n_rows * n_entries, req_stride=n_entries)
     rows = lib.make_rows(T(np.arange(n_rows, dtype=np.int32)), T(np.full(n_rows, n_entries, np.int32)), n_entries)
     qd = torch.as_tensor(q).to(qdt).to(DEV)
+    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256), dtype=torch.uint8, device=DEV)
+    idx_d, cnt_d = T(idx), T(np.asarray(counts, np.int32))
+    wc_d, wsc_d = T(wc), T(wsc)
+    first = T(np.arange(n_rows, dtype=np.int64) * 128)
+    swc = T(np.asarray(swa_counts, np.int32))
+    sk_d = None if sk is None else T(sk)
+    # two-call form
     o_p = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
-    ws = torch.empty(lib.csa2_sparse_attn_workspace_size(n_rows, H), dtype=torch.uint8, device=DEV)
-    lib.csa2_sparse_attn(kv, rows, qd, T(idx), T(np.asarray(counts, np.int32)), SIG, o_p, lse, ws)
+    lib.csa2_sparse_attn(kv, rows, qd, idx_d, cnt_d, SIG, o_p, lse, ws)
     out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
-    first = np.arange(n_rows, dtype=np.int64) * 128
-    lib.csa2_swa_merge(T(wc), T(wsc), T(first), T(np.asarray(swa_counts, np.int32)), qd, SIG, out,
-                       sink=None if sk is None else T(sk), o_partial=o_p, lse=lse)
+    lib.csa2_swa_merge(wc_d, wsc_d, first, swc, qd, SIG, out, ws, sink=sk_d, o_partial=o_p, lse=lse)
+    # one-pass form
+    out2 = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
+    lse2 = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
+    lib.csa2_sparse_swa_attn(kv, rows, qd, idx_d, cnt_d, wc_d, wsc_d, first, swc, SIG, out2, ws, sink=sk_d, lse=lse2)
     torch.cuda.synchronize()
-    O_p, L_p, Out = o_p.cpu().numpy(), lse.cpu().numpy(), out.cpu().numpy()
-    for r in range(n_rows):
+    O_p, L_p, Out, Out2, L2 = (t.cpu().numpy() for t in (o_p, lse, out, out2, lse2))
+    for r in (range(n_rows) if check_rows is None else check_rows):
         Kr = K[r * n_entries + idx[r, :counts[r]]]
         Wr = W[r * 128:r * 128 + swa_counts[r]]
         ro, rl = oracle.attention(q[r], Kr, None, sigma=SIG)
@@ -302,21 +310,35 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
             assert np.allclose(L_p[r], rl, rtol=1e-5, atol=1e-5)
         else:
             assert np.all(np.isneginf(L_p[r])) and not O_p[r].any()
-        fo, _ = oracle.attention(q[r], Kr, Wr, sink=sk, sigma=SIG)
+        fo, fl = oracle.attention(q[r], Kr, Wr, sink=sk, sigma=SIG)
         assert tolerance_ok(Out[r], fo), (r, np.abs(Out[r] - fo).max())
+        assert tolerance_ok(Out2[r], fo), (r, np.abs(Out2[r] - fo).max())
+        if counts[r] or swa_counts[r] or sink:
+            assert np.allclose(L2[r], fl, rtol=1e-5, atol=1e-5)
+        else:
+            assert np.all(np.isneginf(L2[r])) and not Out2[r].any()
 
 
-@pytest.mark.parametrize("H", [16, 64, 128])
+@pytest.mark.parametrize("H", [16, 48, 64, 128])
 def test_attention_counts(H):
     _attn_case(4, H, [512, 1, 65, 0], [128, 128, 1, 100])
 
 
 def test_attention_sink_and_empty_window():
-    _attn_case(3, 32, [300, 0, 64], [0, 128, 0], sink=True)
+    _attn_case(4, 32, [300, 0, 64, 0], [0, 128, 0, 0], sink=True)
 
 
 def test_attention_fp32_query():
     _attn_case(2, 16, [200, 512], [128, 128], qdt=torch.float32)
+
+
+@pytest.mark.parametrize("n_rows", [300, 2600])
+def test_attention_many_rows(n_rows):
+    """Fewer splits per row (300 rows) and one workgroup per row (2,600 rows)."""
+    counts = [int(c) for c in RNG.integers(0, 130, n_rows)]
+    swa_counts = [int(c) for c in RNG.integers(0, 129, n_rows)]
+    counts[0], swa_counts[0] = 512, 128
+    _attn_case(n_rows, 16, counts, swa_counts, n_entries=600, check_rows=list(range(0, n_rows, 97)) + [n_rows - 1])
 
 
 def test_swa_only_and_alias():
@@ -326,9 +348,19 @@ def test_swa_only_and_alias():
     W = oracle.dequant_swa(wc, wsc)
     q = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32)).float().numpy()
     out = torch.full((n_rows, H, 512), 5.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256), dtype=torch.uint8, device=DEV)
     lib.csa2_swa_merge(T(wc), T(wsc), T(np.array([0, 128], np.int64)), T(np.array([128, 37], np.int32)),
-                       bf16(q).to(DEV), SIG, out)
+                       bf16(q).to(DEV), SIG, out, ws)
     torch.cuda.synchronize()
     for r, c in enumerate([128, 37]):
         ref, _ = oracle.attention(q[r], None, W[r * 128:r * 128 + c], sigma=SIG)
         assert tolerance_ok(out[r].cpu().numpy(), ref)
+    # out aliasing o_partial
+    o_p = torch.zeros((n_rows, H, 512), dtype=torch.float32, device=DEV)
+    lse = torch.full((n_rows, H), -np.inf, dtype=torch.float32, device=DEV)
+    lib.csa2_swa_merge(T(wc), T(wsc), T(np.array([0, 128], np.int64)), T(np.array([128, 37], np.int32)),
+                       bf16(q).to(DEV), SIG, o_p, ws, o_partial=o_p, lse=lse)
+    torch.cuda.synchronize()
+    for r, c in enumerate([128, 37]):
+        ref, _ = oracle.attention(q[r], None, W[r * 128:r * 128 + c], sigma=SIG)
+        assert tolerance_ok(o_p[r].cpu().numpy(), ref)
