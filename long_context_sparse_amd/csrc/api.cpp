@@ -173,6 +173,8 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_
     if (!keys || !out_ids || !out_count) return fail(CSA2_ERR_NULL, "keys / out_ids / out_count is NULL");
     if (out_stride < k) return fail(CSA2_ERR_SHAPE, "out_stride < k");
     if (keys_by_id && !pool_blocks) return fail(CSA2_ERR_SHAPE, "keys_by_id needs pool_blocks");
+    if (keys_by_id && (!aligned(keys, 16) || key_stride % 4))
+        return fail(CSA2_ERR_ALIGN, "keys_by_id needs 16-byte aligned keys and key_stride % 4 == 0");
     if (pool_blocks && pool_stride < 1) return fail(CSA2_ERR_SHAPE, "pool_stride must be >= 1");
     if (!keys_by_id && key_stride < max_cols) return fail(CSA2_ERR_SHAPE, "key_stride < max_cols");
     if (pool_blocks && (int64_t)max_cols > 8 * pool_stride) return fail(CSA2_ERR_SHAPE, "max_cols exceeds 8 * pool_stride");

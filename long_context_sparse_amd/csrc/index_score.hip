@@ -36,9 +36,15 @@
 
 namespace csa2 {
 
+#ifndef CSA2_IS_TILES
+#define CSA2_IS_TILES 4
+#endif
+#ifndef CSA2_IS_ITERS
+#define CSA2_IS_ITERS 4
+#endif
 constexpr int IS_WAVES = 4;
-constexpr int IS_TILES = 4;                          // 16-key tiles per batch
-constexpr int IS_ITERS = 4;                          // batches per wave (even)
+constexpr int IS_TILES = CSA2_IS_TILES;              // 16-key tiles per batch
+constexpr int IS_ITERS = CSA2_IS_ITERS;              // batches per wave (even)
 constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16 * IS_ITERS;   // columns per workgroup
 
 struct QShared {
@@ -139,10 +145,39 @@ __device__ float exact_key_score(const QShared& qs, int n_heads, const uint8_t* 
     return acc == 0.0f ? 0.0f : acc;
 }
 
+// The row's indexer query, raw: lane (head m = l%16, block g = l/16) holds
+// the 32 channels it will quantise, as 16 bf16 pairs or 32 floats.
+struct QRaw {
+    uint32_t w[32];
+};
+
+template <bool QBF16>
+__device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, int n_heads) {
+    const int l = threadIdx.x & 63;
+    const int m = l & 15, g = l >> 4;
+    if (m >= n_heads) return;
+    const int64_t off = ((int64_t)row * n_heads + m) * 128 + 32 * g;
+    if (QBF16) {
+        const uint4* p = (const uint4*)((const uint16_t*)q_idx + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = p[i];
+            r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+        }
+    } else {
+        const uint4* p = (const uint4*)((const float*)q_idx + off);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 v = p[i];
+            r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+        }
+    }
+}
+
 // Quantise the row's indexer query to MXFP4 (one lane per (head, block) =
 // exactly the MFMA A-operand layout) and gather the exactness-guard bounds.
 template <bool QBF16>
-__device__ void prep_query(QShared& qs, const void* q_idx, const float* w, int row, int n_heads) {
+__device__ __forceinline__ void prep_query(QShared& qs, const QRaw& r, const float* w, int row, int n_heads) {
     const int l = threadIdx.x & 63;
     const int m = l & 15, g = l >> 4;
     uint32_t words[4] = {0, 0, 0, 0};
@@ -150,23 +185,15 @@ __device__ void prep_query(QShared& qs, const void* q_idx, const float* w, int r
     const bool real = m < n_heads;
     if (real) {
         float x[32];
-        const int64_t off = ((int64_t)row * n_heads + m) * 128 + 32 * g;
         if (QBF16) {
-            const uint16_t* p = (const uint16_t*)q_idx + off;
 #pragma unroll
-            for (int i = 0; i < 32; i += 8) {
-                const uint4 v = *(const uint4*)(p + i);
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[i + 2 * j] = __uint_as_float(u[j] << 16);
-                    x[i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-                }
+            for (int j = 0; j < 16; ++j) {
+                x[2 * j] = __uint_as_float(r.w[j] << 16);
+                x[2 * j + 1] = __uint_as_float(r.w[j] & 0xFFFF0000u);
             }
         } else {
-            const float* p = (const float*)q_idx + off;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) x[i] = p[i];
+            for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(r.w[i]);
         }
         float amax = 0.0f;
 #pragma unroll
@@ -205,18 +232,33 @@ __device__ __forceinline__ int col_pos(const int32_t* pool, int col) {
     return POOL ? 8 * pool[col >> 3] + (col & 7) : col;
 }
 
-// Issue the loads of one batch of this wave (columns clamped into range).
+// Issue the loads of one batch of this wave.  Columns past the end are
+// clamped into range (the loads are always issued, so that the compiler can
+// count outstanding loads exactly and never waits on a prefetched batch).
+// Full scan: a 16-column tile lies inside one page, so its page-table entry
+// is one wave-uniform load.
 template <bool POOL>
 __device__ __forceinline__ void load_batch(const KvView& kv, int req, const int32_t* pool, int nv, int ncols,
-                                           int col_base, int n, int lg, KeyBatch& kb) {
+                                           int col_base, int tstride, int n, int lg, KeyBatch& kb) {
 #pragma unroll
     for (int t = 0; t < IS_TILES; ++t) {
-        const int col0 = col_base + 16 * t;
-        const int c0 = col0 < ncols ? col0 : 0;         // column 0 is always valid when ncols > 0
-        const int col = col0 + n < ncols ? col0 + n : c0;
-        int ld = col_pos<POOL>(pool, col);
-        if (POOL && ld >= nv) ld = 8 * pool[col >> 3];   // a visible position of the same block
-        const int64_t e = entry_of(kv, req, ld);
+        const int col0 = col_base + tstride * t;         // wave-uniform
+        int64_t e;
+        if (POOL) {
+            const int c0 = col0 < ncols ? col0 : 0;      // column 0 is always valid when ncols > 0
+            const int col = col0 + n < ncols ? col0 + n : c0;
+            int ld = 8 * pool[col >> 3] + (col & 7);
+            if (ld >= nv) ld = 8 * pool[col >> 3];       // a visible position of the same block
+            e = entry_of(kv, req, ld);
+        } else {
+            const int t0 = col0 < ncols ? col0 : 0;
+            const int off = min(n, ncols - 1 - t0);      // stays inside the tile
+            int64_t base;
+            if (kv.page_shift < 0) base = (int64_t)req * kv.req_stride + t0;
+            else base = ((int64_t)kv.page_table[(int64_t)req * kv.max_pages + (t0 >> kv.page_shift)] << kv.page_shift) +
+                        (t0 & ((1 << kv.page_shift) - 1));
+            e = base + off;
+        }
         kb.code[t] = *(const uint4*)(kv.idx_codes + e * 64 + 16 * lg);
         kb.scl[t] = *(const uint32_t*)(kv.idx_scales + e * 4);
     }
@@ -240,19 +282,25 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     const int nv = min(a.n_vis[row], a.max_vis);
     const int64_t pool_cap = a.pool_stride < 2048 ? a.pool_stride : 2048;
     const int ncols = POOL ? 8 * (int)min((int64_t)a.pool_count[row], pool_cap) : nv;
-    const int chunk0 = blockIdx.x * IS_CHUNK;
-    if (chunk0 >= ncols) return;                       // uniform over the workgroup
+    // Tiles of 16 columns are dealt out round-robin: tile T of the row goes to
+    // wave T % 4 of workgroup (T / 4) % Gx, so at any moment the resident waves
+    // of a row read one compact run of consecutive 1 KB tiles.
+    const int Gx = gridDim.x;
+    const int tile_first = blockIdx.x * IS_WAVES;      // first tile of wave 0 in round 0
+    if (16 * tile_first >= ncols) return;              // uniform over the workgroup
     const int req = a.req[row];
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const int n = l & 15, lg = l >> 4;
     const int32_t* pool = POOL ? a.pool + (int64_t)row * a.pool_stride : nullptr;
-    // a wave's batch b covers columns wbase + b * BSTRIDE + [0, 16 * IS_TILES)
-    const int wbase = chunk0 + wave * IS_TILES * 16;
-    constexpr int BSTRIDE = IS_WAVES * IS_TILES * 16;
+    const int wbase = 16 * (tile_first + wave);        // column of this wave's first tile
+    const int TSTRIDE = 16 * IS_WAVES * Gx;            // columns between a wave's consecutive tiles
+    const int BSTRIDE = IS_TILES * TSTRIDE;            // columns between a wave's batches
 
+    QRaw qraw;
+    if (wave == 0) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads);      // issued before the keys
     KeyBatch A, B;
-    load_batch<POOL>(kv, req, pool, nv, ncols, wbase, n, lg, A);   // in flight during the query prep
-    if (wave == 0) prep_query<QBF16>(qs, a.q_idx, a.w, row, a.n_heads);
+    load_batch<POOL>(kv, req, pool, nv, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
+    if (wave == 0) prep_query<QBF16>(qs, qraw, a.w, row, a.n_heads);
     if (threadIdx.x == 0) qs.n_fix = 0;
     __syncthreads();
 
@@ -278,7 +326,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     auto compute = [&](const KeyBatch& kb, int col_base) {
 #pragma unroll
         for (int t = 0; t < IS_TILES; ++t) {
-            const int col0 = col_base + 16 * t;
+            const int col0 = col_base + TSTRIDE * t;
             if (col0 >= ncols) break;
             const i32x8 Bk = {(int)kb.code[t].x, (int)kb.code[t].y, (int)kb.code[t].z, (int)kb.code[t].w, 0, 0, 0, 0};
             const uint32_t sd = kb.scl[t];
@@ -320,15 +368,14 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
         }
     };
 
+#pragma unroll
     for (int b = 0; b < IS_ITERS; b += 2) {
         const int c_a = wbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
-        if (c_b < ncols) load_batch<POOL>(kv, req, pool, nv, ncols, c_b, n, lg, B);
+        load_batch<POOL>(kv, req, pool, nv, ncols, c_b, TSTRIDE, n, lg, B);
         compute(A, c_a);
-        if (c_b >= ncols) break;
         const int c_n = c_b + BSTRIDE;
-        if (b + 2 < IS_ITERS && c_n < ncols) load_batch<POOL>(kv, req, pool, nv, ncols, c_n, n, lg, A);
+        if (b + 2 < IS_ITERS) load_batch<POOL>(kv, req, pool, nv, ncols, c_n, TSTRIDE, n, lg, A);
         compute(B, c_b);
-        if (c_n >= ncols) break;
     }
 
     // ---- exact path for the queued 8-blocks (first column of each)

@@ -69,8 +69,26 @@ __device__ __forceinline__ int col_id(const int32_t* pool, int c) {
 
 __device__ __forceinline__ void load_sweep(const TopkArgs& a, const float* krow, const int32_t* pool,
                                            int ncols, int sweep, uint32_t* u) {
-    const int c0 = sweep * TK_SWEEP + threadIdx.x * TK_ITEMS;
-    if (!a.keys_by_id && c0 + TK_ITEMS <= ncols && ((uintptr_t)(krow + c0) & 15) == 0) {
+    const int c0 = sweep * TK_SWEEP + threadIdx.x * TK_ITEMS;   // a multiple of 16
+    if (a.keys_by_id) {
+        // columns c0 .. c0+15 are the two pool blocks c0/8 and c0/8 + 1: two runs of 8 keys
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int cb = c0 + 8 * h;
+            if (cb < ncols) {
+                const float* p = krow + 8 * pool[cb >> 3];
+                const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
+                const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) u[8 * h + i] = cb + i < ncols ? order_key(v[i]) : 0u;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) u[8 * h + i] = 0u;
+            }
+        }
+        return;
+    }
+    if (c0 + TK_ITEMS <= ncols && ((uintptr_t)(krow + c0) & 15) == 0) {
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; i += 4) {
             const float4 v = *(const float4*)(krow + c0 + i);
@@ -81,9 +99,7 @@ __device__ __forceinline__ void load_sweep(const TopkArgs& a, const float* krow,
 #pragma unroll
     for (int i = 0; i < TK_ITEMS; ++i) {
         const int c = c0 + i;
-        uint32_t key = 0u;
-        if (c < ncols) key = order_key(krow[a.keys_by_id ? col_id(pool, c) : c]);
-        u[i] = key;
+        u[i] = c < ncols ? order_key(krow[c]) : 0u;
     }
 }
 
@@ -182,38 +198,41 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     }
     const bool take_all = n_present <= (uint32_t)a.k;
 
-    // ---- selection in column order
-    uint32_t eq_base = 0u, out_base = 0u;
+    // ---- selection in column order: one scan of (greater, equal) counts; the
+    // equal items taken before a thread are min(equal before it, need)
+    uint32_t gt_base = 0u, eq_base = 0u, out_base = 0u;
     for (int s = 0; s < nsweep; ++s) {
         if (nsweep > 1) load_sweep(a, krow, pool, ncols, s, u);
-        uint32_t n_eq = 0u;
-        if (!take_all) {
-#pragma unroll
-            for (int i = 0; i < TK_ITEMS; ++i) n_eq += (u[i] != 0u && (u[i] & mask) == prefix);
-        }
-        uint32_t eq_tot;
-        uint32_t eq_rank = eq_base + block_excl_scan(n_eq, sh.part, eq_tot);
-        uint32_t sel_mask = 0u, n_sel = 0u;
+        uint32_t n_gt = 0u, n_eq = 0u;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
-            bool sel;
-            if (take_all) sel = u[i] != 0u;
-            else {
-                const uint32_t hi = u[i] & mask;
-                sel = u[i] != 0u && hi > prefix;
-                if (u[i] != 0u && hi == prefix) { sel = eq_rank < need; eq_rank++; }
-            }
-            if (sel) { sel_mask |= 1u << i; n_sel++; }
+            if (u[i] == 0u) continue;
+            if (take_all) { n_gt++; continue; }
+            const uint32_t hi = u[i] & mask;
+            n_gt += hi > prefix;
+            n_eq += hi == prefix;
         }
-        uint32_t sel_tot;
-        uint32_t pos = out_base + block_excl_scan(n_sel, sh.part, sel_tot);
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, sh.part, tot);
+        uint32_t eq_rank = eq_base + (ex & 0xFFFFu);
+        uint32_t pos = gt_base + (ex >> 16) + min(eq_rank, need);
         const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
 #pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i)
-            if (sel_mask & (1u << i)) orow[pos++] = col_id(pool, c0 + i);
-        eq_base += eq_tot;
-        out_base += sel_tot;
+        for (int i = 0; i < TK_ITEMS; ++i) {
+            if (u[i] == 0u) continue;
+            bool sel;
+            if (take_all) sel = true;
+            else {
+                const uint32_t hi = u[i] & mask;
+                sel = hi > prefix;
+                if (hi == prefix) { sel = eq_rank < need; eq_rank++; }
+            }
+            if (sel) orow[pos++] = col_id(pool, c0 + i);
+        }
+        gt_base += tot >> 16;
+        eq_base += tot & 0xFFFFu;
     }
+    out_base = gt_base + min(eq_base, need);
     for (int j = (int)out_base + threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = -1;
     if (threadIdx.x == 0) a.out_count[row] = (int32_t)out_base;
 }
