@@ -131,6 +131,14 @@ def make_rows(req, n_vis, max_vis):
     return rows
 
 
+def _rstride(t) -> int:
+    """Elements between consecutive rows of a 2-D (or wider) tensor; a tensor
+    with one row may carry any stride on that axis, so its row length is used."""
+    if t.dim() >= 2 and t.shape[0] == 1:
+        return int(t[0].numel())
+    return int(t.stride(0))
+
+
 # ------------------------------------------------------------------ entry points
 def abi_version() -> int:
     return lib().csa2_abi_version()
@@ -138,7 +146,7 @@ def abi_version() -> int:
 
 def csa2_pack_kv(kind, src, codes, scales, slots=None, stream=None):
     n = int(src.shape[0])
-    _check("csa2_pack_kv", lib().csa2_pack_kv(kind, _ptr(src), _dtype(src), n, int(src.stride(0)),
+    _check("csa2_pack_kv", lib().csa2_pack_kv(kind, _ptr(src), _dtype(src), n, _rstride(src),
                                              _ptr(codes), _ptr(scales), _ptr(slots), _stream(stream)))
 
 
@@ -147,9 +155,9 @@ def csa2_index_score(kv, rows, q_idx, w, scores=None, block_max=None, pool_block
     Hi = int(q_idx.shape[1])
     _check("csa2_index_score", lib().csa2_index_score(
         ctypes.byref(kv), ctypes.byref(rows), _ptr(q_idx), _dtype(q_idx), Hi, _ptr(w),
-        _ptr(pool_blocks), 0 if pool_blocks is None else int(pool_blocks.stride(0)), _ptr(pool_count),
-        _ptr(scores), 0 if scores is None else int(scores.stride(0)),
-        _ptr(block_max), 0 if block_max is None else int(block_max.stride(0)), _stream(stream)))
+        _ptr(pool_blocks), 0 if pool_blocks is None else _rstride(pool_blocks), _ptr(pool_count),
+        _ptr(scores), 0 if scores is None else _rstride(scores),
+        _ptr(block_max), 0 if block_max is None else _rstride(block_max), _stream(stream)))
 
 
 def csa2_select_topk(keys, k, out_ids, out_count, n_cols=None, cols_mul=1, cols_div=1, pool_blocks=None,
@@ -158,9 +166,9 @@ def csa2_select_topk(keys, k, out_ids, out_count, n_cols=None, cols_mul=1, cols_
     if max_cols is None:
         max_cols = int(keys.shape[1]) if not keys_by_id else 8 * int(pool_blocks.shape[1])
     _check("csa2_select_topk", lib().csa2_select_topk(
-        _ptr(keys), int(keys.stride(0)), _ptr(n_cols), cols_mul, cols_div, _ptr(pool_blocks),
-        0 if pool_blocks is None else int(pool_blocks.stride(0)), int(bool(keys_by_id)), n_rows,
-        int(max_cols), int(k), _ptr(out_ids), int(out_ids.stride(0)), _ptr(out_count), _stream(stream)))
+        _ptr(keys), _rstride(keys), _ptr(n_cols), cols_mul, cols_div, _ptr(pool_blocks),
+        0 if pool_blocks is None else _rstride(pool_blocks), int(bool(keys_by_id)), n_rows,
+        int(max_cols), int(k), _ptr(out_ids), _rstride(out_ids), _ptr(out_count), _stream(stream)))
 
 
 def csa2_attn_workspace_size(n_rows, n_heads) -> int:
@@ -174,7 +182,7 @@ def _nbytes(t):
 def csa2_sparse_attn(kv, rows, q, idx, idx_count, softmax_scale, o_partial, lse, workspace, stream=None):
     H = int(q.shape[1])
     _check("csa2_sparse_attn", lib().csa2_sparse_attn(
-        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), int(idx.stride(0)),
+        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), _rstride(idx),
         _ptr(idx_count), float(softmax_scale), _ptr(o_partial), _ptr(lse), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
 
@@ -192,7 +200,7 @@ def csa2_sparse_swa_attn(kv, rows, q, idx, idx_count, swa_codes, swa_scales, swa
                          out, workspace, sink=None, lse=None, stream=None):
     H = int(q.shape[1])
     _check("csa2_sparse_swa_attn", lib().csa2_sparse_swa_attn(
-        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), int(idx.stride(0)),
+        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), _rstride(idx),
         _ptr(idx_count), _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first),
         _ptr(swa_count), _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
         _nbytes(workspace), _stream(stream)))

@@ -337,6 +337,12 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[k], Bk, z, 4, 4, 0, sa[k], 0, sb);
             }
+            // An MFMA takes operands from all 64 lanes.  Only the writer lanes
+            // consume the scores in pool mode, and the compiler would otherwise
+            // sink the MFMA into their lane-masked store branch, where it returns
+            // wrong sums; an opaque use here pins it in wave-uniform control flow.
+#pragma unroll
+            for (int k = 0; k < NM; ++k) asm volatile("" : "+a"(d[k]));
             const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
             const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
             const bool ok = (kmax - kmin + qspread <= 9) && (qmin + kmin >= 136) && (qmax + kmax <= 356);

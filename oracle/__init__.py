@@ -273,10 +273,19 @@ def quant_query(q_idx):
     return pack_index(q_idx)
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def map_rows(fn, items, threads: int | None = None):
     """Run ``fn`` over independent rows on a thread pool (the C calls release
     the GIL); returns the results in order."""
-    threads = threads or os.cpu_count() or 1
+    threads = threads or default_threads()
     if threads <= 1 or len(items) <= 1:
         return [fn(it) for it in items]
     with ThreadPoolExecutor(max_workers=threads) as ex:

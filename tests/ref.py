@@ -60,9 +60,19 @@ class RowRef:
         return f32(synth.normal_bf16_rows(self.cfg.seed, synth.T_SWA + 16 * self.layer, ids, 512))
 
     # ---------------------------------------------------------------- steps
-    def scores_at(self, pos):
-        kc, ks = self.packed_index(pos)
-        return oracle.index_score(self.qc, self.qs, self.w, kc, ks)
+    def scores_at(self, pos, chunk: int = 1 << 15):
+        """Oracle scores of the given positions; long lists are split into
+        chunks scored on a thread pool (each chunk is independent)."""
+        pos = np.asarray(pos, np.int64)
+
+        def one(p):
+            kc, ks = self.packed_index(p)
+            return oracle.index_score(self.qc, self.qs, self.w, kc, ks)
+
+        if len(pos) <= chunk:
+            return one(pos)
+        parts = [pos[i:i + chunk] for i in range(0, len(pos), chunk)]
+        return np.concatenate(oracle.map_rows(one, parts))
 
     def full_scores(self):
         return self.scores_at(np.arange(self.n_vis))

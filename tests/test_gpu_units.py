@@ -164,12 +164,15 @@ def test_index_score_bf16_query_and_fp32_agree():
 
 
 @pytest.mark.parametrize("paged", [False, True])
-def test_index_score_pool_exact(paged):
-    n_rows, n, Hi = 2, 9000, 8
-    keys, q, w, kc, ks = _score_setup(n_rows, n, Hi, spread=True)
-    n_vis = np.array([9000, 8997], np.int32)
+@pytest.mark.parametrize("spread", [False, True])
+def test_index_score_pool_exact(paged, spread):
+    """Pool re-scoring.  Without the exponent spread every key takes the MFMA
+    path (a full 2,048-block pool on row 0); with it most take the exact one."""
+    n_rows, n, Hi = 2, 17000, 8
+    keys, q, w, kc, ks = _score_setup(n_rows, n, Hi, spread=spread)
+    n_vis = np.array([17000, 8997], np.int32)
     pools = np.full((n_rows, 2048), -1, np.int32)
-    counts = np.array([1125, 700], np.int32)
+    counts = np.array([2048, 700], np.int32)
     for r in range(n_rows):
         nb = (int(n_vis[r]) + 7) // 8
         pools[r, :counts[r]] = np.sort(RNG.permutation(nb)[:counts[r]])
@@ -265,6 +268,63 @@ def test_topk_block_counts_and_pool_ids():
         assert int(icnt[r]) == len(ref) and np.array_equal(idx[r, :len(ref)].cpu().numpy(), ref)
         ref2 = oracle.topk(pscores[r, :len(pos)], 512, ids=pos)
         assert int(icnt2[r]) == len(ref2) and np.array_equal(idx2[r, :len(ref2)].cpu().numpy(), ref2)
+
+
+# ---------------------------------------------------------------- whole Full-layer path, degenerate rows
+def test_full_path_empty_and_short_rows():
+    """Rows with no visible entry, fewer than 8, exactly 8, fewer than 512
+    blocks and a partial last block, chained through scoring, both
+    selections and the joint attention: counts, ids and outputs equal the
+    oracle's; an empty row attends to its window alone."""
+    n_vis = np.array([0, 5, 8, 4099, 20000], np.int32)
+    swa_counts = np.array([128, 0, 3, 128, 50], np.int32)
+    n_rows, n, Hi, H = len(n_vis), int(n_vis.max()), 8, 16
+    keys, q, w, kc, ks = _score_setup(n_rows, n, Hi)
+    lat = bf16(RNG.standard_normal((n_rows * n, 512)).astype(np.float32)).float().numpy()
+    mc, ms = oracle.pack_main(lat)
+    swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
+    wc, wsc = oracle.pack_swa(swa)
+    qa = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32)).float().numpy()
+    kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), idx_codes=T(kc), idx_scales=T(ks),
+                     n_slots=n_rows * n, req_stride=n)
+    nv = T(n_vis)
+    rows = lib.make_rows(T(np.arange(n_rows, dtype=np.int32)), nv, n)
+    nv8 = (n + 7) // 8 * 8
+    scores = torch.empty((n_rows, nv8), dtype=torch.float32, device=DEV)
+    bmax = torch.empty((n_rows, nv8 // 8), dtype=torch.float32, device=DEV)
+    pool = torch.empty((n_rows, 2048), dtype=torch.int32, device=DEV)
+    pcnt = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+    idx = torch.empty((n_rows, 512), dtype=torch.int32, device=DEV)
+    icnt = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+    out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256), dtype=torch.uint8, device=DEV)
+    lib.csa2_index_score(kv, rows, T(q), T(w), scores=scores, block_max=bmax)
+    lib.csa2_select_topk(bmax, 2048, pool, pcnt, n_cols=nv, cols_div=8, max_cols=nv8 // 8)
+    lib.csa2_select_topk(scores, 512, idx, icnt, n_cols=pcnt, cols_mul=8, pool_blocks=pool, keys_by_id=True,
+                         max_cols=16384)
+    lib.csa2_sparse_swa_attn(kv, rows, bf16(qa).to(DEV), idx, icnt, T(wc), T(wsc),
+                             T(np.arange(n_rows, dtype=np.int64) * 128), T(swa_counts), SIG, out, ws, lse=lse)
+    torch.cuda.synchronize()
+    qc, qs = oracle.quant_query(q.reshape(-1, 128))
+    K = oracle.dequant_main(mc, ms)
+    W = oracle.dequant_swa(wc, wsc)
+    for r in range(n_rows):
+        m = int(n_vis[r])
+        sc = oracle.index_score(qc[r * Hi:(r + 1) * Hi], qs[r * Hi:(r + 1) * Hi], w[r], kc[r * n:r * n + m],
+                                ks[r * n:r * n + m])
+        assert np.array_equal(scores[r, :m].cpu().numpy(), sc)
+        p_ref, i_ref = oracle.full_select(sc)
+        assert int(pcnt[r]) == len(p_ref) and np.array_equal(pool[r, :len(p_ref)].cpu().numpy(), p_ref)
+        assert int(icnt[r]) == len(i_ref) and np.array_equal(idx[r, :len(i_ref)].cpu().numpy(), i_ref)
+        assert np.all(idx[r, len(i_ref):].cpu().numpy() == -1)
+        o_ref, l_ref = oracle.attention(qa[r], K[r * n + i_ref], W[r * 128:r * 128 + swa_counts[r]], sigma=SIG)
+        got = out[r].cpu().numpy()
+        if len(i_ref) == 0 and swa_counts[r] == 0:
+            assert not got.any() and np.all(np.isneginf(lse[r].cpu().numpy()))
+        else:
+            assert tolerance_ok(got, o_ref), (r, np.abs(got - o_ref).max())
+            assert np.allclose(lse[r].cpu().numpy(), l_ref, rtol=1e-5, atol=1e-5)
 
 
 # ---------------------------------------------------------------- K4 / K5 attention
