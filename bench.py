@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "CSA2 decode steps/s (batch×heads) at 128K ctx; achieved HBM GB/s vs peak"
 DOMINANT = "index_score"          # the kernel the roofline object describes
 DOMINANT_SRC = os.path.join(ROOT, "long_context_sparse_amd", "csrc", "index_score.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_full_decode_16x128k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_{workload}_traffic.json")
 
 
 def parse():
@@ -50,15 +50,15 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from committed counter runs,
-    only while the kernel source is the one they were taken on."""
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs, only for the workload and the kernel source they were taken on."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload=workload)) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256_16") != source_hash(DOMINANT_SRC):
+    if d.get("source_sha256_16") != source_hash(DOMINANT_SRC) or d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
 
@@ -147,7 +147,7 @@ def main():
     k2_bytes = algo.get("index_keys_full", algo.get("index_keys_pool", 0))
     k2_gbs = k2_bytes / (k2_ms * 1e-3) / 1e9
     step_gbs = algo["total"] / (ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(cfg.name)
 
     out = {
         "metric": METRIC,
