@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum {
     CSA2_OK = 0,
@@ -65,7 +65,7 @@ typedef enum {
     CSA2_ERR_RANGE = 3,       /* a size or count outside its allowed range */
     CSA2_ERR_ALIGN = 4,       /* a pointer or stride is not aligned as required */
     CSA2_ERR_UNSUPPORTED = 5, /* a head count or dtype this build does not handle */
-    CSA2_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+    CSA2_ERR_WORKSPACE = 6,   /* reserved: no entry point of this version returns it */
     CSA2_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
 } csa2_status;
 
@@ -187,16 +187,14 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride,
  * (<= 128) of the planes swa_codes [swa_slots][512] / swa_scales [.][32].
  * q [n_rows][n_heads][512] bf16 (fp32 is rounded to bf16 on the way in);
  * n_heads 16, 32, 48, 64 or 128; outputs fp32.  q, o/out 16-B aligned.
- * workspace: csa2_attn_workspace_size(n_rows, n_heads) bytes, 256-B aligned,
- * no initialisation needed, not kept between calls. */
-size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads);
+ * No device memory beyond the arguments is used, and a row's result does not
+ * depend on the other rows of the call. */
 
 /* Selected entries only: o_partial / lse of the sparse branch. */
 csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows,
                              const void* q, csa2_dtype q_dtype, int32_t n_heads,
                              const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
-                             float softmax_scale, float* o_partial, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             float softmax_scale, float* o_partial, float* lse, void* stream);
 
 /* Window branch merged with a sparse-branch result through its log-sum-exp:
  * out = joint softmax over {the entries behind (o_partial, lse)} + {window}
@@ -206,7 +204,7 @@ csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, 
                            const int64_t* swa_first, const int32_t* swa_count, int32_t n_rows,
                            const void* q, csa2_dtype q_dtype, int32_t n_heads, float softmax_scale,
                            const float* sink, const float* o_partial, const float* lse,
-                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+                           float* out, void* stream);
 
 /* Both branches in one pass (the decode step's form): out = joint softmax
  * over selected + window entries (+ sink); lse (may be NULL) of that joint
@@ -216,8 +214,7 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
                                  const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
                                  const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
                                  const int64_t* swa_first, const int32_t* swa_count, const float* sink,
-                                 float softmax_scale, float* out, float* lse,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 float softmax_scale, float* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------- synthetic inputs
  * Counter-based generator for seeded synthetic inputs (SplitMix64; Steele,

@@ -4,96 +4,62 @@
 // Shared-KV MQA: every selected compressed entry is both key and value, and
 // the query heads attend in the 512-channel latent space (absorbed query)
 // ['DeepSeek-V4' paper page, section 2.3.1 "Shared Key-Value MQA"; MLA article,
-// section 4, matrix absorption].  The FP4 main entries are restored before
-// attention [V4.1-Flash architecture page: FP4 storage is dequantised before
-// the matmuls].  The sliding-window entries join the same softmax, and an
-// optional per-head sink adds exp(z'_h) to the denominator [section 2.3.3].
+// key-weight and deferred value absorption].  The FP4 main entries are
+// restored before the matmuls.  The sliding-window entries join the same
+// softmax, and an optional per-head sink adds exp(z'_h) to the denominator
+// [section 2.3.3].
 //
 // MI355X mapping
-//   * A row's entries form one virtual list: its selected FP4 entries, padded
-//     to a multiple of 64, then its window entries.  A workgroup walks a
-//     contiguous range of 64-entry chunks with an online softmax, one wave per
-//     16 heads.  Few rows (decode): each chunk gets its own workgroup and a
-//     merge kernel combines the partials; many rows (prefill): one
-//     workgroup per row writes the final output itself.
-//   * Per chunk the workgroup gathers the 64 entries once and dequantises them
-//     into LDS -- bf16 rows [entry][channel] for Q.K, and columns
-//     [channel][entry] for P.V.  FP4 x E4M3 values have at most 6
-//     significant bits and lie in [2^-10, 2688]: exact in bf16 and in fp16.
-//     E2M1 codes become fp16 through a byte-permute table (V_PERM_B32), are
-//     scaled with packed fp16 multiplies and turned into bf16 by exponent
-//     re-biasing.  Window values E4M3 x 2^e are exact in bf16.
-//   * Two waves per 16 heads: both compute the same scores, each does P.V for
-//     half of the 512 channels (more waves in flight, half the accumulators).
-//   * Split partials are stored normalised (O / l) in fp16 with (max, sum) in
-//     fp32, which halves the merge traffic.
-//   * S^T = K q^T on V_MFMA_F32_16X16X32_BF16 (A = 16 entries from LDS, B = the
-//     wave's 16 query heads held in registers).  The MFMA output layout puts
-//     4 consecutive entries of one head in a lane, which is exactly the
-//     B-operand layout P^T needs for O^T = V^T P^T once the contraction slots
-//     are mapped to entries {4g..4g+3, 16+4g..16+4g+3}: P never leaves
-//     registers.  Selected chunks use V_MFMA_F32_16X16X32_F16 with P in fp16;
-//     window chunks use bf16 with P split into a bf16 head and tail.
+//   * One workgroup per (row, group of 16 heads) walks the row's whole entry
+//     list -- its selected FP4 entries padded to a multiple of 64, then its
+//     window entries -- in chunks of 64 with an online softmax.  No split
+//     partials and no merge pass: the query is read once, every output is
+//     written once, and a row's result does not depend on how many rows share
+//     the launch.  The workgroups of one row are placed on one XCD so that
+//     its gathered entries are fetched into one L2.
+//   * 8 waves: wave w dequantises entries 16(w%4)..+15 of the chunk over the
+//     channel half w/4 straight into registers as the A operand of
+//     S^T = K q^T (V_MFMA_F32_16X16X32_BF16; the channel-to-slot order of the
+//     contraction is chosen so a lane's 64 channels are contiguous bytes), and
+//     writes the same values transposed into LDS for P.V.  The two half-sums
+//     of each S^T tile meet in LDS; every wave then holds all 64 scores of
+//     its 16 heads, runs the same softmax, and keeps P in registers as the B
+//     operand of O^T = V^T P^T over its own 64 channels.
+//   * LDS and the partial scores are double-buffered and the next chunk's
+//     bytes are in flight while the current one is processed: one barrier
+//     per chunk.
+//   * FP4 x E4M3 values have at most 6 significant bits and lie in
+//     [2^-10, 2688]: exact in bf16 and fp16.  E2M1 codes become fp16 through a
+//     byte-permute table, are scaled with packed fp16 multiplies and turned
+//     into bf16 by exponent re-biasing; P.V runs in fp16 with P in fp16.
+//     Window values E4M3 x 2^e are exact in bf16; their P.V runs in bf16 with
+//     P split into a bf16 head and tail.
+#include <type_traits>
+
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
 namespace csa2 {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int AT_ENT = 64;            // entries per chunk
-constexpr int KT_LD = 512 + 8;        // bf16 elements per K row in LDS (padded)
-constexpr int VT_LD = AT_ENT + 4;     // 16-bit elements per V^T row in LDS (padded)
-constexpr size_t AT_LDS = (size_t)AT_ENT * KT_LD * 2 + (size_t)512 * VT_LD * 2;
-constexpr int AT_MAX_SPLITS = 10;     // 512 selected + 128 window entries, 64 per chunk
-constexpr int AT_HEADS_PER_WG = 64;
+constexpr int AT_ENT = 64;              // entries per chunk
+constexpr int AT_WAVES = 8;
+constexpr int AT_THREADS = 64 * AT_WAVES;
+constexpr int V_LD = 512 + 16;          // fp16 elements per entry row of V in LDS (32 B pad spreads the banks)
+constexpr int AT_MAX_SEL = 512;
 
-int attn_splits(int n_rows) {
-    if (n_rows <= 0) return 1;
-    const int s = (2560 + n_rows - 1) / n_rows;   // aim at ~2,560 workgroups
-    return s < 1 ? 1 : (s > AT_MAX_SPLITS ? AT_MAX_SPLITS : s);
-}
+struct AttnSmem {
+    _Float16 v[2][AT_ENT * V_LD];       // the chunk's dequantised entries [entry][channel], double-buffered
+    f32x4 sp[2][AT_WAVES][64];          // per-wave half-channel S^T tiles, double-buffered
+    int64_t ent[AT_MAX_SEL];            // cache slot of each selected entry
+    float qmax[2][16];                  // per channel half and head: largest |q|
+    int wrange[2][AT_WAVES];            // per wave: largest and smallest nonzero window scale code
+};
+constexpr size_t AT_LDS = sizeof(AttnSmem);
+static_assert(AT_LDS <= 160 * 1024, "attention LDS exceeds the 160 KB of a CU");
 
-// per split and head: 512 fp16 (normalised partial output) + max + sum (fp32)
-static size_t split_bytes(int n_heads) { return (size_t)n_heads * (512 * 2 + 8); }
-
-size_t attn_workspace_bytes(int n_rows, int n_heads) {
-    const int s = attn_splits(n_rows);
-    if (s == 1) return 256;
-    return (size_t)n_rows * s * split_bytes(n_heads);
-}
-
-// q B-operand of one wave: lane holds head (h0 + l%16), channels
-// 32*ks + 8*(l/16) .. +8 for ks = 0..15, as bf16 (fp32 input rounded to nearest even).
-template <bool QBF16>
-__device__ __forceinline__ void load_q_operand(const void* q, int64_t row_head0, int n, int g, bf16x8* qv) {
-    if (QBF16) {
-        const uint16_t* p = (const uint16_t*)q + (row_head0 + n) * 512 + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qv[ks] = *(const bf16x8*)(p + 32 * ks);
-    } else {
-        const float* p = (const float*)q + (row_head0 + n) * 512 + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const float4 x0 = *(const float4*)(p + 32 * ks);
-            const float4 x1 = *(const float4*)(p + 32 * ks + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint16_t b[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) b[i] = (uint16_t)f32_to_bf16_rne(xs[i]);
-            qv[ks] = *(const bf16x8*)b;
-        }
-    }
-}
-
-// V^T A-operand for channel tile ct, contraction step u: channel 16ct + n,
-// entries {32u + 4g .. +3} and {32u + 16 + 4g .. +3}.
-__device__ __forceinline__ uint4 vt_operand(const uint16_t* Vt, int ct, int u, int n, int g) {
-    const uint16_t* r = Vt + (16 * ct + n) * VT_LD + 32 * u + 4 * g;
-    const uint2 lo = *(const uint2*)r;
-    const uint2 hi = *(const uint2*)(r + 16);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
 
 // Eight E2M1 codes (one dword) -> four fp16 pairs (channels 2i, 2i+1).
 // The fp16 high byte of each magnitude comes from a byte-permute table:
@@ -124,313 +90,364 @@ __device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Gather + dequantise one chunk of selected FP4 entries (lane = entry); the
-// loads of a lane's channel groups are all issued before any is used.
-__device__ __forceinline__ void dequant_main_chunk(const KvView& kv, const AttnArgs& a, int row, int e0, int nent,
-                                                   uint16_t* Kt, uint16_t* Vt, int wave, int W, int l) {
-    const int j = l;
-    const bool valid = j < nent;
-    int64_t ent = 0;
-    if (valid) ent = entry_of(kv, a.req[row], a.idx[(int64_t)row * a.idx_stride + e0 + j]);
-    constexpr int GPW = 2;
-    for (int g0 = wave; g0 < 32; g0 += W * GPW) {
-        uint2 c[GPW];
-        uint32_t sc[GPW];
+// Raw bytes of one lane's share of a chunk: the 64 channels
+// 256*kh + 64*g .. +63 of one entry (32 B of FP4 codes or 64 B of E4M3 codes)
+// and the 4 scale bytes of those channels.
+struct RawChunk {
+    uint4 c[4];
+    uint32_t s;
+};
+
+__device__ __forceinline__ void load_raw(const KvView& kv, const AttnArgs& a, const AttnSmem& sm, int c, int csp,
+                                         int nsp, int nsw, int64_t swa0, int et, int kh, int n, int g, RawChunk& r) {
+    // Addresses are selected, the loads are issued unconditionally (the
+    // selected-entry case re-reads its 32 code bytes for c[2..3], unused).
+    const bool sel = c < csp;
+    int e = 16 * et + n + 64 * (sel ? c : c - csp);
+    e = e < (sel ? nsp : nsw) ? e : 0;                // padding lanes re-read entry 0 (masked later)
+    const uint8_t* cp;
+    const uint8_t* sp;
+    if (sel) {
+        const int64_t slot = sm.ent[e];
+        cp = kv.main_codes + slot * 256 + 128 * kh + 32 * g;
+        sp = kv.main_scales + slot * 32 + 16 * kh + 4 * g;
+    } else {
+        const int64_t slot = swa0 + e;
+        cp = a.swa_codes + slot * 512 + 256 * kh + 64 * g;
+        sp = a.swa_scales + slot * 32 + 16 * kh + 4 * g;
+    }
+    const uint4* p = (const uint4*)cp;
+    const uint4* p2 = (const uint4*)(cp + (sel ? 0 : 32));
+    r.c[0] = p[0];
+    r.c[1] = p[1];
+    r.c[2] = p2[0];
+    r.c[3] = p2[1];
+    r.s = *(const uint32_t*)sp;
+}
+
+// Selected entry: dequantise the lane's 64 channels into the QK A operand
+// and into V^T, both fp16 and both carrying the row's exact factor 2^tw
+// (-14 <= tw <= 4).  V_CVT_SCALEF32_PK_F16_FP4 expands two E2M1 codes (low
+// nibble first) times the power of two of its f32 scale operand, here
+// 2^(tw+8); the E4M3 scale byte shifted into fp16 position reads as
+// scale * 2^-8 (normal and subnormal alike) and one packed fp16 multiply
+// applies it.  FP4 x E4M3 values have at most 6 significant bits and lie in
+// [2^-10, 2688], so times 2^tw they are exact in fp16.  K-step ks holds
+// channels 8ks .. 8ks+7 of the lane and is also stored to the entry's row in
+// LDS at vrow + 8ks.
+__device__ __forceinline__ void dequant_main(const RawChunk& r, float cvt_scale, _Float16* vrow, f16x8* kop) {
+    const uint32_t words[8] = {r.c[0].x, r.c[0].y, r.c[0].z, r.c[0].w, r.c[1].x, r.c[1].y, r.c[1].z, r.c[1].w};
 #pragma unroll
-        for (int k = 0; k < GPW; ++k) {
-            const int grp = g0 + k * W;
-            c[k] = make_uint2(0u, 0u);
-            sc[k] = 0u;
-            if (valid && grp < 32) {
-                c[k] = *(const uint2*)(kv.main_codes + ent * 256 + 8 * grp);
-                sc[k] = kv.main_scales[ent * 32 + grp];
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < GPW; ++k) {
-            const int grp = g0 + k * W;
-            if (grp >= 32) break;
-            const _Float16 sh = (_Float16)e4m3_to_f32(sc[k]);          // exact
-            const uint32_t s2 = (uint32_t)__builtin_bit_cast(uint16_t, sh) * 0x00010001u;
-            uint32_t hp[8], kb[8];
-            e2m1x8_to_f16x2(c[k].x, hp);
-            e2m1x8_to_f16x2(c[k].y, hp + 4);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                hp[i] = pk_mul_f16(hp[i], s2);                          // exact
-                kb[i] = f16x2_to_bf16x2_exact(hp[i]);
-                Vt[(16 * grp + 2 * i) * VT_LD + j] = (uint16_t)(hp[i] & 0xFFFFu);
-                Vt[(16 * grp + 2 * i + 1) * VT_LD + j] = (uint16_t)(hp[i] >> 16);
-            }
-            uint4* kd = (uint4*)(Kt + j * KT_LD + 16 * grp);
-            kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
-            kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
-        }
+    for (int ks = 0; ks < 8; ++ks) {
+        const uint32_t s16 = ((r.s >> (8 * (ks >> 1))) & 0x7Fu) << 7;
+        const f16x2 s2 = __builtin_bit_cast(f16x2, s16 | (s16 << 16));
+        f16x2 hp[4];
+        hp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[ks], cvt_scale, 0) * s2;
+        hp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[ks], cvt_scale, 1) * s2;
+        hp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[ks], cvt_scale, 2) * s2;
+        hp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[ks], cvt_scale, 3) * s2;
+        kop[ks] = (f16x8){hp[0][0], hp[0][1], hp[1][0], hp[1][1], hp[2][0], hp[2][1], hp[3][0], hp[3][1]};
+        *(f16x8*)(vrow + 8 * ks) = kop[ks];
     }
 }
 
-// Load + dequantise one chunk of window entries (8-bit E4M3 x 2^e).
-__device__ __forceinline__ void dequant_swa_chunk(const AttnArgs& a, int64_t first, int nent,
-                                                  uint16_t* Kt, uint16_t* Vt, int wave, int W, int l) {
-    const int j = l;
-    const bool valid = j < nent;
-    const int64_t ent = first + j;
-    constexpr int GPW = 2;
-    for (int g0 = wave; g0 < 32; g0 += W * GPW) {
-        uint4 c[GPW];
-        uint32_t sc[GPW];
+// Window entry: E4M3 codes times the E8M0 scale 2^e of their 16 channels,
+// times the row's 2^tw, in fp16 (V_CVT_SCALEF32_PK_F16_FP8 converts two E4M3
+// bytes and multiplies by the power of two of its f32 scale operand).
+// E4M3 * 2^(e + tw) is exact in fp16 while -15 <= e + tw <= 7.
+__device__ __forceinline__ void dequant_swa(const RawChunk& r, int tw, _Float16* vrow, f16x8* kop) {
+    const uint32_t words[16] = {r.c[0].x, r.c[0].y, r.c[0].z, r.c[0].w, r.c[1].x, r.c[1].y, r.c[1].z, r.c[1].w,
+                                r.c[2].x, r.c[2].y, r.c[2].z, r.c[2].w, r.c[3].x, r.c[3].y, r.c[3].z, r.c[3].w};
 #pragma unroll
-        for (int k = 0; k < GPW; ++k) {
-            const int grp = g0 + k * W;
-            c[k] = make_uint4(0u, 0u, 0u, 0u);
-            sc[k] = 127u;
-            if (valid && grp < 32) {
-                c[k] = *(const uint4*)(a.swa_codes + ent * 512 + 16 * grp);
-                sc[k] = a.swa_scales[ent * 32 + grp];
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < GPW; ++k) {
-            const int grp = g0 + k * W;
-            if (grp >= 32) break;
-            const float s = e8m0_to_f32(sc[k]);
-            const uint32_t words[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
-            uint32_t kb[8];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float v = e4m3_to_f32((words[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
-                const uint32_t bb = __float_as_uint(v) >> 16;          // exact bf16
-                if (i & 1) kb[i >> 1] |= bb << 16; else kb[i >> 1] = bb;
-                Vt[(16 * grp + i) * VT_LD + j] = (uint16_t)bb;
-            }
-            uint4* kd = (uint4*)(Kt + j * KT_LD + 16 * grp);
-            kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
-            kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
-        }
+    for (int ks = 0; ks < 8; ++ks) {
+        int ef = (int)((r.s >> (8 * (ks >> 1))) & 0xFFu) + tw;    // biased exponent of 2^(e + tw)
+        ef = ef < 0 ? 0 : (ef > 254 ? 254 : ef);                   // only all-zero groups reach the clamps
+        const float sc = __uint_as_float((uint32_t)ef << 23);
+        f16x2 b[4];
+        b[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(words[2 * ks], sc, false);
+        b[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(words[2 * ks], sc, true);
+        b[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(words[2 * ks + 1], sc, false);
+        b[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(words[2 * ks + 1], sc, true);
+        kop[ks] = (f16x8){b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
+        *(f16x8*)(vrow + 8 * ks) = kop[ks];
     }
 }
 
-// Workgroup = (split, row, group of up to 64 heads); two waves per 16 heads
-// (wave 2p and 2p+1 share heads 16p..16p+15 and take channel halves 0 / 1).
+// q B operand of a lane: head h, channels 256*kh + 64*g + 8ks .. +7, ks = 0..7,
+// as bf16 (an fp32 query is rounded to nearest even), and the lane's largest
+// magnitude.
 template <bool QBF16>
-__global__ __launch_bounds__(512) void attn_kernel(KvView kv, AttnArgs a) {
+__device__ __forceinline__ float load_q_operand(const void* q, int64_t qrow, int kh, int g, bf16x8* qv) {
+    const int64_t off = qrow * 512 + 256 * kh + 64 * g;
+    float amax = 0.0f;
+    if (QBF16) {
+        const bf16x8* p = (const bf16x8*)((const uint16_t*)q + off);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qv[ks] = p[ks];
+    } else {
+        const float4* p = (const float4*)((const float*)q + off);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const float4 x0 = p[2 * ks], x1 = p[2 * ks + 1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16_rne(xs[2 * i]) | (f32_to_bf16_rne(xs[2 * i + 1]) << 16);
+            qv[ks] = __builtin_bit_cast(bf16x8, make_uint4(b[0], b[1], b[2], b[3]));
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const uint4 u = __builtin_bit_cast(uint4, qv[ks]);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+        }
+    }
+    return amax;
+}
+
+// The fp16 copy of the query for the selected entries: q * 2^kq with
+// 2^14 <= amax * 2^kq < 2^15, so the head's largest component keeps full
+// precision and the whole head stays in fp16 range (components below
+// amax * 2^-29 lose bits, far below the attention tolerance).
+__device__ __forceinline__ void q_to_f16(const bf16x8* qv, int kq, f16x8* qh) {
+    const float f = __uint_as_float((uint32_t)(127 + kq) << 23);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const uint4 u = __builtin_bit_cast(uint4, qv[ks]);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        f16x8 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[2 * i] = (_Float16)(__uint_as_float(w[i] << 16) * f);
+            h[2 * i + 1] = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * f);
+        }
+        qh[ks] = h;
+    }
+}
+
+// V^T A operand of P.V for channels ch0 .. ch0+15, contraction step u, read
+// from V [entry][channel] with DS_READ_B64_TR_B16.  Within each 16-lane group
+// the transposing read hands lane 4a+b element b of the 4-element rows
+// addressed by lanes a, a+4, a+8, a+12; lane i of group g addresses entry
+// base + i/4, channels ch0 + 4(i%4) .. +3, so lane j receives channel ch0 + j
+// of entries base .. base+3.  Two reads fill the 8 slots of group g: entries
+// {32u + 4g .. +3} and {32u + 16 + 4g .. +3} (the slots of P^T).
+__device__ __forceinline__ f16x8 v_operand(const _Float16* vb, int ch0, int u, int n, int g) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int off = (32 * u + 4 * g + (n >> 2)) * V_LD + ch0 + 4 * (n & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + off + 16 * V_LD));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Block -> (row, head group): the workgroups are dealt to the XCDs in turn,
+// so block b runs on XCD b % 8; number the (row, group) pairs so that each
+// XCD receives a consecutive run of them (a row's groups share an L2).
+__device__ __forceinline__ int xcd_order(int b, int total) {
+    const int x = b & 7, k = b >> 3;
+    int base = 0;
+    for (int y = 0; y < x; ++y) base += (total - y + 7) >> 3;
+    return base + k;
+}
+
+template <bool QBF16>
+__global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a) {
     extern __shared__ __align__(16) uint8_t at_smem[];
-    uint16_t* Kt = (uint16_t*)at_smem;
-    uint16_t* Vt = Kt + AT_ENT * KT_LD;
-    const int row = blockIdx.y, split = blockIdx.x;
-    const int H = a.n_heads, W = blockDim.x >> 6;
+    AttnSmem& sm = *(AttnSmem*)at_smem;
+    const int G = a.n_heads >> 4;
+    const int id = xcd_order(blockIdx.x, a.n_rows * G);
+    const int row = id / G, h0 = 16 * (id - row * G);
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int n = l & 15, g = l >> 4;
-    const int half = wave & 1;
-    const int h0 = blockIdx.z * AT_HEADS_PER_WG + (wave >> 1) * 16;
-    const int nsp = a.idx ? min(a.idx_count[row], 512) : 0;
-    const int nsw = a.swa_codes ? min(a.swa_count[row], 128) : 0;
+    const int et = wave & 3, kh = wave >> 2;
+    const int nsp = a.idx ? min(max(a.idx_count[row], 0), AT_MAX_SEL) : 0;
+    const int nsw = a.swa_codes ? min(max(a.swa_count[row], 0), 128) : 0;
     const int csp = (nsp + AT_ENT - 1) / AT_ENT;
     const int ctot = csp + (nsw + AT_ENT - 1) / AT_ENT;
-    const int per = (ctot + a.n_splits - 1) / a.n_splits;
-    const int cb = min(split * per, ctot), ce = min(cb + per, ctot);
+    const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
-    bf16x8 qv[16];
-    load_q_operand<QBF16>(a.q, (int64_t)row * H + h0, n, g, qv);
-    f32x4 oacc[16];
+    // cache slots of the selected entries; the query and its per-head scale;
+    // the exponent range of the row's window scales
+    if ((int)threadIdx.x < nsp)
+        sm.ent[threadIdx.x] = entry_of(kv, a.req[row], a.idx[(int64_t)row * a.idx_stride + threadIdx.x]);
+    int wmax = 0, wmin = 255;                       // over nonzero scale codes (all-zero groups have code 0)
+    if ((int)threadIdx.x * 8 < nsw * 32) {
+        const uint2 v = *(const uint2*)(a.swa_scales + swa0 * 32 + 8 * threadIdx.x);
 #pragma unroll
-    for (int ct = 0; ct < 16; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    for (int c = cb; c < ce; ++c) {
-        const bool is_sw = c >= csp;
-        const int e0 = is_sw ? (c - csp) * AT_ENT : c * AT_ENT;
-        const int nent = min((is_sw ? nsw : nsp) - e0, AT_ENT);
-        __syncthreads();                               // previous chunk fully consumed
-        if (is_sw) dequant_swa_chunk(a, a.swa_first[row] + e0, nent, Kt, Vt, wave, W, l);
-        else dequant_main_chunk(kv, a, row, e0, nent, Kt, Vt, wave, W, l);
-        __syncthreads();
-        // ---- S^T tiles: acc[et][i] = K[16et + 4g + i] . q[head n]
-        f32x4 acc[4];
-#pragma unroll
-        for (int et = 0; et < 4; ++et) acc[et] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        {
-            const uint16_t* base = Kt + n * KT_LD + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < 16; ++ks) {
-#pragma unroll
-                for (int et = 0; et < 4; ++et)
-                    acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        *(const bf16x8*)(base + 16 * et * KT_LD + 32 * ks), qv[ks], acc[et], 0, 0, 0);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const int c = (int)(((i < 4 ? v.x : v.y) >> (8 * (i & 3))) & 0xFFu);
+            if (c) { wmax = max(wmax, c); wmin = min(wmin, c); }
         }
-        // ---- online softmax (column = head)
-        float m = -INFINITY;
+    }
+    bf16x8 qb[8];
+    float qa = load_q_operand<QBF16>(a.q, (int64_t)row * a.n_heads + h0 + n, kh, g, qb);
+    qa = fmaxf(qa, shfl_xor_f(qa, 16));
+    qa = fmaxf(qa, shfl_xor_f(qa, 32));
+    if (et == 0 && g == 0) sm.qmax[kh][n] = qa;
 #pragma unroll
-        for (int et = 0; et < 4; ++et)
+    for (int d = 1; d < 64; d <<= 1) {
+        wmax = max(wmax, __shfl_xor(wmax, d, 64));
+        wmin = min(wmin, __shfl_xor(wmin, d, 64));
+    }
+    if (l == 0) { sm.wrange[0][wave] = wmax; sm.wrange[1][wave] = wmin; }
+    __syncthreads();
+    const float qmax = fmaxf(sm.qmax[0][n], sm.qmax[1][n]);
+    int kq = qmax > 0.0f ? 14 - ((int)((__float_as_uint(qmax) >> 23) & 0xFFu) - 127) : 0;
+    kq = kq < -110 ? -110 : (kq > 110 ? 110 : kq);
+    f16x8 qh[8];
+    q_to_f16(qb, kq, qh);
+    wmax = 0;
+    wmin = 255;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float z = (16 * et + 4 * g + i) < nent ? acc[et][i] * a.scale : -INFINITY;
-                acc[et][i] = z;
-                m = fmaxf(m, z);
-            }
+    for (int w = 0; w < AT_WAVES; ++w) { wmax = max(wmax, sm.wrange[0][w]); wmin = min(wmin, sm.wrange[1][w]); }
+    // The row's power of two 2^tw on every dequantised entry: selected entries
+    // are exact in fp16 for -14 <= tw <= 4, window ones while the exponents
+    // e + tw of their groups stay in [-15, 7]; tw brings the largest window
+    // group as close to 7 as the selected range allows (window groups more than
+    // 22 octaves below the largest one would be rounded).
+    int tw = wmax ? 134 - wmax : 0;
+    tw = tw < -14 ? -14 : (tw > 4 ? 4 : tw);
+    // logits in base 2: z2 = S' * cz with S' = S * 2^(kq + tw)
+    constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
+    const float cz = ldexpf(a.scale * LOG2E, -kq - tw);
+    const float cvt_sel = __uint_as_float((uint32_t)(127 + tw + 8) << 23);     // 2^(tw + 8)
+
+    // Software pipeline, one barrier per chunk: while a wave turns the scores of
+    // chunk c into probabilities and accumulates P.V (LDS buffers c & 1), it
+    // dequantises chunk c + 1 and computes its partial scores (buffers
+    // (c + 1) & 1).  Chunk c's bytes sit in raw[c & 1]; right after they are
+    // dequantised the loads of chunk c + 2 go into the same registers.
+    RawChunk raw0, raw1;
+    if (ctot > 0) {
+        load_raw(kv, a, sm, 0, csp, nsp, nsw, swa0, et, kh, n, g, raw0);
+        load_raw(kv, a, sm, min(1, ctot - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw1);
+    }
+    f32x4 oacc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;            // base-2 running max and sum
+    const int chb = 256 * kh + 64 * g;               // first of this lane's 64 dequant channels
+    const int v_lane = (16 * et + n) * V_LD + chb;  // this lane's entry row and channels in LDS
+
+    // dequantise chunk c, its partial scores into sp[c & 1]; reload raw with chunk c + 2
+    auto stage_a = [&](auto swc, const int c, RawChunk& raw) __attribute__((always_inline)) {
+        constexpr bool SW = decltype(swc)::value;
+        _Float16* vb = sm.v[c & 1];
+        f16x8 kop[8];
+        if (SW) dequant_swa(raw, tw, vb + v_lane, kop);
+        else dequant_main(raw, cvt_sel, vb + v_lane, kop);
+        // always issued (the last two re-read the final chunk, unused): a load
+        // under a branch makes the compiler wait for it at the join
+        load_raw(kv, a, sm, min(c + 2, ctot - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw);
+        f32x4 sc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], qh[ks], sc, 0, 0, 0);
+        sm.sp[c & 1][wave][l] = sc;
+    };
+    // probabilities of chunk c and O^T += V^T P^T over channels 64*wave .. +63
+    auto stage_b = [&](const int c) __attribute__((always_inline)) {
+        const int buf = c & 1;
+        const int nent = min(c < csp ? nsp - 64 * c : nsw - 64 * (c - csp), AT_ENT);   // <= 0 past the end
+        f32x4 z[4];                                      // z[t][i]: entry 16t + 4g + i, head n
+#pragma unroll
+        for (int t = 0; t < 4; ++t) z[t] = sm.sp[buf][t][l] + sm.sp[buf][t + 4][l];
+        if (nent < AT_ENT) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * t + 4 * g + i >= nent) z[t][i] = -INFINITY;
+        }
+        float m = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(z[2][0], z[2][1]), fmaxf(z[2][2], z[2][3])),
+                           fmaxf(fmaxf(z[3][0], z[3][1]), fmaxf(z[3][2], z[3][3]))));
         m = fmaxf(m, shfl_xor_f(m, 16));
         m = fmaxf(m, shfl_xor_f(m, 32));
-        const float m_new = fmaxf(m_run, m);
-        const float alpha = (m_run == -INFINITY) ? 0.0f : expf(m_run - m_new);
+        const float m_new = fmaxf(m_run, m * cz);         // cz > 0: the scaled maximum
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         float lsum = 0.0f;
+        f16x8 pb[2];                                     // P^T slot 8g + j of step u: entry 32u + 4g + j (j < 4), 32u + 12 + 4g + j
 #pragma unroll
-        for (int et = 0; et < 4; ++et)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = expf(acc[et][i] - m_new);
-                acc[et][i] = p;
+                const float p = __builtin_amdgcn_exp2f(fmaf(z[t][i], cz, -m_new));
                 lsum += p;
+                pb[t >> 1][4 * (t & 1) + i] = (_Float16)p;
             }
         lsum += shfl_xor_f(lsum, 16);
         lsum += shfl_xor_f(lsum, 32);
         l_run = l_run * alpha + lsum;
         m_run = m_new;
-        // ---- O^T += V^T P^T over this wave's 16 channel tiles
-        const int ct0 = 16 * half;
-        if (!is_sw) {
-            f16x8 pb[2];
+        const _Float16* vb = sm.v[buf];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 o = oacc[ct] * alpha;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pb[u][i] = (_Float16)acc[2 * u + (i >> 2)][i & 3];
-#pragma unroll
-            for (int ct = 0; ct < 16; ++ct) {
-                f32x4 o = oacc[ct] * alpha;
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const uint4 av = vt_operand(Vt, ct0 + ct, u, n, g);
-                    o = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const f16x8*)&av, pb[u], o, 0, 0, 0);
-                }
-                oacc[ct] = o;
-            }
-        } else {
-            bf16x8 phi[2], plo[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p = acc[2 * u + (i >> 2)][i & 3];
-                    const uint32_t hb = f32_to_bf16_rne(p);
-                    const uint32_t lb = f32_to_bf16_rne(p - __uint_as_float(hb << 16));
-                    phi[u][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-                    plo[u][i] = __builtin_bit_cast(__bf16, (uint16_t)lb);
-                }
-#pragma unroll
-            for (int ct = 0; ct < 16; ++ct) {
-                f32x4 o = oacc[ct] * alpha;
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const uint4 av = vt_operand(Vt, ct0 + ct, u, n, g);
-                    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&av, phi[u], o, 0, 0, 0);
-                    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)&av, plo[u], o, 0, 0, 0);
-                }
-                oacc[ct] = o;
-            }
+                o = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand(vb, 64 * wave + 16 * ct, u, n, g), pb[u], o, 0, 0, 0);
+            oacc[ct] = o;
+        }
+    };
+    const std::integral_constant<bool, false> SEL{};
+    const std::integral_constant<bool, true> WIN{};
+    // One pipeline step: stage A of chunk c + 1 with stage B of chunk c.  The
+    // steps run in pairs with nothing conditional but the chunk type, so the
+    // compiler can count the loads in flight; chunks past the end are
+    // processed as empty (their scores are all masked: no contribution).
+    auto step = [&](const int c, RawChunk& next_raw) __attribute__((always_inline)) {
+        const int ca = min(c + 1, ctot - 1) < csp ? 0 : 1;
+        if (ca == 0) stage_a(SEL, c + 1, next_raw);
+        else stage_a(WIN, c + 1, next_raw);
+        stage_b(c);
+        __syncthreads();
+    };
+
+    if (ctot > 0) {
+        if (csp > 0) stage_a(SEL, 0, raw0);
+        else stage_a(WIN, 0, raw0);
+        __syncthreads();
+        for (int c = 0; c < ctot; c += 2) {
+            step(c, raw1);
+            step(c + 1, raw0);
         }
     }
 
+    // ---- epilogue: join an external partial (o_in, lse_in) and the sink; write
+    // O^T[64*wave + 16ct + 4g + i][head h0 + n].  Natural-log terms become
+    // base 2 with log2(e); oacc carries the entries' 2^tw.
     const int h = h0 + n;
-    const int cbase = 256 * half;                      // first channel of this wave
-    if (a.n_splits > 1) {
-        // normalised partial output (fp16) plus (max, sum) of this split
-        const size_t ps = ((size_t)row * a.n_splits + split) * H + h;
-        uint16_t* wsO = (uint16_t*)a.ws;
-        float* wsM = (float*)(wsO + (size_t)a.n_rows * a.n_splits * H * 512);
-        float* wsL = wsM + (size_t)a.n_rows * a.n_splits * H;
-        if (cb < ce) {
-            const float inv = 1.0f / l_run;
-            uint16_t* orow = wsO + ps * 512 + cbase;
-#pragma unroll
-            for (int ct = 0; ct < 16; ++ct) {
-                const _Float16 v0 = (_Float16)(oacc[ct][0] * inv), v1 = (_Float16)(oacc[ct][1] * inv);
-                const _Float16 v2 = (_Float16)(oacc[ct][2] * inv), v3 = (_Float16)(oacc[ct][3] * inv);
-                const uint2 pk = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16),
-                                            (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16));
-                *(uint2*)(orow + 16 * ct + 4 * g) = pk;
-            }
-        }
-        if (g == 0 && half == 0) { wsM[ps] = m_run; wsL[ps] = l_run; }
-        return;
-    }
-    // ---- single split: merge with the external partial and the sink here
-    const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * H + h] : -INFINITY;
-    const float sk = a.sink ? a.sink[h] : -INFINITY;
+    const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * a.n_heads + h] * LOG2E : -INFINITY;
+    const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
     const float M = fmaxf(fmaxf(m_run, lse_p), sk);
-    const float w_run = (m_run == -INFINITY) ? 0.0f : expf(m_run - M);
-    const float w_p = (lse_p == -INFINITY) ? 0.0f : expf(lse_p - M);
-    const float w_s = (sk == -INFINITY) ? 0.0f : expf(sk - M);
+    const float w_run = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    const float w_p = (lse_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lse_p - M);
+    const float w_s = (sk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sk - M);
     const float den = w_run * l_run + w_p + w_s;
     const float inv = (M == -INFINITY || den == 0.0f) ? 0.0f : 1.0f / den;
-    const float* oin = a.o_in ? a.o_in + ((int64_t)row * H + h) * 512 : nullptr;
-    float* orow = a.out + ((int64_t)row * H + h) * 512;
+    const float wo = ldexpf(w_run, -tw);
+    const float* oin = a.o_in ? a.o_in + ((int64_t)row * a.n_heads + h) * 512 : nullptr;
+    float* orow = a.out + ((int64_t)row * a.n_heads + h) * 512;
 #pragma unroll
-    for (int ct = 0; ct < 16; ++ct) {
-        const int c = cbase + 16 * ct + 4 * g;
-        const float4 pin = oin ? *(const float4*)(oin + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int ct = 0; ct < 4; ++ct) {
+        const int ch = 64 * wave + 16 * ct + 4 * g;
+        const float4 pin = oin ? *(const float4*)(oin + ch) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         float4 r;
-        r.x = (w_run * oacc[ct][0] + w_p * pin.x) * inv;
-        r.y = (w_run * oacc[ct][1] + w_p * pin.y) * inv;
-        r.z = (w_run * oacc[ct][2] + w_p * pin.z) * inv;
-        r.w = (w_run * oacc[ct][3] + w_p * pin.w) * inv;
-        *(float4*)(orow + c) = r;
+        r.x = (wo * oacc[ct][0] + w_p * pin.x) * inv;
+        r.y = (wo * oacc[ct][1] + w_p * pin.y) * inv;
+        r.z = (wo * oacc[ct][2] + w_p * pin.z) * inv;
+        r.w = (wo * oacc[ct][3] + w_p * pin.w) * inv;
+        *(float4*)(orow + ch) = r;
     }
-    if (a.lse_out && g == 0 && half == 0)
-        a.lse_out[(int64_t)row * H + h] = (M == -INFINITY || den == 0.0f) ? -INFINITY : M + logf(den);
-}
-
-// out = (sum_s e^(m_s - M) l_s o_s + e^(lse_in - M) o_in) / (sum_s e^(m_s - M) l_s + e^(lse_in - M) + e^(sink - M))
-// with o_s the normalised fp16 partial of split s.  One thread per (head, 8 channels).
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-    const int H = a.n_heads, S = a.n_splits;
-    const int row = blockIdx.y;
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= H * 64) return;
-    const int h = t >> 6, c8 = t & 63;
-    const uint16_t* wsO = (const uint16_t*)a.ws;
-    const float* wsM = (const float*)(wsO + (size_t)a.n_rows * S * H * 512);
-    const float* wsL = wsM + (size_t)a.n_rows * S * H;
-    float ms[AT_MAX_SPLITS];
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) {
-        ms[s] = wsM[((size_t)row * S + s) * H + h];
-        M = fmaxf(M, ms[s]);
-    }
-    const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * H + h] : -INFINITY;
-    const float sk = a.sink ? a.sink[h] : -INFINITY;
-    M = fmaxf(fmaxf(M, lse_p), sk);
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float den = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            if (ms[s] == -INFINITY) continue;
-            const size_t ps = ((size_t)row * S + s) * H + h;
-            const float wgt = expf(ms[s] - M) * wsL[ps];
-            den += wgt;
-            const uint4 v = *(const uint4*)(wsO + ps * 512 + 8 * c8);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f16x2 pr = __builtin_bit_cast(f16x2, wv[i]);
-                o[2 * i] += wgt * (float)pr[0];
-                o[2 * i + 1] += wgt * (float)pr[1];
-            }
-        }
-        if (lse_p != -INFINITY) {
-            const float wgt = expf(lse_p - M);
-            den += wgt;
-            const float* pin = a.o_in + ((int64_t)row * H + h) * 512 + 8 * c8;
-            const float4 v0 = *(const float4*)pin, v1 = *(const float4*)(pin + 4);
-            o[0] += wgt * v0.x; o[1] += wgt * v0.y; o[2] += wgt * v0.z; o[3] += wgt * v0.w;
-            o[4] += wgt * v1.x; o[5] += wgt * v1.y; o[6] += wgt * v1.z; o[7] += wgt * v1.w;
-        }
-        if (sk != -INFINITY) den += expf(sk - M);
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    float* orow = a.out + ((int64_t)row * H + h) * 512 + 8 * c8;
-    *(float4*)orow = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-    *(float4*)(orow + 4) = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
-    if (a.lse_out && c8 == 0) a.lse_out[(int64_t)row * H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
+    if (a.lse_out && wave == 0 && g == 0)
+        a.lse_out[(int64_t)row * a.n_heads + h] = (M == -INFINITY || den == 0.0f) ? -INFINITY : (M + log2f(den)) * LN2;
 }
 
 static bool g_attr_set = false;
@@ -444,25 +461,13 @@ static hipError_t set_lds_attrs() {
     return hipSuccess;
 }
 
-hipError_t launch_attn(const KvView& kv, const AttnArgs& a_in, hipStream_t st) {
+hipError_t launch_attn(const KvView& kv, const AttnArgs& a, hipStream_t st) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
-    AttnArgs a = a_in;
-    a.n_splits = attn_splits(a.n_rows);
-    if (a.n_splits > a.max_chunks) a.n_splits = a.max_chunks > 0 ? a.max_chunks : 1;
-    const int hg = (a.n_heads + AT_HEADS_PER_WG - 1) / AT_HEADS_PER_WG;
-    const int heads_in_wg = a.n_heads < AT_HEADS_PER_WG ? a.n_heads : AT_HEADS_PER_WG;
-    const dim3 grid((unsigned)a.n_splits, (unsigned)a.n_rows, (unsigned)hg);
-    const dim3 block((unsigned)(2 * 64 * (heads_in_wg / 16)));
-    if (a.q_bf16) hipLaunchKernelGGL(attn_kernel<true>, grid, block, AT_LDS, st, kv, a);
-    else hipLaunchKernelGGL(attn_kernel<false>, grid, block, AT_LDS, st, kv, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.n_splits > 1) {
-        const dim3 mgrid((unsigned)((a.n_heads * 64 + 255) / 256), (unsigned)a.n_rows);
-        hipLaunchKernelGGL(attn_merge_kernel, mgrid, dim3(256), 0, st, a);
-        e = hipGetLastError();
-    }
-    return e;
+    const unsigned blocks = (unsigned)a.n_rows * (unsigned)(a.n_heads >> 4);
+    if (a.q_bf16) hipLaunchKernelGGL(attn_kernel<true>, dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else hipLaunchKernelGGL(attn_kernel<false>, dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    return hipGetLastError();
 }
 
 }  // namespace csa2

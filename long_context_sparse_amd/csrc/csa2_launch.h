@@ -67,11 +67,7 @@ struct AttnArgs {
     const float* lse_in;
     float* out;
     float* lse_out;
-    float* ws;
-    int n_splits;                // set by launch_attn
-    int max_chunks;              // upper bound on 64-entry chunks per row
 };
-size_t attn_workspace_bytes(int n_rows, int n_heads);
 hipError_t launch_attn(const KvView& kv, const AttnArgs& a, hipStream_t st);
 
 hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,

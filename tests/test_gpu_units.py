@@ -298,13 +298,12 @@ def test_full_path_empty_and_short_rows():
     icnt = torch.empty(n_rows, dtype=torch.int32, device=DEV)
     out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
-    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256), dtype=torch.uint8, device=DEV)
     lib.csa2_index_score(kv, rows, T(q), T(w), scores=scores, block_max=bmax)
     lib.csa2_select_topk(bmax, 2048, pool, pcnt, n_cols=nv, cols_div=8, max_cols=nv8 // 8)
     lib.csa2_select_topk(scores, 512, idx, icnt, n_cols=pcnt, cols_mul=8, pool_blocks=pool, keys_by_id=True,
                          max_cols=16384)
     lib.csa2_sparse_swa_attn(kv, rows, bf16(qa).to(DEV), idx, icnt, T(wc), T(wsc),
-                             T(np.arange(n_rows, dtype=np.int64) * 128), T(swa_counts), SIG, out, ws, lse=lse)
+                             T(np.arange(n_rows, dtype=np.int64) * 128), T(swa_counts), SIG, out, lse=lse)
     torch.cuda.synchronize()
     qc, qs = oracle.quant_query(q.reshape(-1, 128))
     K = oracle.dequant_main(mc, ms)
@@ -343,7 +342,6 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
     kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), n_slots=n_rows * n_entries, req_stride=n_entries)
     rows = lib.make_rows(T(np.arange(n_rows, dtype=np.int32)), T(np.full(n_rows, n_entries, np.int32)), n_entries)
     qd = torch.as_tensor(q).to(qdt).to(DEV)
-    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256), dtype=torch.uint8, device=DEV)
     idx_d, cnt_d = T(idx), T(np.asarray(counts, np.int32))
     wc_d, wsc_d = T(wc), T(wsc)
     first = T(np.arange(n_rows, dtype=np.int64) * 128)
@@ -352,13 +350,13 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
     # two-call form
     o_p = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
-    lib.csa2_sparse_attn(kv, rows, qd, idx_d, cnt_d, SIG, o_p, lse, ws)
+    lib.csa2_sparse_attn(kv, rows, qd, idx_d, cnt_d, SIG, o_p, lse)
     out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
-    lib.csa2_swa_merge(wc_d, wsc_d, first, swc, qd, SIG, out, ws, sink=sk_d, o_partial=o_p, lse=lse)
+    lib.csa2_swa_merge(wc_d, wsc_d, first, swc, qd, SIG, out, sink=sk_d, o_partial=o_p, lse=lse)
     # one-pass form
     out2 = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse2 = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
-    lib.csa2_sparse_swa_attn(kv, rows, qd, idx_d, cnt_d, wc_d, wsc_d, first, swc, SIG, out2, ws, sink=sk_d, lse=lse2)
+    lib.csa2_sparse_swa_attn(kv, rows, qd, idx_d, cnt_d, wc_d, wsc_d, first, swc, SIG, out2, sink=sk_d, lse=lse2)
     torch.cuda.synchronize()
     O_p, L_p, Out, Out2, L2 = (t.cpu().numpy() for t in (o_p, lse, out, out2, lse2))
     for r in (range(n_rows) if check_rows is None else check_rows):
@@ -394,7 +392,7 @@ def test_attention_fp32_query():
 
 @pytest.mark.parametrize("n_rows", [300, 2600])
 def test_attention_many_rows(n_rows):
-    """Fewer splits per row (300 rows) and one workgroup per row (2,600 rows)."""
+    """Many rows with ragged selected and window counts (one workgroup per row and head group)."""
     counts = [int(c) for c in RNG.integers(0, 130, n_rows)]
     swa_counts = [int(c) for c in RNG.integers(0, 129, n_rows)]
     counts[0], swa_counts[0] = 512, 128
@@ -408,9 +406,8 @@ def test_swa_only_and_alias():
     W = oracle.dequant_swa(wc, wsc)
     q = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32)).float().numpy()
     out = torch.full((n_rows, H, 512), 5.0, dtype=torch.float32, device=DEV)
-    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256), dtype=torch.uint8, device=DEV)
     lib.csa2_swa_merge(T(wc), T(wsc), T(np.array([0, 128], np.int64)), T(np.array([128, 37], np.int32)),
-                       bf16(q).to(DEV), SIG, out, ws)
+                       bf16(q).to(DEV), SIG, out)
     torch.cuda.synchronize()
     for r, c in enumerate([128, 37]):
         ref, _ = oracle.attention(q[r], None, W[r * 128:r * 128 + c], sigma=SIG)
@@ -419,7 +416,7 @@ def test_swa_only_and_alias():
     o_p = torch.zeros((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.full((n_rows, H), -np.inf, dtype=torch.float32, device=DEV)
     lib.csa2_swa_merge(T(wc), T(wsc), T(np.array([0, 128], np.int64)), T(np.array([128, 37], np.int32)),
-                       bf16(q).to(DEV), SIG, o_p, ws, o_partial=o_p, lse=lse)
+                       bf16(q).to(DEV), SIG, o_p, o_partial=o_p, lse=lse)
     torch.cuda.synchronize()
     for r, c in enumerate([128, 37]):
         ref, _ = oracle.attention(q[r], None, W[r * 128:r * 128 + c], sigma=SIG)
