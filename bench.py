@@ -130,7 +130,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- per-kernel breakdown (separate, untimed pass)
-    names = ["index_score", "select_blocks", "select_positions", "attention"]
+    names = ["index_score", "select", "attention"]
     if cfg.mode != "full" and cfg.mode != "mixed":
         names = ["index_score", "select_positions", "attention"]
     per = {n: [] for n in names}

@@ -81,6 +81,7 @@ typedef enum { CSA2_MAIN_FP4 = 0, CSA2_INDEX_MXFP4 = 1, CSA2_SWA_FP8 = 2 } csa2_
 #define CSA2_TOPK 512
 #define CSA2_WINDOW 128
 #define CSA2_MAX_SELECT 2048  /* largest k csa2_select_topk accepts */
+#define CSA2_MAX_POOL_BLOCKS 2048  /* largest pool csa2_select_full builds */
 
 /* The global (compressed) KV cache: MAIN and INDEX planes indexed by entry id.
  *   page_entries == 0: contiguous; entry(req, pos) = req * req_stride + pos.
@@ -169,6 +170,27 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride,
                              const int32_t* pool_blocks, int64_t pool_stride, int32_t keys_by_id,
                              int32_t n_rows, int32_t max_cols, int32_t k,
                              int32_t* out_ids, int64_t out_stride, int32_t* out_count,
+                             void* stream);
+
+/* The Full layer's selection in one pass per row (V4.1-Flash architecture
+ * page, hierarchical sparse indexer: the first Full layer keeps up to 2,048
+ * groups of 8 positions ranked by their maximum and picks its own top-512
+ * among them).  Same result as two csa2_select_topk calls:
+ *   pool = top-n_pool_blocks of block_max[r][0 .. ceil(n_vis[r]/8)) by
+ *          (maximum descending, block ascending), ids ascending, -1 padded,
+ *          count in pool_count[r];
+ *   idx  = top-k of scores[r][p] over the pool's positions p = 8 b + i
+ *          (i < 8), ids ascending, -1 padded, count in idx_count[r].
+ * block_max and scores are csa2_index_score's full-scan outputs (scores
+ * beyond n_vis up to a multiple of 8 hold -inf); scores rows 16-B aligned
+ * (scores_stride a multiple of 4).  1 <= n_pool_blocks <= 2,048,
+ * 1 <= k <= 2,048. */
+csa2_status csa2_select_full(const float* block_max, int64_t block_max_stride,
+                             const float* scores, int64_t scores_stride,
+                             const int32_t* n_vis, int32_t n_rows, int32_t max_vis,
+                             int32_t n_pool_blocks, int32_t k,
+                             int32_t* pool, int64_t pool_stride, int32_t* pool_count,
+                             int32_t* idx, int64_t idx_stride, int32_t* idx_count,
                              void* stream);
 
 /* ---------------------------------------------------------------- attention

@@ -46,7 +46,7 @@ class Rows(ctypes.Structure):
 _lib = None
 EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
-    "csa2_select_topk", "csa2_sparse_attn", "csa2_swa_merge",
+    "csa2_select_topk", "csa2_select_full", "csa2_sparse_attn", "csa2_swa_merge",
     "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost",
 )
 
@@ -68,6 +68,7 @@ def lib():
     L.csa2_index_score.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P,
                                    P, i64, P, P, i64, P, i64, P]
     L.csa2_select_topk.argtypes = [P, i64, P, i32, i32, P, i64, i32, i32, i32, i32, P, i64, P, P]
+    L.csa2_select_full.argtypes = [P, i64, P, i64, P, i32, i32, i32, i32, P, i64, P, P, i64, P, P]
     L.csa2_sparse_attn.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P, i64, P,
                                    f32, P, P, P]
     L.csa2_swa_merge.argtypes = [P, P, i64, P, P, i32, P, ctypes.c_int, i32, f32, P, P, P, P, P]
@@ -165,6 +166,17 @@ def csa2_select_topk(keys, k, out_ids, out_count, n_cols=None, cols_mul=1, cols_
         _ptr(keys), _rstride(keys), _ptr(n_cols), cols_mul, cols_div, _ptr(pool_blocks),
         0 if pool_blocks is None else _rstride(pool_blocks), int(bool(keys_by_id)), n_rows,
         int(max_cols), int(k), _ptr(out_ids), _rstride(out_ids), _ptr(out_count), _stream(stream)))
+
+
+def csa2_select_full(block_max, scores, n_vis, max_vis, pool, pool_count, idx, idx_count, n_pool_blocks=2048,
+                     k=512, stream=None):
+    """The Full layer's pool (top n_pool_blocks blocks by maximum) and its
+    top-k positions, in one pass per row."""
+    n_rows = int(pool.shape[0])
+    _check("csa2_select_full", lib().csa2_select_full(
+        _ptr(block_max), _rstride(block_max), _ptr(scores), _rstride(scores), _ptr(n_vis), n_rows, int(max_vis),
+        int(n_pool_blocks), int(k), _ptr(pool), _rstride(pool), _ptr(pool_count), _ptr(idx), _rstride(idx),
+        _ptr(idx_count), _stream(stream)))
 
 
 def csa2_sparse_attn(kv, rows, q, idx, idx_count, softmax_scale, o_partial, lse, stream=None):

@@ -231,6 +231,44 @@ static void fill_q(csa2::AttnArgs& a, const void* q, csa2_dtype q_dtype, int32_t
     a.scale = scale;
 }
 
+csa2_status csa2_select_full(const float* block_max, int64_t block_max_stride, const float* scores,
+                             int64_t scores_stride, const int32_t* n_vis, int32_t n_rows, int32_t max_vis,
+                             int32_t n_pool_blocks, int32_t k, int32_t* pool, int64_t pool_stride,
+                             int32_t* pool_count, int32_t* idx, int64_t idx_stride, int32_t* idx_count,
+                             void* stream) {
+    if (n_rows < 0 || n_rows > 65535) return fail(CSA2_ERR_RANGE, "n_rows out of range");
+    if (max_vis < 0 || max_vis > (1 << 24)) return fail(CSA2_ERR_RANGE, "max_vis out of range");
+    if (n_pool_blocks < 1 || n_pool_blocks > CSA2_MAX_POOL_BLOCKS)
+        return fail(CSA2_ERR_RANGE, "n_pool_blocks must be in 1..%d (got %d)", CSA2_MAX_POOL_BLOCKS, n_pool_blocks);
+    if (k < 1 || k > CSA2_MAX_SELECT) return fail(CSA2_ERR_RANGE, "k must be in 1..%d (got %d)", CSA2_MAX_SELECT, k);
+    if (n_rows == 0) return CSA2_OK;
+    if (!block_max || !scores || !n_vis || !pool || !pool_count || !idx || !idx_count)
+        return fail(CSA2_ERR_NULL, "a required pointer is NULL");
+    const int64_t nv8 = ((int64_t)max_vis + 7) & ~(int64_t)7;
+    if (block_max_stride < nv8 / 8) return fail(CSA2_ERR_SHAPE, "block_max_stride < ceil(max_vis / 8)");
+    if (scores_stride < nv8) return fail(CSA2_ERR_SHAPE, "scores_stride < roundup(max_vis, 8)");
+    if (pool_stride < n_pool_blocks) return fail(CSA2_ERR_SHAPE, "pool_stride < n_pool_blocks");
+    if (idx_stride < k) return fail(CSA2_ERR_SHAPE, "idx_stride < k");
+    if (!aligned(scores, 16) || scores_stride % 4) return fail(CSA2_ERR_ALIGN, "scores rows must be 16-byte aligned");
+    csa2::SelectFullArgs a;
+    a.block_max = block_max;
+    a.block_max_stride = block_max_stride;
+    a.scores = scores;
+    a.scores_stride = scores_stride;
+    a.n_vis = n_vis;
+    a.n_rows = n_rows;
+    a.max_vis = max_vis;
+    a.n_pool = n_pool_blocks;
+    a.k = k;
+    a.pool = pool;
+    a.pool_stride = pool_stride;
+    a.pool_count = pool_count;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.idx_count = idx_count;
+    return hip_status(csa2::launch_select_full(a, (hipStream_t)stream), "csa2_select_full launch");
+}
+
 csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
                              int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
                              float softmax_scale, float* o_partial, float* lse, void* stream) {

@@ -46,6 +46,24 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
+// The Full layer's two selections in one pass per row: the pool (top n_pool
+// blocks by block maximum) and the top k positions among the pool's scores.
+struct SelectFullArgs {
+    const float* block_max;
+    int64_t block_max_stride;
+    const float* scores;          // 16-B aligned rows, -inf past n_vis up to a multiple of 8
+    int64_t scores_stride;
+    const int32_t* n_vis;
+    int n_rows, max_vis, n_pool, k;
+    int32_t* pool;
+    int64_t pool_stride;
+    int32_t* pool_count;
+    int32_t* idx;
+    int64_t idx_stride;
+    int32_t* idx_count;
+};
+hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st);
+
 // Joint attention over a row's selected FP4 entries (idx) and its 8-bit
 // window (swa_*), plus an optional external partial (o_in, lse_in) and sink.
 struct AttnArgs {

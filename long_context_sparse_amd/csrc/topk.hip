@@ -7,16 +7,26 @@
 // are in id order, so ties go to the lower position / block.
 //
 // One 1024-thread workgroup per row.  Keys become order-preserving 32-bit
-// integers.  The bits above the highest bit in which the smallest and the
-// largest present key differ are common to every key and are skipped; an
-// MSB-first radix select then resolves 12, 10 and 10 bits per pass with an
-// LDS histogram of 4,096 bins (scores of one row share few exponent values,
-// so a digit that covers only exponent bits would send most atomics to one
-// bin; 12 bits reach into the mantissa), and stops as soon as the bin
-// holding the k-th key is taken whole.  A block-wide scan in column order
-// writes the selected ids ascending.  Thread t owns columns [16t, 16t+16) of
-// each 16,384-column sweep, so column order is thread order, then item order.
-// Rows of at most 16,384 columns stay in registers; longer rows are re-read.
+// integers (-inf = 0 = absent).  The bits above the highest bit in which the
+// smallest and the largest present key differ are common to every key and
+// are skipped; an MSB-first radix select then resolves 12, 10 and 10 bits per
+// pass with an LDS histogram of 4,096 bins (scores of one row share few
+// exponent values, so a digit that covers only exponent bits would send most
+// atomics to one bin; 12 bits reach into the mantissa), and stops as soon as
+// the bin holding the k-th key is taken whole.  A block-wide scan in column
+// order writes the selected ids ascending.  Thread t owns columns
+// [16t, 16t+16) of each 16,384-column sweep, so column order is thread order,
+// then item order.  Rows of at most 16,384 columns stay in registers; longer
+// rows are re-read.
+//
+// Wave-level scans and reductions use DPP row shifts and row broadcasts (no
+// LDS round trips); the 16 wave totals meet in LDS behind one barrier, and
+// every thread forms its own prefix from them.  A radix pass costs three
+// barriers.
+//
+// The Full layer's two selections (2,048 blocks by their maxima, then 512
+// positions among those blocks' scores) also run fused in one workgroup per
+// row, with the pool kept in LDS between them.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -26,68 +36,201 @@ constexpr int TK_THREADS = 1024;
 constexpr int TK_ITEMS = 16;
 constexpr int TK_SWEEP = TK_THREADS * TK_ITEMS;
 constexpr int TK_WAVES = TK_THREADS / 64;
-
 constexpr int TK_BINS = 4096;
+constexpr int TK_POOL = 2048;
 
-struct TkShared {
+struct __align__(16) TkShared {
     uint32_t hist[TK_BINS];
-    uint32_t part[TK_WAVES];
+    uint32_t part[2][TK_WAVES];
     uint32_t red[3][TK_WAVES];
     uint32_t digit, above, count;
+    int32_t pool[TK_POOL];             // fused selection: the row's pool, ascending
 };
 
-// Exclusive scan of v over the workgroup in thread order; `total` gets the sum.
+// ---------------------------------------------------------------- wave primitives
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t x, uint32_t identity) {
+    return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive scan (sum) over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x += dpp<0x111>(x, 0u);            // row_shr:1
+    x += dpp<0x112>(x, 0u);            // row_shr:2
+    x += dpp<0x114>(x, 0u);            // row_shr:4
+    x += dpp<0x118>(x, 0u);            // row_shr:8
+    x += dpp<0x142, 0xA>(x, 0u);       // row_bcast:15 into rows 1 and 3
+    x += dpp<0x143, 0xC>(x, 0u);       // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = max(x, dpp<0x111>(x, 0u));
+    x = max(x, dpp<0x112>(x, 0u));
+    x = max(x, dpp<0x114>(x, 0u));
+    x = max(x, dpp<0x118>(x, 0u));
+    x = max(x, dpp<0x142, 0xA>(x, 0u));
+    x = max(x, dpp<0x143, 0xC>(x, 0u));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+    x = min(x, dpp<0x111>(x, 0xFFFFFFFFu));
+    x = min(x, dpp<0x112>(x, 0xFFFFFFFFu));
+    x = min(x, dpp<0x114>(x, 0xFFFFFFFFu));
+    x = min(x, dpp<0x118>(x, 0xFFFFFFFFu));
+    x = min(x, dpp<0x142, 0xA>(x, 0xFFFFFFFFu));
+    x = min(x, dpp<0x143, 0xC>(x, 0xFFFFFFFFu));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Exclusive scan of v over the workgroup in thread order; `total` gets the
+// sum.  One barrier; part[buf] must not be in use by a previous scan.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, uint32_t& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
+    const uint32_t incl = wave_incl_sum(v);
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
+    for (int w = 0; w < TK_WAVES; ++w) {
+        const uint32_t p = part[w];
+        before += (w < wave) ? p : 0u;
+        tot += p;
     }
-    if (lane == 63) part[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-        uint32_t p = lane < TK_WAVES ? part[lane] : 0u;
-#pragma unroll
-        for (int d = 1; d < TK_WAVES; d <<= 1) {
-            const uint32_t y = __shfl_up(p, d, 64);
-            if (lane >= d) p += y;
-        }
-        if (lane < TK_WAVES) part[lane] = p;
-    }
-    __syncthreads();
-    const uint32_t base = wave > 0 ? part[wave - 1] : 0u;
-    total = part[TK_WAVES - 1];
-    __syncthreads();
-    return base + x - v;
+    total = tot;
+    return before + incl - v;
 }
 
-__device__ __forceinline__ int col_id(const int32_t* pool, int c) {
-    return pool ? 8 * pool[c >> 3] + (c & 7) : c;
-}
+// ---------------------------------------------------------------- one row's selection
+// KEYS(sweep, u) fills u[16] with the order keys of columns
+// sweep*16384 + 16*threadIdx.x + i (0 where absent); EMIT(col, slot) writes
+// the id of selected column `col` to output slot `slot`.  Returns the count.
+template <class KEYS, class EMIT>
+__device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nsweep = (ncols + TK_SWEEP - 1) / TK_SWEEP;
+    uint32_t u[TK_ITEMS];
+#pragma unroll
+    for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
 
-__device__ __forceinline__ void load_sweep(const TopkArgs& a, const float* krow, const int32_t* pool,
-                                           int ncols, int sweep, uint32_t* u) {
-    const int c0 = sweep * TK_SWEEP + threadIdx.x * TK_ITEMS;   // a multiple of 16
-    if (a.keys_by_id) {
-        // columns c0 .. c0+15 are the two pool blocks c0/8 and c0/8 + 1: two runs of 8 keys
+    // ---- count, min and max of the present keys; clear the histogram
+    uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
+    for (int s = 0; s < nsweep; ++s) {
+        keys(s, u);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int cb = c0 + 8 * h;
-            if (cb < ncols) {
-                const float* p = krow + 8 * pool[cb >> 3];
-                const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
-                const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        for (int i = 0; i < TK_ITEMS; ++i)
+            if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
+    }
+    for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
+    cnt = __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
+    umin = wave_min(umin);
+    umax = wave_max(umax);
+    if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = umin; sh.red[2][wave] = umax; }
+    __syncthreads();
+    uint32_t n_present = 0;
+    umin = 0xFFFFFFFFu; umax = 0u;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) u[8 * h + i] = cb + i < ncols ? order_key(v[i]) : 0u;
-            } else {
+    for (int w = 0; w < TK_WAVES; ++w) {
+        n_present += sh.red[0][w];
+        umin = min(umin, sh.red[1][w]);
+        umax = max(umax, sh.red[2][w]);
+    }
+
+    // ---- radix select: prefix/mask describe the bits decided so far
+    uint32_t prefix = 0u, mask = 0u, need = 0u;   // select (u & mask) > prefix, or == prefix for the first `need`
+    int pb = 0;                                    // part buffer of the next scan
+    if (n_present > (uint32_t)k) {
+        const uint32_t diff = umin ^ umax;
+        int hb = diff ? 31 - __clz(diff) : -1;     // highest bit that is not common to all keys
+        mask = hb < 0 ? 0xFFFFFFFFu : (hb >= 31 ? 0u : ~((2u << hb) - 1u));
+        prefix = umin & mask;
+        uint32_t rem = (uint32_t)k;
+        uint32_t in_bin = n_present;
+        int pass = 0;
+        while (hb >= 0 && in_bin != rem) {
+            const int wbits = pass == 0 ? 12 : 10;
+            const int shift = hb >= wbits - 1 ? hb - (wbits - 1) : 0;
+            const int width = hb - shift + 1;
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int s = 0; s < nsweep; ++s) {
+                if (nsweep > 1) keys(s, u);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) u[8 * h + i] = 0u;
+                for (int i = 0; i < TK_ITEMS; ++i)
+                    if (u[i] != 0u && (u[i] & mask) == prefix) atomicAdd(&sh.hist[(u[i] >> shift) & dmask], 1u);
             }
+            __syncthreads();
+            // thread t owns the 4 bins 4095-4t .. 4092-4t (descending digits);
+            // it reads them once and clears them for the next pass
+            const int b0 = TK_BINS - 4 - 4 * threadIdx.x;
+            const uint4 hv = *(const uint4*)&sh.hist[b0];
+            *(uint4*)&sh.hist[b0] = make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t hb4[4] = {hv.w, hv.z, hv.y, hv.x};
+            const uint32_t h = hb4[0] + hb4[1] + hb4[2] + hb4[3];
+            uint32_t tot;
+            uint32_t before = block_excl_scan(h, sh.part[pb], tot);
+            pb ^= 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (hb4[j] != 0u && before < rem && rem <= before + hb4[j]) {
+                    sh.digit = (uint32_t)(b0 + 3 - j);
+                    sh.above = before;
+                    sh.count = hb4[j];
+                }
+                before += hb4[j];
+            }
+            __syncthreads();
+            prefix |= sh.digit << shift;
+            mask |= dmask << shift;
+            rem -= sh.above;
+            in_bin = sh.count;
+            hb = shift - 1;
+            ++pass;
         }
-        return;
+        need = rem;
     }
+    const bool take_all = n_present <= (uint32_t)k;
+
+    // ---- selection in column order: one scan of (greater, equal) counts; the
+    // equal items taken before a thread are min(equal before it, need)
+    uint32_t gt_base = 0u, eq_base = 0u;
+    for (int s = 0; s < nsweep; ++s) {
+        if (nsweep > 1) keys(s, u);
+        uint32_t n_gt = 0u, n_eq = 0u;
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; ++i) {
+            if (u[i] == 0u) continue;
+            if (take_all) { n_gt++; continue; }
+            const uint32_t hi = u[i] & mask;
+            n_gt += hi > prefix;
+            n_eq += hi == prefix;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, sh.part[pb], tot);
+        pb ^= 1;
+        uint32_t eq_rank = eq_base + (ex & 0xFFFFu);
+        uint32_t pos = gt_base + (ex >> 16) + min(eq_rank, need);
+        const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; ++i) {
+            if (u[i] == 0u) continue;
+            bool sel;
+            if (take_all) sel = true;
+            else {
+                const uint32_t hi = u[i] & mask;
+                sel = hi > prefix;
+                if (hi == prefix) { sel = eq_rank < need; eq_rank++; }
+            }
+            if (sel) emit(c0 + i, pos++);
+        }
+        gt_base += tot >> 16;
+        eq_base += tot & 0xFFFFu;
+    }
+    return gt_base + min(eq_base, need);
+}
+
+// Keys of 16 consecutive columns c0 .. c0+15 of a row (absent past ncols).
+__device__ __forceinline__ void load_cols(const float* krow, int ncols, int c0, uint32_t* u) {
     if (c0 + TK_ITEMS <= ncols && ((uintptr_t)(krow + c0) & 15) == 0) {
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; i += 4) {
@@ -103,142 +246,87 @@ __device__ __forceinline__ void load_sweep(const TopkArgs& a, const float* krow,
     }
 }
 
+// Keys of the two pool blocks behind columns c0 .. c0+15 (c0 a multiple of
+// 16), read by position from a 16-B aligned row: two runs of 8 keys.
+__device__ __forceinline__ void load_pool_keys(const float* krow, const int32_t* pool, int ncols, int c0, uint32_t* u) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cb = c0 + 8 * h;
+        if (cb < ncols) {
+            const float* p = krow + 8 * pool[cb >> 3];
+            const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
+            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[8 * h + i] = cb + i < ncols ? order_key(v[i]) : 0u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[8 * h + i] = 0u;
+        }
+    }
+}
+
+__device__ __forceinline__ int col_id(const int32_t* pool, int c) {
+    return pool ? 8 * pool[c >> 3] + (c & 7) : c;
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     __shared__ TkShared sh;
     const int row = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int ncols = a.max_cols;
     if (a.n_cols) {
         const int64_t v = ((int64_t)a.n_cols[row] * a.cols_mul + a.cols_div - 1) / a.cols_div;
         ncols = (int)(v < a.max_cols ? (v > 0 ? v : 0) : a.max_cols);
     }
-    const int nsweep = (ncols + TK_SWEEP - 1) / TK_SWEEP;
     const float* krow = a.keys + (int64_t)row * a.key_stride;
     const int32_t* pool = a.pool ? a.pool + (int64_t)row * a.pool_stride : nullptr;
     int32_t* orow = a.out_ids + (int64_t)row * a.out_stride;
-
-    uint32_t u[TK_ITEMS];
-#pragma unroll
-    for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
-
-    // ---- count, min and max of the present keys
-    uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
-    for (int s = 0; s < nsweep; ++s) {
-        load_sweep(a, krow, pool, ncols, s, u);
-#pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i)
-            if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
-    }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        cnt += __shfl_xor(cnt, d, 64);
-        umin = min(umin, (uint32_t)__shfl_xor(umin, d, 64));
-        umax = max(umax, (uint32_t)__shfl_xor(umax, d, 64));
-    }
-    if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = umin; sh.red[2][wave] = umax; }
-    __syncthreads();
-    uint32_t n_present = 0;
-    umin = 0xFFFFFFFFu; umax = 0u;
-#pragma unroll
-    for (int w = 0; w < TK_WAVES; ++w) {
-        n_present += sh.red[0][w];
-        umin = min(umin, sh.red[1][w]);
-        umax = max(umax, sh.red[2][w]);
-    }
-
-    // ---- radix select: prefix/mask describe the bits decided so far
-    uint32_t prefix = 0u, mask = 0u, need = 0u;   // select (u & mask) > prefix, or == prefix for the first `need`
-    if (n_present > (uint32_t)a.k) {
-        const uint32_t diff = umin ^ umax;
-        int hb = diff ? 31 - __clz(diff) : -1;   // highest bit that is not common to all keys
-        mask = hb < 0 ? 0xFFFFFFFFu : (hb >= 31 ? 0u : ~((2u << hb) - 1u));
-        prefix = umin & mask;
-        uint32_t rem = (uint32_t)a.k;
-        uint32_t in_bin = n_present;
-        int pass = 0;
-        while (hb >= 0 && in_bin != rem) {
-            const int wbits = pass == 0 ? 12 : 10;
-            const int shift = hb >= wbits - 1 ? hb - (wbits - 1) : 0;
-            const int width = hb - shift + 1;
-            const uint32_t dmask = (1u << width) - 1u;
-            for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
-            __syncthreads();
-            for (int s = 0; s < nsweep; ++s) {
-                if (nsweep > 1) load_sweep(a, krow, pool, ncols, s, u);
-#pragma unroll
-                for (int i = 0; i < TK_ITEMS; ++i)
-                    if (u[i] != 0u && (u[i] & mask) == prefix) atomicAdd(&sh.hist[(u[i] >> shift) & dmask], 1u);
-            }
-            __syncthreads();
-            // thread t owns the 4 bins 4095-4t .. 4092-4t (descending digits)
-            uint32_t hb4[4], h = 0u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { hb4[j] = sh.hist[TK_BINS - 1 - 4 * threadIdx.x - j]; h += hb4[j]; }
-            uint32_t tot;
-            uint32_t before = block_excl_scan(h, sh.part, tot);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (hb4[j] != 0u && before < rem && rem <= before + hb4[j]) {
-                    sh.digit = (uint32_t)(TK_BINS - 1 - 4 * threadIdx.x - j);
-                    sh.above = before;
-                    sh.count = hb4[j];
-                }
-                before += hb4[j];
-            }
-            __syncthreads();
-            prefix |= sh.digit << shift;
-            mask |= dmask << shift;
-            rem -= sh.above;
-            in_bin = sh.count;
-            hb = shift - 1;
-            ++pass;
-            __syncthreads();
-        }
-        need = rem;
-    }
-    const bool take_all = n_present <= (uint32_t)a.k;
-
-    // ---- selection in column order: one scan of (greater, equal) counts; the
-    // equal items taken before a thread are min(equal before it, need)
-    uint32_t gt_base = 0u, eq_base = 0u, out_base = 0u;
-    for (int s = 0; s < nsweep; ++s) {
-        if (nsweep > 1) load_sweep(a, krow, pool, ncols, s, u);
-        uint32_t n_gt = 0u, n_eq = 0u;
-#pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i) {
-            if (u[i] == 0u) continue;
-            if (take_all) { n_gt++; continue; }
-            const uint32_t hi = u[i] & mask;
-            n_gt += hi > prefix;
-            n_eq += hi == prefix;
-        }
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, sh.part, tot);
-        uint32_t eq_rank = eq_base + (ex & 0xFFFFu);
-        uint32_t pos = gt_base + (ex >> 16) + min(eq_rank, need);
+    auto keys = [&](int s, uint32_t* u) {
         const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
-#pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i) {
-            if (u[i] == 0u) continue;
-            bool sel;
-            if (take_all) sel = true;
-            else {
-                const uint32_t hi = u[i] & mask;
-                sel = hi > prefix;
-                if (hi == prefix) { sel = eq_rank < need; eq_rank++; }
-            }
-            if (sel) orow[pos++] = col_id(pool, c0 + i);
-        }
-        gt_base += tot >> 16;
-        eq_base += tot & 0xFFFFu;
-    }
-    out_base = gt_base + min(eq_base, need);
-    for (int j = (int)out_base + threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = -1;
-    if (threadIdx.x == 0) a.out_count[row] = (int32_t)out_base;
+        if (a.keys_by_id) load_pool_keys(krow, pool, ncols, c0, u);
+        else load_cols(krow, ncols, c0, u);
+    };
+    auto emit = [&](int col, uint32_t slot) { orow[slot] = col_id(pool, col); };
+    const uint32_t n = select_row(sh, ncols, a.k, keys, emit);
+    for (int j = (int)n + threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = -1;
+    if (threadIdx.x == 0) a.out_count[row] = (int32_t)n;
+}
+
+// The Full layer's selection for one row: the pool (top n_pool blocks by
+// block maximum) and then the top k positions among the pool's scores.
+__global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs a) {
+    __shared__ TkShared sh;
+    const int row = blockIdx.x;
+    const int nv = max(0, min(a.n_vis[row], a.max_vis));
+    const int nb = (nv + 7) >> 3;
+    const float* brow = a.block_max + (int64_t)row * a.block_max_stride;
+    const float* srow = a.scores + (int64_t)row * a.scores_stride;
+    int32_t* prow = a.pool + (int64_t)row * a.pool_stride;
+    int32_t* irow = a.idx + (int64_t)row * a.idx_stride;
+
+    // ---- blocks
+    auto bkeys = [&](int s, uint32_t* u) { load_cols(brow, nb, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
+    auto bemit = [&](int col, uint32_t slot) { sh.pool[slot] = col; prow[slot] = col; };
+    const uint32_t np = select_row(sh, nb, a.n_pool, bkeys, bemit);
+    for (int j = (int)np + threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = -1;
+    if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
+    __syncthreads();                                  // the pool is complete in LDS
+
+    // ---- positions: column c is position 8 * pool[c/8] + c%8 (-inf past n_vis)
+    const int ncols = 8 * (int)np;
+    auto pkeys = [&](int s, uint32_t* u) { load_pool_keys(srow, sh.pool, ncols, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
+    auto pemit = [&](int col, uint32_t slot) { irow[slot] = 8 * sh.pool[col >> 3] + (col & 7); };
+    const uint32_t ni = select_row(sh, ncols, a.k, pkeys, pemit);
+    for (int j = (int)ni + threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = -1;
+    if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.n_rows), dim3(TK_THREADS), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows), dim3(TK_THREADS), 0, st, a);
     return hipGetLastError();
 }
 

@@ -5,10 +5,11 @@ library's own generator and packer, then strings the five entry points
 together as one step of the hot path:
 
   Full layer    csa2_index_score (full scan + block max)
-                -> csa2_select_topk (2,048 blocks) -> csa2_select_topk (512 positions)
-                -> csa2_sparse_attn -> csa2_swa_merge
+                -> csa2_select_full (2,048 blocks, then 512 positions among them;
+                   or the two csa2_select_topk calls)
+                -> csa2_sparse_swa_attn (or csa2_sparse_attn -> csa2_swa_merge)
   Reindex layer csa2_index_score (pool) -> csa2_select_topk (512)
-                -> csa2_sparse_attn -> csa2_swa_merge
+                -> csa2_sparse_swa_attn (or csa2_sparse_attn -> csa2_swa_merge)
 
 ('DeepSeek V4.1 Flash architecture analysis' page, hierarchical sparse
 indexer: the first Full layer scores every position and builds the pool that
@@ -25,7 +26,7 @@ import synth
 from synth.configs import Config
 
 from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_index_score,
-               csa2_pack_kv, csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge,
+               csa2_pack_kv, csa2_select_full, csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge,
                csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform, make_kv, make_rows)
 
 GEN_CHUNK = 1 << 20   # entries generated per chunk
@@ -83,9 +84,11 @@ class Layer:
 class Workload:
     """All device buffers of one configuration; ``step()`` runs the hot path."""
 
-    def __init__(self, cfg: Config, copies: int = 1, dev="cuda", separate: bool = False):
+    def __init__(self, cfg: Config, copies: int = 1, dev="cuda", separate: bool = False,
+                 two_call_select: bool = False):
         self.cfg = cfg
         self.separate = separate
+        self.two_call_select = two_call_select
         self.dev = dev
         L = cfg.lens
         base = cfg.req_base
@@ -196,7 +199,7 @@ class Workload:
             csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.n_vis,
                              max_cols=self.max_vis, stream=stream)
             m(marks, "select_positions", 1)
-        else:
+        elif self.two_call_select:
             m(marks, "select_blocks", 0)
             csa2_select_topk(self.block_max, 2048, self.pool, self.pool_count, n_cols=self.n_vis, cols_div=8,
                              max_cols=self.nv8 // 8, stream=stream)
@@ -205,6 +208,11 @@ class Workload:
             csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.pool_count, cols_mul=8,
                              pool_blocks=self.pool, keys_by_id=True, max_cols=16384, stream=stream)
             m(marks, "select_positions", 1)
+        else:
+            m(marks, "select", 0)
+            csa2_select_full(self.block_max, self.scores, self.n_vis, self.max_vis, self.pool, self.pool_count,
+                             layer.idx, layer.idx_count, stream=stream)
+            m(marks, "select", 1)
         self._attend(layer, kv, stream, marks)
 
     def run_reindex(self, layer: "Layer", kv, stream=None, marks=None):

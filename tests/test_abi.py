@@ -63,6 +63,27 @@ def test_topk_rejects_shapes():
     assert L.csa2_select_topk(None, 0, None, 1, 1, None, 0, 0, 0, 0, 10, None, 0, None, None) == 0
 
 
+def test_select_full_rejects():
+    L = lib.lib()
+    f = L.csa2_select_full
+    ok = (256, 16, 256, 128, 256, 4, 100, 2048, 512, 256, 2048, 256, 256, 512, 256, None)   # never launched
+    bad = list(ok); bad[7] = 2049                   # pool too large
+    assert f(*bad) == 3
+    bad = list(ok); bad[8] = 0                      # k
+    assert f(*bad) == 3
+    bad = list(ok); bad[0] = None                   # block_max
+    assert f(*bad) == 1
+    bad = list(ok); bad[3] = 100                    # scores_stride < roundup(max_vis, 8)
+    assert f(*bad) == 2
+    bad = list(ok); bad[1] = 12                     # block_max_stride < ceil(max_vis / 8)
+    assert f(*bad) == 2
+    bad = list(ok); bad[2] = 260                    # scores not 16-byte aligned
+    assert f(*bad) == 4
+    bad = list(ok); bad[13] = 100                   # idx_stride < k
+    assert f(*bad) == 2
+    assert f(None, 0, None, 0, None, 0, 0, 2048, 512, None, 0, None, None, 0, None, None) == 0   # no rows
+
+
 def test_pack_rejects():
     L = lib.lib()
     assert L.csa2_pack_kv(7, 256, 0, 4, 512, 256, 256, None, None) == 5

@@ -60,8 +60,10 @@ def test_tiny_full_decode(tiny):
     check_full_row(tiny, 0)
 
 
-def test_tiny_full_decode_two_call_attention():
-    wl = Workload(configs.tiny_full_decode(), separate=True)
+def test_tiny_full_decode_two_call_forms():
+    """The two-call selection (blocks, then positions) and the two-call
+    attention (sparse branch, then window merge) give the same results."""
+    wl = Workload(configs.tiny_full_decode(), separate=True, two_call_select=True)
     wl.step()
     torch.cuda.synchronize()
     check_full_row(wl, 0)

@@ -270,6 +270,46 @@ def test_topk_block_counts_and_pool_ids():
         assert int(icnt2[r]) == len(ref2) and np.array_equal(idx2[r, :len(ref2)].cpu().numpy(), ref2)
 
 
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_full_exact(ties):
+    """The fused Full-layer selection equals the oracle's pool + top-512 and
+    the two-call form, on rows with no entry, a partial block, fewer than
+    2,048 blocks and more than 16,384 blocks (two sweeps)."""
+    n_vis = np.array([0, 13, 5003, 16384 * 8 + 21], np.int32)
+    n_rows, n = len(n_vis), int(n_vis.max())
+    nv8 = (n + 7) // 8 * 8
+    sc = np.full((n_rows, nv8), -np.inf, np.float32)
+    for r in range(n_rows):
+        m = int(n_vis[r])
+        v = RNG.standard_normal(m).astype(np.float32) * 10
+        if ties:
+            v = np.round(v * 2) / 2                     # many equal scores
+        sc[r, :m] = v
+    bm = np.stack([np.concatenate([oracle.block_max(sc[r, :n_vis[r]]),
+                                   np.full(nv8 // 8 - (int(n_vis[r]) + 7) // 8, -np.inf, np.float32)])
+                   for r in range(n_rows)]).astype(np.float32)
+    S, Bm, nv = T(sc), T(bm), T(n_vis)
+    pool = torch.full((n_rows, 2048), -7, dtype=torch.int32, device=DEV)
+    pcnt = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
+    idx = torch.full((n_rows, 512), -7, dtype=torch.int32, device=DEV)
+    icnt = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
+    lib.csa2_select_full(Bm, S, nv, n, pool, pcnt, idx, icnt)
+    pool2 = torch.empty_like(pool); pcnt2 = torch.empty_like(pcnt)
+    idx2 = torch.empty_like(idx); icnt2 = torch.empty_like(icnt)
+    lib.csa2_select_topk(Bm, 2048, pool2, pcnt2, n_cols=nv, cols_div=8, max_cols=nv8 // 8)
+    lib.csa2_select_topk(S, 512, idx2, icnt2, n_cols=pcnt2, cols_mul=8, pool_blocks=pool2, keys_by_id=True,
+                         max_cols=16384)
+    torch.cuda.synchronize()
+    for r in range(n_rows):
+        p_ref, i_ref = oracle.full_select(sc[r, :n_vis[r]])
+        assert int(pcnt[r]) == len(p_ref) and np.array_equal(pool[r, :len(p_ref)].cpu().numpy(), p_ref)
+        assert np.all(pool[r, len(p_ref):].cpu().numpy() == -1)
+        assert int(icnt[r]) == len(i_ref) and np.array_equal(idx[r, :len(i_ref)].cpu().numpy(), i_ref)
+        assert np.all(idx[r, len(i_ref):].cpu().numpy() == -1)
+    assert torch.equal(pool, pool2) and torch.equal(pcnt, pcnt2)
+    assert torch.equal(idx, idx2) and torch.equal(icnt, icnt2)
+
+
 # ---------------------------------------------------------------- whole Full-layer path, degenerate rows
 def test_full_path_empty_and_short_rows():
     """Rows with no visible entry, fewer than 8, exactly 8, fewer than 512
