@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum {
     CSA2_OK = 0,
@@ -209,14 +209,19 @@ csa2_status csa2_select_full(const float* block_max, int64_t block_max_stride,
  * (<= 128) of the planes swa_codes [swa_slots][512] / swa_scales [.][32].
  * q [n_rows][n_heads][512] bf16 (fp32 is rounded to bf16 on the way in);
  * n_heads 16, 32, 48, 64 or 128; outputs fp32.  q, o/out 16-B aligned.
- * No device memory beyond the arguments is used, and a row's result does not
- * depend on the other rows of the call. */
+ * workspace: NULL, or csa2_attn_workspace_size(n_rows, n_heads) bytes,
+ * 256-B aligned, no initialisation, not kept between calls.  With it, a call
+ * with few rows spreads each row's entry list over several workgroups and
+ * joins their partial results in a second pass; without it (or when the size
+ * is 0) every row and group of 16 heads is one workgroup. */
+size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads);
 
 /* Selected entries only: o_partial / lse of the sparse branch. */
 csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows,
                              const void* q, csa2_dtype q_dtype, int32_t n_heads,
                              const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
-                             float softmax_scale, float* o_partial, float* lse, void* stream);
+                             float softmax_scale, float* o_partial, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Window branch merged with a sparse-branch result through its log-sum-exp:
  * out = joint softmax over {the entries behind (o_partial, lse)} + {window}
@@ -226,7 +231,7 @@ csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, 
                            const int64_t* swa_first, const int32_t* swa_count, int32_t n_rows,
                            const void* q, csa2_dtype q_dtype, int32_t n_heads, float softmax_scale,
                            const float* sink, const float* o_partial, const float* lse,
-                           float* out, void* stream);
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Both branches in one pass (the decode step's form): out = joint softmax
  * over selected + window entries (+ sink); lse (may be NULL) of that joint
@@ -236,7 +241,8 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
                                  const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
                                  const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
                                  const int64_t* swa_first, const int32_t* swa_count, const float* sink,
-                                 float softmax_scale, float* out, float* lse, void* stream);
+                                 float softmax_scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- synthetic inputs
  * Counter-based generator for seeded synthetic inputs (SplitMix64; Steele,

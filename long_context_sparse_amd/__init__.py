@@ -46,7 +46,7 @@ class Rows(ctypes.Structure):
 _lib = None
 EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
-    "csa2_select_topk", "csa2_select_full", "csa2_sparse_attn", "csa2_swa_merge",
+    "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
     "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost",
 )
 
@@ -69,16 +69,18 @@ def lib():
                                    P, i64, P, P, i64, P, i64, P]
     L.csa2_select_topk.argtypes = [P, i64, P, i32, i32, P, i64, i32, i32, i32, i32, P, i64, P, P]
     L.csa2_select_full.argtypes = [P, i64, P, i64, P, i32, i32, i32, i32, P, i64, P, P, i64, P, P]
+    L.csa2_attn_workspace_size.restype = ctypes.c_size_t
+    L.csa2_attn_workspace_size.argtypes = [i32, i32]
     L.csa2_sparse_attn.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P, i64, P,
-                                   f32, P, P, P]
-    L.csa2_swa_merge.argtypes = [P, P, i64, P, P, i32, P, ctypes.c_int, i32, f32, P, P, P, P, P]
+                                   f32, P, P, P, ctypes.c_size_t, P]
+    L.csa2_swa_merge.argtypes = [P, P, i64, P, P, i32, P, ctypes.c_int, i32, f32, P, P, P, P, P, ctypes.c_size_t, P]
     L.csa2_sparse_swa_attn.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P, i64, P,
-                                       P, P, i64, P, P, P, f32, P, P, P]
+                                       P, P, i64, P, P, P, f32, P, P, P, ctypes.c_size_t, P]
     L.csa2_synth_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, ctypes.c_int, P, P]
     L.csa2_synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, P, P]
     L.csa2_synth_boost.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, i32, P, P]
     for name in EXPORTS:
-        if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error"):
+        if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_attn_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -179,30 +181,39 @@ def csa2_select_full(block_max, scores, n_vis, max_vis, pool, pool_count, idx, i
         _ptr(idx_count), _stream(stream)))
 
 
-def csa2_sparse_attn(kv, rows, q, idx, idx_count, softmax_scale, o_partial, lse, stream=None):
+def csa2_attn_workspace_size(n_rows, n_heads) -> int:
+    return int(lib().csa2_attn_workspace_size(int(n_rows), int(n_heads)))
+
+
+def _ws(workspace):
+    return (None, 0) if workspace is None else (_ptr(workspace), int(workspace.numel() * workspace.element_size()))
+
+
+def csa2_sparse_attn(kv, rows, q, idx, idx_count, softmax_scale, o_partial, lse, workspace=None, stream=None):
     H = int(q.shape[1])
     _check("csa2_sparse_attn", lib().csa2_sparse_attn(
         ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), _rstride(idx),
-        _ptr(idx_count), float(softmax_scale), _ptr(o_partial), _ptr(lse), _stream(stream)))
+        _ptr(idx_count), float(softmax_scale), _ptr(o_partial), _ptr(lse), *_ws(workspace),
+        _stream(stream)))
 
 
 def csa2_swa_merge(swa_codes, swa_scales, swa_first, swa_count, q, softmax_scale, out, sink=None,
-                   o_partial=None, lse=None, stream=None):
+                   o_partial=None, lse=None, workspace=None, stream=None):
     n_rows, H = int(q.shape[0]), int(q.shape[1])
     _check("csa2_swa_merge", lib().csa2_swa_merge(
         _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first), _ptr(swa_count), n_rows,
         _ptr(q), _dtype(q), H, float(softmax_scale), _ptr(sink), _ptr(o_partial), _ptr(lse), _ptr(out),
-        _stream(stream)))
+        *_ws(workspace), _stream(stream)))
 
 
 def csa2_sparse_swa_attn(kv, rows, q, idx, idx_count, swa_codes, swa_scales, swa_first, swa_count, softmax_scale,
-                         out, sink=None, lse=None, stream=None):
+                         out, sink=None, lse=None, workspace=None, stream=None):
     H = int(q.shape[1])
     _check("csa2_sparse_swa_attn", lib().csa2_sparse_swa_attn(
         ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), _rstride(idx),
         _ptr(idx_count), _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first),
         _ptr(swa_count), _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse),
-        _stream(stream)))
+        *_ws(workspace), _stream(stream)))
 
 
 def csa2_synth_normal(seed, tensor_id, first, out, stream=None):

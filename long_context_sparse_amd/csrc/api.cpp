@@ -196,13 +196,19 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_
     return hip_status(csa2::launch_topk(a, (hipStream_t)stream), "csa2_select_topk launch");
 }
 
+size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads) {
+    if (n_rows <= 0 || n_heads < 16 || n_heads > 128) return 0;
+    return csa2::attn_workspace_bytes(n_rows, n_heads, csa2::attn_splits(n_rows, n_heads));
+}
+
 static csa2_status check_heads(int32_t h) {
     if (!(h == 16 || h == 32 || h == 48 || h == 64 || h == 128))
         return fail(CSA2_ERR_UNSUPPORTED, "n_heads must be 16, 32, 48, 64 or 128 (got %d)", h);
     return CSA2_OK;
 }
 
-static csa2_status check_common(int32_t n_rows, const void* q, csa2_dtype q_dtype, int32_t n_heads, float scale) {
+static csa2_status check_common(int32_t n_rows, const void* q, csa2_dtype q_dtype, int32_t n_heads, float scale,
+                                const void* workspace) {
     csa2_status s = check_heads(n_heads);
     if (s != CSA2_OK) return s;
     if (n_rows < 0 || n_rows > 65535) return fail(CSA2_ERR_RANGE, "n_rows out of range");
@@ -211,6 +217,7 @@ static csa2_status check_common(int32_t n_rows, const void* q, csa2_dtype q_dtyp
     if (!q) return fail(CSA2_ERR_NULL, "q is NULL");
     if (!aligned(q, 16)) return fail(CSA2_ERR_ALIGN, "q must be 16-byte aligned");
     if (!(scale > 0.0f) || scale > 1e30f) return fail(CSA2_ERR_RANGE, "softmax_scale must be positive and finite");
+    if (workspace && !aligned(workspace, 256)) return fail(CSA2_ERR_ALIGN, "workspace must be 256-byte aligned");
     return CSA2_OK;
 }
 
@@ -222,13 +229,15 @@ static csa2_status check_swa(const uint8_t* codes, const uint8_t* scales, int64_
     return CSA2_OK;
 }
 
-static void fill_q(csa2::AttnArgs& a, const void* q, csa2_dtype q_dtype, int32_t n_heads, int32_t n_rows, float scale) {
+static void fill_q(csa2::AttnArgs& a, const void* q, csa2_dtype q_dtype, int32_t n_heads, int32_t n_rows, float scale,
+                   void* workspace) {
     memset(&a, 0, sizeof a);
     a.q = q;
     a.q_bf16 = q_dtype == CSA2_BF16;
     a.n_heads = n_heads;
     a.n_rows = n_rows;
     a.scale = scale;
+    a.ws = (float*)workspace;
 }
 
 csa2_status csa2_select_full(const float* block_max, int64_t block_max_stride, const float* scores,
@@ -271,32 +280,34 @@ csa2_status csa2_select_full(const float* block_max, int64_t block_max_stride, c
 
 csa2_status csa2_sparse_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
                              int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
-                             float softmax_scale, float* o_partial, float* lse, void* stream) {
+                             float softmax_scale, float* o_partial, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     csa2::KvView v;
     csa2_status s = make_view(kv, true, false, &v);
     if (s != CSA2_OK) return s;
     if ((s = check_rows(rows)) != CSA2_OK) return s;
-    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale)) != CSA2_OK) return s;
+    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale, workspace)) != CSA2_OK) return s;
     if (rows->n_rows == 0) return CSA2_OK;
     if (!idx || !idx_count || !o_partial || !lse) return fail(CSA2_ERR_NULL, "idx / idx_count / o_partial / lse is NULL");
     if (!aligned(o_partial, 16)) return fail(CSA2_ERR_ALIGN, "o_partial must be 16-byte aligned");
     if (idx_stride < 1) return fail(CSA2_ERR_SHAPE, "idx_stride must be >= 1");
     csa2::AttnArgs a;
-    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale);
+    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
     a.req = rows->req;
     a.idx = idx;
     a.idx_stride = idx_stride;
     a.idx_count = idx_count;
     a.out = o_partial;
     a.lse_out = lse;
-    return hip_status(csa2::launch_attn(v, a, (hipStream_t)stream), "csa2_sparse_attn launch");
+    return hip_status(csa2::launch_attn(v, a, workspace_bytes, (hipStream_t)stream), "csa2_sparse_attn launch");
 }
 
 csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
                            const int64_t* swa_first, const int32_t* swa_count, int32_t n_rows, const void* q,
                            csa2_dtype q_dtype, int32_t n_heads, float softmax_scale, const float* sink,
-                           const float* o_partial, const float* lse, float* out, void* stream) {
-    csa2_status s = check_common(n_rows, q, q_dtype, n_heads, softmax_scale);
+                           const float* o_partial, const float* lse, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    csa2_status s = check_common(n_rows, q, q_dtype, n_heads, softmax_scale, workspace);
     if (s != CSA2_OK) return s;
     if (n_rows == 0) return CSA2_OK;
     if ((s = check_swa(swa_codes, swa_scales, swa_slots, swa_first, swa_count)) != CSA2_OK) return s;
@@ -304,7 +315,7 @@ csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, 
     if ((o_partial == nullptr) != (lse == nullptr)) return fail(CSA2_ERR_NULL, "o_partial and lse must be both set or both NULL");
     if (!aligned(out, 16) || (o_partial && !aligned(o_partial, 16))) return fail(CSA2_ERR_ALIGN, "out and o_partial must be 16-byte aligned");
     csa2::AttnArgs a;
-    fill_q(a, q, q_dtype, n_heads, n_rows, softmax_scale);
+    fill_q(a, q, q_dtype, n_heads, n_rows, softmax_scale, workspace);
     a.swa_codes = swa_codes;
     a.swa_scales = swa_scales;
     a.swa_first = swa_first;
@@ -315,26 +326,27 @@ csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, 
     a.out = out;
     csa2::KvView none;
     memset(&none, 0, sizeof none);
-    return hip_status(csa2::launch_attn(none, a, (hipStream_t)stream), "csa2_swa_merge launch");
+    return hip_status(csa2::launch_attn(none, a, workspace_bytes, (hipStream_t)stream), "csa2_swa_merge launch");
 }
 
 csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
                                  int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
                                  const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
                                  const int64_t* swa_first, const int32_t* swa_count, const float* sink,
-                                 float softmax_scale, float* out, float* lse, void* stream) {
+                                 float softmax_scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
     csa2::KvView v;
     csa2_status s = make_view(kv, true, false, &v);
     if (s != CSA2_OK) return s;
     if ((s = check_rows(rows)) != CSA2_OK) return s;
-    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale)) != CSA2_OK) return s;
+    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale, workspace)) != CSA2_OK) return s;
     if (rows->n_rows == 0) return CSA2_OK;
     if ((s = check_swa(swa_codes, swa_scales, swa_slots, swa_first, swa_count)) != CSA2_OK) return s;
     if (!idx || !idx_count || !out) return fail(CSA2_ERR_NULL, "idx / idx_count / out is NULL");
     if (!aligned(out, 16)) return fail(CSA2_ERR_ALIGN, "out must be 16-byte aligned");
     if (idx_stride < 1) return fail(CSA2_ERR_SHAPE, "idx_stride must be >= 1");
     csa2::AttnArgs a;
-    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale);
+    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
     a.req = rows->req;
     a.idx = idx;
     a.idx_stride = idx_stride;
@@ -346,7 +358,7 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const
     a.sink = sink;
     a.out = out;
     a.lse_out = lse;
-    return hip_status(csa2::launch_attn(v, a, (hipStream_t)stream), "csa2_sparse_swa_attn launch");
+    return hip_status(csa2::launch_attn(v, a, workspace_bytes, (hipStream_t)stream), "csa2_sparse_swa_attn launch");
 }
 
 csa2_status csa2_synth_normal(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n, csa2_dtype out_dtype,

@@ -49,6 +49,7 @@ constexpr int AT_WAVES = 8;
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int V_LD = 512 + 16;          // fp16 elements per entry row of V in LDS (32 B pad spreads the banks)
 constexpr int AT_MAX_SEL = 512;
+constexpr int AT_MAX_SPLITS = 8;        // workgroups sharing one (row, head group)
 
 struct AttnSmem {
     _Float16 v[2][AT_ENT * V_LD];       // the chunk's dequantised entries [entry][channel], double-buffered
@@ -260,9 +261,11 @@ template <bool QBF16>
 __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a) {
     extern __shared__ __align__(16) uint8_t at_smem[];
     AttnSmem& sm = *(AttnSmem*)at_smem;
-    const int G = a.n_heads >> 4;
-    const int id = xcd_order(blockIdx.x, a.n_rows * G);
-    const int row = id / G, h0 = 16 * (id - row * G);
+    const int G = a.n_heads >> 4, S = a.n_splits;
+    const int id = xcd_order(blockIdx.x, a.n_rows * G * S);   // a (row, group)'s splits are consecutive
+    const int row = id / (G * S);
+    const int hg = (id - row * G * S) / S, split = id - (row * G + hg) * S;
+    const int h0 = 16 * hg;
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int n = l & 15, g = l >> 4;
     const int et = wave & 3, kh = wave >> 2;
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int nsw = a.swa_codes ? min(max(a.swa_count[row], 0), 128) : 0;
     const int csp = (nsp + AT_ENT - 1) / AT_ENT;
     const int ctot = csp + (nsw + AT_ENT - 1) / AT_ENT;
+    const int cb = split * ctot / S, ce = (split + 1) * ctot / S;   // this split's chunks
     const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
     // cache slots of the selected entries; the query and its per-head scale;
@@ -324,9 +328,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // (c + 1) & 1).  Chunk c's bytes sit in raw[c & 1]; right after they are
     // dequantised the loads of chunk c + 2 go into the same registers.
     RawChunk raw0, raw1;
-    if (ctot > 0) {
-        load_raw(kv, a, sm, 0, csp, nsp, nsw, swa0, et, kh, n, g, raw0);
-        load_raw(kv, a, sm, min(1, ctot - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw1);
+    if (ce > cb) {
+        load_raw(kv, a, sm, cb, csp, nsp, nsw, swa0, et, kh, n, g, raw0);
+        load_raw(kv, a, sm, min(cb + 1, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw1);
     }
     f32x4 oacc[4];
 #pragma unroll
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         else dequant_main(raw, cvt_sel, vb + v_lane, kop);
         // always issued (the last two re-read the final chunk, unused): a load
         // under a branch makes the compiler wait for it at the join
-        load_raw(kv, a, sm, min(c + 2, ctot - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw);
+        load_raw(kv, a, sm, min(c + 2, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw);
         f32x4 sc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], qh[ks], sc, 0, 0, 0);
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // probabilities of chunk c and O^T += V^T P^T over channels 64*wave .. +63
     auto stage_b = [&](const int c) __attribute__((always_inline)) {
         const int buf = c & 1;
-        const int nent = min(c < csp ? nsp - 64 * c : nsw - 64 * (c - csp), AT_ENT);   // <= 0 past the end
+        const int nent = c >= ce ? 0 : min(c < csp ? nsp - 64 * c : nsw - 64 * (c - csp), AT_ENT);
         f32x4 z[4];                                      // z[t][i]: entry 16t + 4g + i, head n
 #pragma unroll
         for (int t = 0; t < 4; ++t) z[t] = sm.sp[buf][t][l] + sm.sp[buf][t + 4][l];
@@ -403,27 +407,45 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // compiler can count the loads in flight; chunks past the end are
     // processed as empty (their scores are all masked: no contribution).
     auto step = [&](const int c, RawChunk& next_raw) __attribute__((always_inline)) {
-        const int ca = min(c + 1, ctot - 1) < csp ? 0 : 1;
+        const int ca = min(c + 1, ce - 1) < csp ? 0 : 1;
         if (ca == 0) stage_a(SEL, c + 1, next_raw);
         else stage_a(WIN, c + 1, next_raw);
         stage_b(c);
         __syncthreads();
     };
 
-    if (ctot > 0) {
-        if (csp > 0) stage_a(SEL, 0, raw0);
-        else stage_a(WIN, 0, raw0);
+    if (ce > cb) {
+        if (cb < csp) stage_a(SEL, cb, raw0);
+        else stage_a(WIN, cb, raw0);
         __syncthreads();
-        for (int c = 0; c < ctot; c += 2) {
+        for (int c = cb; c < ce; c += 2) {
             step(c, raw1);
             step(c + 1, raw0);
         }
     }
 
+    const int h = h0 + n;
+    if (S > 1) {
+        // ---- one split of several: its normalised partial (fp32, without the
+        // 2^tw) and its base-2 max and sum; attn_merge_kernel joins them
+        const size_t ps = ((size_t)row * a.n_heads + h) * S + split;
+        float* wsO = a.ws;
+        float* wsM = wsO + (size_t)a.n_rows * a.n_heads * S * 512;
+        float* wsL = wsM + (size_t)a.n_rows * a.n_heads * S;
+        const float inv = l_run > 0.0f ? ldexpf(1.0f / l_run, -tw) : 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int ch = 64 * wave + 16 * ct + 4 * g;
+            *(float4*)(wsO + ps * 512 + ch) = make_float4(oacc[ct][0] * inv, oacc[ct][1] * inv,
+                                                          oacc[ct][2] * inv, oacc[ct][3] * inv);
+        }
+        if (wave == 0 && g == 0) { wsM[ps] = m_run; wsL[ps] = l_run; }
+        return;
+    }
+
     // ---- epilogue: join an external partial (o_in, lse_in) and the sink; write
     // O^T[64*wave + 16ct + 4g + i][head h0 + n].  Natural-log terms become
     // base 2 with log2(e); oacc carries the entries' 2^tw.
-    const int h = h0 + n;
     const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * a.n_heads + h] * LOG2E : -INFINITY;
     const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
     const float M = fmaxf(fmaxf(m_run, lse_p), sk);
@@ -450,6 +472,70 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         a.lse_out[(int64_t)row * a.n_heads + h] = (M == -INFINITY || den == 0.0f) ? -INFINITY : (M + log2f(den)) * LN2;
 }
 
+// Joins the splits of every (row, head): out = (sum_s 2^(m_s - M) l_s o_s
+// + e^(lse_in - M') o_in) / (sum_s 2^(m_s - M) l_s + e^(lse_in) + e^(sink)),
+// all in base 2.  One thread per (row, head, 4 channels); every load is
+// issued before any is used.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
+    const int S = a.n_splits;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)a.n_rows * a.n_heads * 128) return;
+    const int64_t rh = t >> 7;                        // row * n_heads + head
+    const int c4 = (int)(t & 127) * 4;
+    const int h = (int)(rh % a.n_heads);
+    const float* wsO = a.ws;
+    const float* wsM = wsO + (size_t)a.n_rows * a.n_heads * S * 512;
+    const float* wsL = wsM + (size_t)a.n_rows * a.n_heads * S;
+    float m[AT_MAX_SPLITS], lw[AT_MAX_SPLITS];
+    float4 o[AT_MAX_SPLITS];
+#pragma unroll
+    for (int s = 0; s < AT_MAX_SPLITS; ++s) {
+        const int sc = s < S ? s : S - 1;             // loads stay unconditional
+        m[s] = wsM[rh * S + sc];
+        lw[s] = wsL[rh * S + sc];
+        o[s] = *(const float4*)(wsO + (rh * S + sc) * 512 + c4);
+    }
+    const float lse_p = a.lse_in ? a.lse_in[rh] * LOG2E : -INFINITY;
+    const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
+    float M = fmaxf(lse_p, sk);
+#pragma unroll
+    for (int s = 0; s < AT_MAX_SPLITS; ++s) if (s < S) M = fmaxf(M, m[s]);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int s = 0; s < AT_MAX_SPLITS; ++s) {
+            if (s >= S || m[s] == -INFINITY) continue;
+            const float w = __builtin_amdgcn_exp2f(m[s] - M) * lw[s];
+            den += w;
+            acc.x += w * o[s].x; acc.y += w * o[s].y; acc.z += w * o[s].z; acc.w += w * o[s].w;
+        }
+        if (lse_p != -INFINITY) {
+            const float w = __builtin_amdgcn_exp2f(lse_p - M);
+            const float4 pin = *(const float4*)(a.o_in + rh * 512 + c4);
+            den += w;
+            acc.x += w * pin.x; acc.y += w * pin.y; acc.z += w * pin.z; acc.w += w * pin.w;
+        }
+        if (sk != -INFINITY) den += __builtin_amdgcn_exp2f(sk - M);
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    *(float4*)(a.out + rh * 512 + c4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (a.lse_out && c4 == 0) a.lse_out[rh] = den > 0.0f ? (M + log2f(den)) * LN2 : -INFINITY;
+}
+
+int attn_splits(int n_rows, int n_heads) {
+    const int groups = n_rows * (n_heads >> 4);
+    if (groups <= 0) return 1;
+    const int s = 256 / groups;                       // fill the 256 CUs, one workgroup each
+    return s < 2 ? 1 : (s > AT_MAX_SPLITS ? AT_MAX_SPLITS : s);
+}
+
+size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits) {
+    if (n_splits <= 1) return 0;
+    return (size_t)n_rows * n_heads * n_splits * (512 + 2) * sizeof(float);
+}
+
 static bool g_attr_set = false;
 
 static hipError_t set_lds_attrs() {
@@ -461,12 +547,18 @@ static hipError_t set_lds_attrs() {
     return hipSuccess;
 }
 
-hipError_t launch_attn(const KvView& kv, const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn(const KvView& kv, const AttnArgs& a_in, size_t ws_bytes, hipStream_t st) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)a.n_rows * (unsigned)(a.n_heads >> 4);
+    AttnArgs a = a_in;
+    a.n_splits = attn_splits(a.n_rows, a.n_heads);
+    if (!a.ws || ws_bytes < attn_workspace_bytes(a.n_rows, a.n_heads, a.n_splits)) a.n_splits = 1;
+    const unsigned blocks = (unsigned)a.n_rows * (unsigned)(a.n_heads >> 4) * (unsigned)a.n_splits;
     if (a.q_bf16) hipLaunchKernelGGL(attn_kernel<true>, dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
     else hipLaunchKernelGGL(attn_kernel<false>, dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    if ((e = hipGetLastError()) != hipSuccess || a.n_splits == 1) return e;
+    const int64_t threads = (int64_t)a.n_rows * a.n_heads * 128;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

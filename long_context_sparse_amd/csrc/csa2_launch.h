@@ -85,8 +85,12 @@ struct AttnArgs {
     const float* lse_in;
     float* out;
     float* lse_out;
+    float* ws;                   // split partials (NULL: one workgroup per row and head group)
+    int n_splits;                // set by launch_attn
 };
-hipError_t launch_attn(const KvView& kv, const AttnArgs& a, hipStream_t st);
+int attn_splits(int n_rows, int n_heads);
+size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits);
+hipError_t launch_attn(const KvView& kv, const AttnArgs& a, size_t ws_bytes, hipStream_t st);
 
 hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,
                                void* out, hipStream_t st);

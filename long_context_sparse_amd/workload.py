@@ -26,7 +26,7 @@ import synth
 from synth.configs import Config
 
 from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_index_score,
-               csa2_pack_kv, csa2_select_full, csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge,
+               csa2_attn_workspace_size, csa2_pack_kv, csa2_select_full, csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge,
                csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform, make_kv, make_rows)
 
 GEN_CHUNK = 1 << 20   # entries generated per chunk
@@ -156,6 +156,8 @@ class Workload:
             self.pool = torch.empty((self.n_rows, 2048), dtype=torch.int32, device=dev)
             self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
             self.pool_scores = torch.empty((self.n_rows, 16384), dtype=torch.float32, device=dev)
+        ws = csa2_attn_workspace_size(self.n_rows, cfg.heads)
+        self.workspace = torch.empty(max(ws, 256) // 4, dtype=torch.float32, device=dev) if ws else None
         if mode == "reindex":
             pools = np.stack([synth.given_pool(cfg.seed, r, int(L[r]) // 8, 2048) for r in range(self.n_rows)])
             self.pool.copy_(torch.as_tensor(pools))
@@ -234,18 +236,18 @@ class Workload:
         if self.separate:
             m(marks, "sparse_attn", 0)
             csa2_sparse_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, self.sigma, layer.o_partial,
-                             layer.lse, stream=stream)
+                             layer.lse, workspace=self.workspace, stream=stream)
             m(marks, "sparse_attn", 1)
             m(marks, "swa_merge", 0)
             csa2_swa_merge(layer.swa_codes, layer.swa_scales, layer.swa_first, layer.swa_count, layer.q,
-                           self.sigma, layer.out, o_partial=layer.o_partial, lse=layer.lse,
+                           self.sigma, layer.out, o_partial=layer.o_partial, lse=layer.lse, workspace=self.workspace,
                            stream=stream)
             m(marks, "swa_merge", 1)
         else:
             m(marks, "attention", 0)
             csa2_sparse_swa_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, layer.swa_codes,
                                  layer.swa_scales, layer.swa_first, layer.swa_count, self.sigma, layer.out,
-                                 stream=stream)
+                                 workspace=self.workspace, stream=stream)
             m(marks, "attention", 1)
 
     def step(self, copy: int = 0, stream=None, marks=None):

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lib.EXPORTS)
-    assert L.csa2_abi_version() == 2
+    assert L.csa2_abi_version() == 3
 
 
 def _kv(**over):
@@ -121,17 +121,22 @@ def test_attn_rejects():
     B = ctypes.byref
     f = L.csa2_sparse_attn
     F = ctypes.c_float(0.04)
-    assert f(B(kv), B(rows), 256, 0, 40, 256, 512, 256, F, 256, 256, None) == 5          # heads
-    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(-1.0), 256, 256, None) == 3
-    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, F, None, 256, None) == 1          # o_partial
-    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, F, 260, 256, None) == 4           # alignment
-    assert f(B(_kv(main_codes=None)), B(rows), 256, 0, 64, 256, 512, 256, F, 256, 256, None) == 1
+    assert f(B(kv), B(rows), 256, 0, 40, 256, 512, 256, F, 256, 256, None, 0, None) == 5          # heads
+    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, ctypes.c_float(-1.0), 256, 256, None, 0, None) == 3
+    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, F, None, 256, None, 0, None) == 1          # o_partial
+    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, F, 260, 256, None, 0, None) == 4           # alignment
+    assert f(B(kv), B(rows), 256, 0, 64, 256, 512, 256, F, 256, 256, 300, 4096, None) == 4         # workspace
+    assert f(B(_kv(main_codes=None)), B(rows), 256, 0, 64, 256, 512, 256, F, 256, 256, None, 0, None) == 1
+    assert L.csa2_attn_workspace_size(2, 64) > 0 and L.csa2_attn_workspace_size(4096, 64) == 0
     g = L.csa2_swa_merge
-    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, F, None, 256, None, 256, None) == 1   # o_partial without lse
-    assert g(256, 256, 10, 256, 256, 2, 256, 0, 200, F, None, None, None, 256, None) == 5
-    assert g(264, 256, 10, 256, 256, 2, 256, 0, 64, F, None, None, None, 256, None) == 4
-    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, F, None, None, None, None, None) == 1  # out
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, F, None, 256, None, 256, None, 0, None) == 1   # o_partial, no lse
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 200, F, None, None, None, 256, None, 0, None) == 5
+    assert g(264, 256, 10, 256, 256, 2, 256, 0, 64, F, None, None, None, 256, None, 0, None) == 4
+    assert g(256, 256, 10, 256, 256, 2, 256, 0, 64, F, None, None, None, None, None, 0, None) == 1  # out
     h = L.csa2_sparse_swa_attn
-    assert h(B(kv), B(rows), 256, 0, 64, 256, 512, 256, None, 256, 10, 256, 256, None, F, 256, None, None) == 1
-    assert h(B(kv), B(rows), 256, 0, 64, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 260, None, None) == 4
-    assert h(B(kv), B(rows), 256, 0, 24, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 256, None, None) == 5
+    assert h(B(kv), B(rows), 256, 0, 64, 256, 512, 256, None, 256, 10, 256, 256, None, F, 256, None, None, 0,
+             None) == 1
+    assert h(B(kv), B(rows), 256, 0, 64, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 260, None, None, 0,
+             None) == 4
+    assert h(B(kv), B(rows), 256, 0, 24, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 256, None, None, 0,
+             None) == 5

@@ -387,18 +387,25 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
     first = T(np.arange(n_rows, dtype=np.int64) * 128)
     swc = T(np.asarray(swa_counts, np.int32))
     sk_d = None if sk is None else T(sk)
-    # two-call form
+    # two-call form, rows split over several workgroups when there are few
+    wsb = lib.csa2_attn_workspace_size(n_rows, H)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV) if wsb else None
     o_p = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
-    lib.csa2_sparse_attn(kv, rows, qd, idx_d, cnt_d, SIG, o_p, lse)
+    lib.csa2_sparse_attn(kv, rows, qd, idx_d, cnt_d, SIG, o_p, lse, workspace=ws)
     out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
-    lib.csa2_swa_merge(wc_d, wsc_d, first, swc, qd, SIG, out, sink=sk_d, o_partial=o_p, lse=lse)
-    # one-pass form
+    lib.csa2_swa_merge(wc_d, wsc_d, first, swc, qd, SIG, out, sink=sk_d, o_partial=o_p, lse=lse, workspace=ws)
+    # one-pass form, one workgroup per row and head group
     out2 = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse2 = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
     lib.csa2_sparse_swa_attn(kv, rows, qd, idx_d, cnt_d, wc_d, wsc_d, first, swc, SIG, out2, sink=sk_d, lse=lse2)
+    # one-pass form with the workspace
+    out3 = torch.empty((n_rows, H, 512), dtype=torch.float32, device=DEV)
+    lse3 = torch.empty((n_rows, H), dtype=torch.float32, device=DEV)
+    lib.csa2_sparse_swa_attn(kv, rows, qd, idx_d, cnt_d, wc_d, wsc_d, first, swc, SIG, out3, sink=sk_d, lse=lse3,
+                             workspace=ws)
     torch.cuda.synchronize()
-    O_p, L_p, Out, Out2, L2 = (t.cpu().numpy() for t in (o_p, lse, out, out2, lse2))
+    O_p, L_p, Out, Out2, L2, Out3, L3 = (t.cpu().numpy() for t in (o_p, lse, out, out2, lse2, out3, lse3))
     for r in (range(n_rows) if check_rows is None else check_rows):
         Kr = K[r * n_entries + idx[r, :counts[r]]]
         Wr = W[r * 128:r * 128 + swa_counts[r]]
@@ -410,11 +417,12 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
             assert np.all(np.isneginf(L_p[r])) and not O_p[r].any()
         fo, fl = oracle.attention(q[r], Kr, Wr, sink=sk, sigma=SIG)
         assert tolerance_ok(Out[r], fo), (r, np.abs(Out[r] - fo).max())
-        assert tolerance_ok(Out2[r], fo), (r, np.abs(Out2[r] - fo).max())
-        if counts[r] or swa_counts[r] or sink:
-            assert np.allclose(L2[r], fl, rtol=1e-5, atol=1e-5)
-        else:
-            assert np.all(np.isneginf(L2[r])) and not Out2[r].any()
+        for Oo, Ll in ((Out2, L2), (Out3, L3)):
+            assert tolerance_ok(Oo[r], fo), (r, np.abs(Oo[r] - fo).max())
+            if counts[r] or swa_counts[r] or sink:
+                assert np.allclose(Ll[r], fl, rtol=1e-5, atol=1e-5)
+            else:
+                assert np.all(np.isneginf(Ll[r])) and not Oo[r].any()
 
 
 @pytest.mark.parametrize("H", [16, 48, 64, 128])
@@ -455,8 +463,9 @@ def test_swa_only_and_alias():
     # out aliasing o_partial
     o_p = torch.zeros((n_rows, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.full((n_rows, H), -np.inf, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(lib.csa2_attn_workspace_size(n_rows, H), 256) // 4, dtype=torch.float32, device=DEV)
     lib.csa2_swa_merge(T(wc), T(wsc), T(np.array([0, 128], np.int64)), T(np.array([128, 37], np.int32)),
-                       bf16(q).to(DEV), SIG, o_p, o_partial=o_p, lse=lse)
+                       bf16(q).to(DEV), SIG, o_p, o_partial=o_p, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     for r, c in enumerate([128, 37]):
         ref, _ = oracle.attention(q[r], None, W[r * 128:r * 128 + c], sigma=SIG)
