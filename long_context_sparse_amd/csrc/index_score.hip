@@ -282,19 +282,20 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     const int nv = min(a.n_vis[row], a.max_vis);
     const int64_t pool_cap = a.pool_stride < 2048 ? a.pool_stride : 2048;
     const int ncols = POOL ? 8 * (int)min((int64_t)a.pool_count[row], pool_cap) : nv;
-    // Tiles of 16 columns are dealt out round-robin: tile T of the row goes to
-    // wave T % 4 of workgroup (T / 4) % Gx, so at any moment the resident waves
-    // of a row read one compact run of consecutive 1 KB tiles.
+    // A wave takes batches of IS_TILES consecutive 16-column tiles (64 keys,
+    // 4 KB of codes); batch b of wave w of workgroup x starts at column
+    // 64 ((b Gx + x) IS_WAVES + w), so the resident waves of a row read one
+    // compact run of consecutive batches.
     const int Gx = gridDim.x;
-    const int tile_first = blockIdx.x * IS_WAVES;      // first tile of wave 0 in round 0
-    if (16 * tile_first >= ncols) return;              // uniform over the workgroup
+    static_assert(IS_TILES == 4, "a batch is one tile per lane group");
+    if (64 * IS_WAVES * (int)blockIdx.x >= ncols) return;   // uniform over the workgroup
     const int req = a.req[row];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const int n = l & 15, lg = l >> 4;
     const int32_t* pool = POOL ? a.pool + (int64_t)row * a.pool_stride : nullptr;
-    const int wbase = 16 * (tile_first + wave);        // column of this wave's first tile
-    const int TSTRIDE = 16 * IS_WAVES * Gx;            // columns between a wave's consecutive tiles
-    const int BSTRIDE = IS_TILES * TSTRIDE;            // columns between a wave's batches
+    const int wbase = 64 * (IS_WAVES * (int)blockIdx.x + wave);   // first column of this wave's first batch
+    constexpr int TSTRIDE = 16;                        // columns between the tiles of a batch
+    const int BSTRIDE = 64 * IS_WAVES * Gx;            // columns between a wave's batches
 
     QRaw qraw;
     if (wave == 0) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads);      // issued before the keys
@@ -323,9 +324,15 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     const int nv8 = (nv + 7) & ~7;
     const bool writer = lg == 0;                       // the 4 row groups hold identical results
 
+    // One batch: tile t's MFMAs leave key 16t + n's score in every lane n of
+    // each row group; lane l keeps the one of tile l / 16, so the batch's 64
+    // scores leave in one coalesced 256-B store, and its 8 block maxima in one
+    // 32-B store.
     auto compute = [&](const KeyBatch& kb, int col_base) {
+        float vt[IS_TILES];
 #pragma unroll
         for (int t = 0; t < IS_TILES; ++t) {
+            vt[t] = -INFINITY;
             const int col0 = col_base + TSTRIDE * t;
             if (col0 >= ncols) break;
             const i32x8 Bk = {(int)kb.code[t].x, (int)kb.code[t].y, (int)kb.code[t].z, (int)kb.code[t].w, 0, 0, 0, 0};
@@ -337,10 +344,9 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[k], Bk, z, 4, 4, 0, sa[k], 0, sb);
             }
-            // An MFMA takes operands from all 64 lanes.  Only the writer lanes
-            // consume the scores in pool mode, and the compiler would otherwise
-            // sink the MFMA into their lane-masked store branch, where it returns
-            // wrong sums; an opaque use here pins it in wave-uniform control flow.
+            // An MFMA takes operands from all 64 lanes: an opaque use pins it in
+            // wave-uniform control flow (the compiler may otherwise sink it into
+            // a lane-masked branch, where it returns wrong sums).
 #pragma unroll
             for (int k = 0; k < NM; ++k) asm volatile("" : "+a"(d[k]));
             const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
@@ -359,18 +365,21 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             if (__builtin_expect(__any(!ok), 0)) {
                 if (writer && !ok && in_cols && pos < nv) qs.fix[atomicAdd(&qs.n_fix, 1)] = col & ~7;
             }
-            const float val = (in_cols && pos < nv) ? acc : -INFINITY;
-            if (srow && writer) {
-                if (POOL) { if (in_cols) srow[col] = val; }
-                else if (pos < nv8) srow[pos] = val;
-            }
-            if (!POOL && brow) {
-                float bm = dpp_row_shr_max(val, 1);
-                bm = dpp_row_shr_max(bm, 2);
-                bm = dpp_row_shr_max(bm, 4);
-                // lanes 7 and 15 of the row now hold the maxima of keys 0..7 and 8..15
-                if (writer && (n & 7) == 7 && (pos & ~7) < nv) brow[pos >> 3] = bm;
-            }
+            vt[t] = (in_cols && pos < nv) ? acc : -INFINITY;
+        }
+        const float val = lg == 0 ? vt[0] : (lg == 1 ? vt[1] : (lg == 2 ? vt[2] : vt[3]));
+        const int col = col_base + l;                  // = col_base + 16 lg + n
+        const bool in_cols = col < ncols;
+        if (srow) {
+            if (POOL) { if (in_cols) srow[col] = val; }
+            else if (col < nv8) srow[col] = val;
+        }
+        if (!POOL && brow) {
+            float bm = dpp_row_shr_max(val, 1);
+            bm = dpp_row_shr_max(bm, 2);
+            bm = dpp_row_shr_max(bm, 4);
+            // lanes 8j + 7 now hold the maximum of keys 8j .. 8j+7 of the batch
+            if ((n & 7) == 7 && (col & ~7) < nv) brow[col >> 3] = bm;
         }
     };
 
