@@ -10,30 +10,36 @@
 // [section 2.3.3].
 //
 // MI355X mapping
-//   * One workgroup per (row, group of 16 heads) walks the row's whole entry
-//     list -- its selected FP4 entries padded to a multiple of 64, then its
-//     window entries -- in chunks of 64 with an online softmax.  No split
-//     partials and no merge pass: the query is read once, every output is
-//     written once, and a row's result does not depend on how many rows share
-//     the launch.  The workgroups of one row are placed on one XCD so that
-//     its gathered entries are fetched into one L2.
+//   * A row's entry list is its selected FP4 entries padded to a multiple of
+//     64, then its window entries; it is walked in chunks of 64 with an
+//     online softmax.  One workgroup takes (row, group of 16 heads, split):
+//     without a workspace there is one split and the workgroup writes the
+//     final output; with one, a launch with few rows gives each (row, group)
+//     up to 8 splits of consecutive chunks (so the grid reaches about 256
+//     workgroups), each split writes its normalised partial output with its
+//     running max and sum, and attn_merge_kernel joins the splits (and, in the
+//     two-call form, the other branch's partial and the sink) in a fixed
+//     order.  Workgroups are numbered so that a row's workgroups share one
+//     XCD and its gathered entries one L2.
 //   * 8 waves: wave w dequantises entries 16(w%4)..+15 of the chunk over the
 //     channel half w/4 straight into registers as the A operand of
-//     S^T = K q^T (V_MFMA_F32_16X16X32_BF16; the channel-to-slot order of the
-//     contraction is chosen so a lane's 64 channels are contiguous bytes), and
-//     writes the same values transposed into LDS for P.V.  The two half-sums
-//     of each S^T tile meet in LDS; every wave then holds all 64 scores of
-//     its 16 heads, runs the same softmax, and keeps P in registers as the B
-//     operand of O^T = V^T P^T over its own 64 channels.
+//     S^T = K q^T (V_MFMA_F32_16X16X32_F16), and stores the same values
+//     row-major into LDS.  The two half-sums of each S^T tile meet in LDS;
+//     every wave then holds all 64 scores of its 16 heads, runs the same
+//     softmax in base 2, and keeps P in registers as the B operand of
+//     O^T = V^T P^T over its own 64 channels, with V^T read from the
+//     row-major LDS copy by transposing reads (DS_READ_B64_TR_B16).
 //   * LDS and the partial scores are double-buffered and the next chunk's
 //     bytes are in flight while the current one is processed: one barrier
 //     per chunk.
-//   * FP4 x E4M3 values have at most 6 significant bits and lie in
-//     [2^-10, 2688]: exact in bf16 and fp16.  E2M1 codes become fp16 through a
-//     byte-permute table, are scaled with packed fp16 multiplies and turned
-//     into bf16 by exponent re-biasing; P.V runs in fp16 with P in fp16.
-//     Window values E4M3 x 2^e are exact in bf16; their P.V runs in bf16 with
-//     P split into a bf16 head and tail.
+//   * Both matmuls run in fp16 with exact operands: the query is scaled by a
+//     power of two per head so its largest component sits in [2^14, 2^15);
+//     every entry of a row is scaled by one power of two 2^tw chosen from the
+//     row's window scales, so FP4 x E4M3 values (at most 6 significant bits,
+//     in [2^-10, 2688]) and E4M3 x 2^e window values are exact in fp16.  The
+//     scaled conversion instructions (V_CVT_SCALEF32_PK_F16_FP4 / _FP8) apply
+//     the power of two as they convert.  The scalings are undone on the fp32
+//     scores and outputs.
 #include <type_traits>
 
 #include "csa2_device.h"
@@ -42,7 +48,6 @@
 namespace csa2 {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int AT_ENT = 64;              // entries per chunk
 constexpr int AT_WAVES = 8;
@@ -61,35 +66,6 @@ struct AttnSmem {
 constexpr size_t AT_LDS = sizeof(AttnSmem);
 static_assert(AT_LDS <= 160 * 1024, "attention LDS exceeds the 160 KB of a CU");
 
-
-// Eight E2M1 codes (one dword) -> four fp16 pairs (channels 2i, 2i+1).
-// The fp16 high byte of each magnitude comes from a byte-permute table:
-// 0, 0.5, 1, 1.5, 2, 3, 4, 6 = 0x00, 0x38, 0x3C, 0x3E, 0x40, 0x42, 0x44, 0x46.
-__device__ __forceinline__ void e2m1x8_to_f16x2(uint32_t w, uint32_t* pr) {
-    const uint32_t lut_lo = 0x3E3C3800u, lut_hi = 0x46444240u;
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    const uint32_t hb_lo = __builtin_amdgcn_perm(lut_hi, lut_lo, lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
-    const uint32_t hb_hi = __builtin_amdgcn_perm(lut_hi, lut_lo, hi & 0x07070707u) | ((hi & 0x08080808u) << 4);
-    pr[0] = __builtin_amdgcn_perm(hb_hi, hb_lo, 0x040C000Cu);
-    pr[1] = __builtin_amdgcn_perm(hb_hi, hb_lo, 0x050C010Cu);
-    pr[2] = __builtin_amdgcn_perm(hb_hi, hb_lo, 0x060C020Cu);
-    pr[3] = __builtin_amdgcn_perm(hb_hi, hb_lo, 0x070C030Cu);
-}
-
-// fp16 pair -> bf16 pair, exact for zero and for normal fp16 values whose
-// mantissa fits in 7 bits (all dequantised FP4 x E4M3 values): re-bias the
-// exponent by 127 - 15 = 112 and drop three zero mantissa bits.
-__device__ __forceinline__ uint32_t f16x2_to_bf16x2_exact(uint32_t x) {
-    const uint32_t t = x & 0x7FFF7FFFu, sgn = x & 0x80008000u;
-    const uint32_t m = (t >> 3) & 0x0FFF0FFFu;
-    const uint32_t nz = ((t + 0x7FFF7FFFu) >> 15) & 0x00010001u;   // per half: value != 0
-    return sgn | (m + nz * 0x3800u);
-}
-
-__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
-    const f16x2 r = __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b);
-    return __builtin_bit_cast(uint32_t, r);
-}
 
 // Raw bytes of one lane's share of a chunk: the 64 channels
 // 256*kh + 64*g .. +63 of one entry (32 B of FP4 codes or 64 B of E4M3 codes)
