@@ -43,7 +43,7 @@ struct __align__(16) TkShared {
     uint32_t hist[TK_BINS];
     uint32_t part[2][TK_WAVES];
     uint32_t red[3][TK_WAVES];
-    uint32_t digit, above, count;
+    uint32_t digit, above, count, digit2;
     int32_t pool[TK_POOL];             // fused selection: the row's pool, ascending
 };
 
@@ -104,10 +104,17 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
 
 // ---------------------------------------------------------------- one row's selection
 // KEYS(sweep, u) fills u[16] with the order keys of columns
-// sweep*16384 + 16*threadIdx.x + i (0 where absent); EMIT(col, slot) writes
-// the id of selected column `col` to output slot `slot`.  Returns the count.
+// sweep*16384 + 16*threadIdx.x + i (0 where absent); EMIT(col, slot, key)
+// writes the id of selected column `col` to output slot `slot`.  Returns the
+// count.
+//
+// With 0 < k2 < k, the first radix pass also locates the histogram bin of the
+// k2-th largest key, and (thr_mask, thr_val) are set so that the keys u with
+// (u & thr_mask) >= thr_val are those of that bin and above: a superset of
+// the top k2.  Otherwise every key passes (thr_mask = thr_val = 0).
 template <class KEYS, class EMIT>
-__device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit) {
+__device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit,
+                                               uint32_t k2, uint32_t& thr_mask, uint32_t& thr_val) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsweep = (ncols + TK_SWEEP - 1) / TK_SWEEP;
     uint32_t u[TK_ITEMS];
@@ -140,6 +147,8 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
     // ---- radix select: prefix/mask describe the bits decided so far
     uint32_t prefix = 0u, mask = 0u, need = 0u;   // select (u & mask) > prefix, or == prefix for the first `need`
     int pb = 0;                                    // part buffer of the next scan
+    thr_mask = 0u;
+    thr_val = 0u;
     if (n_present > (uint32_t)k) {
         const uint32_t diff = umin ^ umax;
         int hb = diff ? 31 - __clz(diff) : -1;     // highest bit that is not common to all keys
@@ -177,9 +186,15 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
                     sh.above = before;
                     sh.count = hb4[j];
                 }
+                // first pass: every present key is in the histogram, rem == k
+                if (pass == 0 && hb4[j] != 0u && before < k2 && k2 <= before + hb4[j]) sh.digit2 = (uint32_t)(b0 + 3 - j);
                 before += hb4[j];
             }
             __syncthreads();
+            if (pass == 0 && k2 > 0u && k2 < (uint32_t)k) {
+                thr_mask = mask | (dmask << shift);
+                thr_val = prefix | (sh.digit2 << shift);
+            }
             prefix |= sh.digit << shift;
             mask |= dmask << shift;
             rem -= sh.above;
@@ -221,7 +236,7 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
                 sel = hi > prefix;
                 if (hi == prefix) { sel = eq_rank < need; eq_rank++; }
             }
-            if (sel) emit(c0 + i, pos++);
+            if (sel) emit(c0 + i, pos++, u[i]);
         }
         gt_base += tot >> 16;
         eq_base += tot & 0xFFFFu;
@@ -247,12 +262,13 @@ __device__ __forceinline__ void load_cols(const float* krow, int ncols, int c0, 
 }
 
 // Keys of the two pool blocks behind columns c0 .. c0+15 (c0 a multiple of
-// 16), read by position from a 16-B aligned row: two runs of 8 keys.
+// 16), read by position from a 16-B aligned row: two runs of 8 keys.  A
+// negative pool entry marks a block that is skipped (its keys are absent).
 __device__ __forceinline__ void load_pool_keys(const float* krow, const int32_t* pool, int ncols, int c0, uint32_t* u) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int cb = c0 + 8 * h;
-        if (cb < ncols) {
+        if (cb < ncols && pool[cb >> 3] >= 0) {
             const float* p = krow + 8 * pool[cb >> 3];
             const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
             const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -285,8 +301,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         if (a.keys_by_id) load_pool_keys(krow, pool, ncols, c0, u);
         else load_cols(krow, ncols, c0, u);
     };
-    auto emit = [&](int col, uint32_t slot) { orow[slot] = col_id(pool, col); };
-    const uint32_t n = select_row(sh, ncols, a.k, keys, emit);
+    auto emit = [&](int col, uint32_t slot, uint32_t) { orow[slot] = col_id(pool, col); };
+    uint32_t thr_mask, thr_val;
+    const uint32_t n = select_row(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val);
     for (int j = (int)n + threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = -1;
     if (threadIdx.x == 0) a.out_count[row] = (int32_t)n;
 }
@@ -303,10 +320,19 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     int32_t* prow = a.pool + (int64_t)row * a.pool_stride;
     int32_t* irow = a.idx + (int64_t)row * a.idx_stride;
 
-    // ---- blocks
+    // ---- blocks.  The top k positions lie in the top k blocks: a block ranked
+    // above the block of a top-k position holds a distinct position ranked
+    // above that position (its maximum; on equal values its lower id), so
+    // fewer than k blocks rank above it.  The first radix pass bounds the top
+    // k blocks from below by a histogram bin; pool blocks below that bin are
+    // kept in the pool but marked (negative in LDS) and not read again.
+    uint32_t thr_mask = 0u, thr_val = 0u;
     auto bkeys = [&](int s, uint32_t* u) { load_cols(brow, nb, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
-    auto bemit = [&](int col, uint32_t slot) { sh.pool[slot] = col; prow[slot] = col; };
-    const uint32_t np = select_row(sh, nb, a.n_pool, bkeys, bemit);
+    auto bemit = [&](int col, uint32_t slot, uint32_t key) {
+        sh.pool[slot] = (key & thr_mask) >= thr_val ? col : (int32_t)((uint32_t)col | 0x80000000u);
+        prow[slot] = col;
+    };
+    const uint32_t np = select_row(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
     for (int j = (int)np + threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = -1;
     if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
     __syncthreads();                                  // the pool is complete in LDS
@@ -314,8 +340,9 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     // ---- positions: column c is position 8 * pool[c/8] + c%8 (-inf past n_vis)
     const int ncols = 8 * (int)np;
     auto pkeys = [&](int s, uint32_t* u) { load_pool_keys(srow, sh.pool, ncols, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
-    auto pemit = [&](int col, uint32_t slot) { irow[slot] = 8 * sh.pool[col >> 3] + (col & 7); };
-    const uint32_t ni = select_row(sh, ncols, a.k, pkeys, pemit);
+    auto pemit = [&](int col, uint32_t slot, uint32_t) { irow[slot] = 8 * sh.pool[col >> 3] + (col & 7); };
+    uint32_t thr2_mask, thr2_val;
+    const uint32_t ni = select_row(sh, ncols, a.k, pkeys, pemit, 0u, thr2_mask, thr2_val);
     for (int j = (int)ni + threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = -1;
     if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
 }

@@ -270,11 +270,13 @@ def test_topk_block_counts_and_pool_ids():
         assert int(icnt2[r]) == len(ref2) and np.array_equal(idx2[r, :len(ref2)].cpu().numpy(), ref2)
 
 
-@pytest.mark.parametrize("ties", [False, True])
-def test_select_full_exact(ties):
-    """The fused Full-layer selection equals the oracle's pool + top-512 and
+@pytest.mark.parametrize("ties,k", [(False, 512), (True, 512), (False, 37), (True, 37), (True, 2048)])
+def test_select_full_exact(ties, k):
+    """The fused Full-layer selection equals the oracle's pool + top-k and
     the two-call form, on rows with no entry, a partial block, fewer than
-    2,048 blocks and more than 16,384 blocks (two sweeps)."""
+    2,048 blocks and more than 16,384 blocks (two sweeps).  With k below the
+    pool size only the pool blocks at or above the histogram bin of the k-th
+    block are read again; heavy ties put many blocks into that bin."""
     n_vis = np.array([0, 13, 5003, 16384 * 8 + 21], np.int32)
     n_rows, n = len(n_vis), int(n_vis.max())
     nv8 = (n + 7) // 8 * 8
@@ -291,17 +293,17 @@ def test_select_full_exact(ties):
     S, Bm, nv = T(sc), T(bm), T(n_vis)
     pool = torch.full((n_rows, 2048), -7, dtype=torch.int32, device=DEV)
     pcnt = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
-    idx = torch.full((n_rows, 512), -7, dtype=torch.int32, device=DEV)
+    idx = torch.full((n_rows, k), -7, dtype=torch.int32, device=DEV)
     icnt = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
-    lib.csa2_select_full(Bm, S, nv, n, pool, pcnt, idx, icnt)
+    lib.csa2_select_full(Bm, S, nv, n, pool, pcnt, idx, icnt, k=k)
     pool2 = torch.empty_like(pool); pcnt2 = torch.empty_like(pcnt)
     idx2 = torch.empty_like(idx); icnt2 = torch.empty_like(icnt)
     lib.csa2_select_topk(Bm, 2048, pool2, pcnt2, n_cols=nv, cols_div=8, max_cols=nv8 // 8)
-    lib.csa2_select_topk(S, 512, idx2, icnt2, n_cols=pcnt2, cols_mul=8, pool_blocks=pool2, keys_by_id=True,
+    lib.csa2_select_topk(S, k, idx2, icnt2, n_cols=pcnt2, cols_mul=8, pool_blocks=pool2, keys_by_id=True,
                          max_cols=16384)
     torch.cuda.synchronize()
     for r in range(n_rows):
-        p_ref, i_ref = oracle.full_select(sc[r, :n_vis[r]])
+        p_ref, i_ref = oracle.full_select(sc[r, :n_vis[r]], k=k)
         assert int(pcnt[r]) == len(p_ref) and np.array_equal(pool[r, :len(p_ref)].cpu().numpy(), p_ref)
         assert np.all(pool[r, len(p_ref):].cpu().numpy() == -1)
         assert int(icnt[r]) == len(i_ref) and np.array_equal(idx[r, :len(i_ref)].cpu().numpy(), i_ref)
