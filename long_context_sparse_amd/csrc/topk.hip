@@ -27,6 +27,7 @@
 // The Full layer's two selections (2,048 blocks by their maxima, then 512
 // positions among those blocks' scores) also run fused in one workgroup per
 // row, with the pool kept in LDS between them.
+#include "csa2.h"
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -38,6 +39,8 @@ constexpr int TK_SWEEP = TK_THREADS * TK_ITEMS;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_BINS = 4096;
 constexpr int TK_POOL = 2048;
+static_assert(CSA2_MAX_SELECT <= TK_BINS, "selected ids are staged in the histogram");
+static_assert(CSA2_MAX_POOL_BLOCKS <= TK_POOL, "the pool is held in LDS");
 
 struct __align__(16) TkShared {
     uint32_t hist[TK_BINS];
@@ -105,18 +108,19 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
 // ---------------------------------------------------------------- one row's selection
 // KEYS(sweep, u) fills u[16] with the order keys of columns
 // sweep*16384 + 16*threadIdx.x + i (0 where absent); EMIT(col, slot, key)
-// writes the id of selected column `col` to output slot `slot`.  Returns the
-// count.
+// records selected column `col` for output slot `slot`.  Returns the count.
+// NSW = 1 compiles the case of one sweep (ncols <= 16,384: the keys are read
+// once and stay in registers); NSW = 0 handles any ncols.
 //
 // With 0 < k2 < k, the first radix pass also locates the histogram bin of the
 // k2-th largest key, and (thr_mask, thr_val) are set so that the keys u with
 // (u & thr_mask) >= thr_val are those of that bin and above: a superset of
 // the top k2.  Otherwise every key passes (thr_mask = thr_val = 0).
-template <class KEYS, class EMIT>
+template <int NSW, class KEYS, class EMIT>
 __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit,
                                                uint32_t k2, uint32_t& thr_mask, uint32_t& thr_val) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nsweep = (ncols + TK_SWEEP - 1) / TK_SWEEP;
+    const int nsweep = NSW ? NSW : (ncols + TK_SWEEP - 1) / TK_SWEEP;
     uint32_t u[TK_ITEMS];
 #pragma unroll
     for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
@@ -301,10 +305,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         if (a.keys_by_id) load_pool_keys(krow, pool, ncols, c0, u);
         else load_cols(krow, ncols, c0, u);
     };
-    auto emit = [&](int col, uint32_t slot, uint32_t) { orow[slot] = col_id(pool, col); };
+    // selected columns are staged in LDS (the histogram is free once the
+    // threshold is known) and leave in coalesced runs
+    auto emit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)col; };
     uint32_t thr_mask, thr_val;
-    const uint32_t n = select_row(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val);
-    for (int j = (int)n + threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = -1;
+    const uint32_t n = ncols <= TK_SWEEP ? select_row<1>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val)
+                                         : select_row<0>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val);
+    __syncthreads();
+    for (int j = threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = j < (int)n ? col_id(pool, (int)sh.hist[j]) : -1;
     if (threadIdx.x == 0) a.out_count[row] = (int32_t)n;
 }
 
@@ -330,21 +338,24 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     auto bkeys = [&](int s, uint32_t* u) { load_cols(brow, nb, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
     auto bemit = [&](int col, uint32_t slot, uint32_t key) {
         sh.pool[slot] = (key & thr_mask) >= thr_val ? col : (int32_t)((uint32_t)col | 0x80000000u);
-        prow[slot] = col;
     };
-    const uint32_t np = select_row(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
-    for (int j = (int)np + threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = -1;
-    if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
+    const uint32_t np = nb <= TK_SWEEP ? select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val)
+                                       : select_row<0>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
     __syncthreads();                                  // the pool is complete in LDS
 
     // ---- positions: column c is position 8 * pool[c/8] + c%8 (-inf past n_vis)
     const int ncols = 8 * (int)np;
     auto pkeys = [&](int s, uint32_t* u) { load_pool_keys(srow, sh.pool, ncols, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
-    auto pemit = [&](int col, uint32_t slot, uint32_t) { irow[slot] = 8 * sh.pool[col >> 3] + (col & 7); };
+    // (only candidate blocks have present keys, so their entries are >= 0)
+    auto pemit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)(8 * sh.pool[col >> 3] + (col & 7)); };
     uint32_t thr2_mask, thr2_val;
-    const uint32_t ni = select_row(sh, ncols, a.k, pkeys, pemit, 0u, thr2_mask, thr2_val);
-    for (int j = (int)ni + threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = -1;
-    if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
+    const uint32_t ni = select_row<1>(sh, ncols, a.k, pkeys, pemit, 0u, thr2_mask, thr2_val);
+    __syncthreads();
+
+    // ---- outputs, from LDS in coalesced runs (no barrier waits on these stores)
+    for (int j = threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = j < (int)np ? (sh.pool[j] & 0x7FFFFFFF) : -1;
+    for (int j = threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = j < (int)ni ? (int32_t)sh.hist[j] : -1;
+    if (threadIdx.x == 0) { a.pool_count[row] = (int32_t)np; a.idx_count[row] = (int32_t)ni; }
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
