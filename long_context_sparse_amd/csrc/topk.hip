@@ -207,8 +207,9 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
             ++pass;
         }
         need = rem;
+    } else {
+        need = (uint32_t)k;        // mask = prefix = 0: every present key counts as equal and is taken
     }
-    const bool take_all = n_present <= (uint32_t)k;
 
     // ---- selection in column order: one scan of (greater, equal) counts; the
     // equal items taken before a thread are min(equal before it, need)
@@ -218,11 +219,9 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
         uint32_t n_gt = 0u, n_eq = 0u;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
-            if (u[i] == 0u) continue;
-            if (take_all) { n_gt++; continue; }
             const uint32_t hi = u[i] & mask;
-            n_gt += hi > prefix;
-            n_eq += hi == prefix;
+            n_gt += u[i] != 0u && hi > prefix;
+            n_eq += u[i] != 0u && hi == prefix;
         }
         uint32_t tot;
         const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, sh.part[pb], tot);
@@ -232,15 +231,12 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
         const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
-            if (u[i] == 0u) continue;
-            bool sel;
-            if (take_all) sel = true;
-            else {
-                const uint32_t hi = u[i] & mask;
-                sel = hi > prefix;
-                if (hi == prefix) { sel = eq_rank < need; eq_rank++; }
-            }
-            if (sel) emit(c0 + i, pos++, u[i]);
+            const uint32_t hi = u[i] & mask;
+            const bool eq = u[i] != 0u && hi == prefix;
+            const bool sel = (u[i] != 0u && hi > prefix) || (eq && eq_rank < need);
+            eq_rank += eq;
+            if (sel) emit(c0 + i, pos, u[i]);
+            pos += sel;
         }
         gt_base += tot >> 16;
         eq_base += tot & 0xFFFFu;
@@ -346,8 +342,11 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     // ---- positions: column c is position 8 * pool[c/8] + c%8 (-inf past n_vis)
     const int ncols = 8 * (int)np;
     auto pkeys = [&](int s, uint32_t* u) { load_pool_keys(srow, sh.pool, ncols, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
-    // (only candidate blocks have present keys, so their entries are >= 0)
-    auto pemit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)(8 * sh.pool[col >> 3] + (col & 7)); };
+    // Thread t's columns 16t .. 16t+15 are pool blocks 2t and 2t+1; only
+    // candidate blocks have present keys, so the entries used are >= 0.
+    const int pb0 = 2 * (int)threadIdx.x < (int)np ? 8 * (sh.pool[2 * threadIdx.x] & 0x7FFFFFFF) : 0;
+    const int pb1 = 2 * (int)threadIdx.x + 1 < (int)np ? 8 * (sh.pool[2 * threadIdx.x + 1] & 0x7FFFFFFF) : 0;
+    auto pemit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)(((col & 8) ? pb1 : pb0) + (col & 7)); };
     uint32_t thr2_mask, thr2_val;
     const uint32_t ni = select_row<1>(sh, ncols, a.k, pkeys, pemit, 0u, thr2_mask, thr2_val);
     __syncthreads();
