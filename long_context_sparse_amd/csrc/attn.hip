@@ -252,10 +252,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int cb = split * ctot / S, ce = (split + 1) * ctot / S;   // this split's chunks
     const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
-    // cache slots of the selected entries; the query and its per-head scale;
+    // cache slots of the selected entries (the index is read before its count
+    // is known: one dependent load less); the query and its per-head scale;
     // the exponent range of the row's window scales
-    if ((int)threadIdx.x < nsp)
-        sm.ent[threadIdx.x] = entry_of(kv, a.req[row], a.idx[(int64_t)row * a.idx_stride + threadIdx.x]);
+    const int32_t my_idx = a.idx ? a.idx[(int64_t)row * a.idx_stride + min((int64_t)threadIdx.x, a.idx_stride - 1)] : 0;
+    if ((int)threadIdx.x < nsp) sm.ent[threadIdx.x] = entry_of(kv, a.req[row], my_idx);
     int wmax = 0, wmin = 255;                       // over nonzero scale codes (all-zero groups have code 0)
     if ((int)threadIdx.x * 8 < nsw * 32) {
         const uint2 v = *(const uint2*)(a.swa_scales + swa0 * 32 + 8 * threadIdx.x);
@@ -301,12 +302,15 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // Software pipeline, one barrier per chunk: while a wave turns the scores of
     // chunk c into probabilities and accumulates P.V (LDS buffers c & 1), it
     // dequantises chunk c + 1 and computes its partial scores (buffers
-    // (c + 1) & 1).  Chunk c's bytes sit in raw[c & 1]; right after they are
-    // dequantised the loads of chunk c + 2 go into the same registers.
-    RawChunk raw0, raw1;
+    // (c + 1) & 1).  Three chunks are in flight: chunk c's bytes sit in
+    // raw[(c - cb) % 3], and right after they are dequantised the loads of
+    // chunk c + 3 go into the same registers (a gathered entry takes several
+    // microseconds to arrive when every CU is gathering).
+    RawChunk raw0, raw1, raw2;
     if (ce > cb) {
         load_raw(kv, a, sm, cb, csp, nsp, nsw, swa0, et, kh, n, g, raw0);
         load_raw(kv, a, sm, min(cb + 1, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw1);
+        load_raw(kv, a, sm, min(cb + 2, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw2);
     }
     f32x4 oacc[4];
 #pragma unroll
@@ -315,16 +319,16 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int chb = 256 * kh + 64 * g;               // first of this lane's 64 dequant channels
     const int v_lane = (16 * et + n) * V_LD + chb;  // this lane's entry row and channels in LDS
 
-    // dequantise chunk c, its partial scores into sp[c & 1]; reload raw with chunk c + 2
+    // dequantise chunk c, its partial scores into sp[c & 1]; reload raw with chunk c + 3
     auto stage_a = [&](auto swc, const int c, RawChunk& raw) __attribute__((always_inline)) {
         constexpr bool SW = decltype(swc)::value;
         _Float16* vb = sm.v[c & 1];
         f16x8 kop[8];
         if (SW) dequant_swa(raw, tw, vb + v_lane, kop);
         else dequant_main(raw, cvt_sel, vb + v_lane, kop);
-        // always issued (the last two re-read the final chunk, unused): a load
-        // under a branch makes the compiler wait for it at the join
-        load_raw(kv, a, sm, min(c + 2, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw);
+        // always issued (near the end they re-read the final chunk, unused): a
+        // load under a branch makes the compiler wait for it at the join
+        load_raw(kv, a, sm, min(c + 3, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw);
         f32x4 sc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], qh[ks], sc, 0, 0, 0);
@@ -379,12 +383,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const std::integral_constant<bool, false> SEL{};
     const std::integral_constant<bool, true> WIN{};
     // One pipeline step: stage A of chunk c + 1 with stage B of chunk c.  The
-    // steps run in pairs with nothing conditional but the chunk type, so the
-    // compiler can count the loads in flight; chunks past the end are
-    // processed as empty (their scores are all masked: no contribution).
+    // steps run in threes with nothing conditional but the chunk type, so the
+    // compiler can count the loads in flight on every path that continues;
+    // the last chunk leaves the loop through a branch that issues no load.
     auto step = [&](const int c, RawChunk& next_raw) __attribute__((always_inline)) {
-        const int ca = min(c + 1, ce - 1) < csp ? 0 : 1;
-        if (ca == 0) stage_a(SEL, c + 1, next_raw);
+        if (c + 1 < csp) stage_a(SEL, c + 1, next_raw);
         else stage_a(WIN, c + 1, next_raw);
         stage_b(c);
         __syncthreads();
@@ -394,9 +397,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         if (cb < csp) stage_a(SEL, cb, raw0);
         else stage_a(WIN, cb, raw0);
         __syncthreads();
-        for (int c = cb; c < ce; c += 2) {
+        for (int c = cb;; c += 3) {
+            if (c + 1 >= ce) { stage_b(c); break; }
             step(c, raw1);
-            step(c + 1, raw0);
+            if (c + 2 >= ce) { stage_b(c + 1); break; }
+            step(c + 1, raw2);
+            if (c + 3 >= ce) { stage_b(c + 2); break; }
+            step(c + 2, raw0);
         }
     }
 
