@@ -341,7 +341,14 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
 
     // ---- positions: column c is position 8 * pool[c/8] + c%8 (-inf past n_vis)
     const int ncols = 8 * (int)np;
-    auto pkeys = [&](int s, uint32_t* u) { load_pool_keys(srow, sh.pool, ncols, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
+    // The k largest block maxima are k distinct scores, so the k-th largest
+    // score is at least the k-th largest block maximum: positions below the
+    // histogram bin of that block are dropped as they are read.
+    auto pkeys = [&](int s, uint32_t* u) {
+        load_pool_keys(srow, sh.pool, ncols, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u);
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; ++i) u[i] = (u[i] & thr_mask) >= thr_val ? u[i] : 0u;
+    };
     // Thread t's columns 16t .. 16t+15 are pool blocks 2t and 2t+1; only
     // candidate blocks have present keys, so the entries used are >= 0.
     const int pb0 = 2 * (int)threadIdx.x < (int)np ? 8 * (sh.pool[2 * threadIdx.x] & 0x7FFFFFFF) : 0;

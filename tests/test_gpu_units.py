@@ -449,6 +449,47 @@ def test_attention_many_rows(n_rows):
     _attn_case(n_rows, 16, counts, swa_counts, n_entries=600, check_rows=list(range(0, n_rows, 97)) + [n_rows - 1])
 
 
+def test_attention_workspace_reuse():
+    """One workspace serves calls of different shapes in a row: each call
+    through it equals, bit for bit, the same call through a fresh workspace
+    (nothing is carried over between calls) and stays within the tolerance
+    of the oracle."""
+    n_rows, H, n_entries = 4, 64, 700
+    lat = bf16(RNG.standard_normal((n_rows * n_entries, 512)).astype(np.float32)).float().numpy()
+    mc, ms = oracle.pack_main(lat)
+    K = oracle.dequant_main(mc, ms)
+    swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
+    wc, wsc = oracle.pack_swa(swa)
+    W = oracle.dequant_swa(wc, wsc)
+    q = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32) * 2)
+    qn = q.float().numpy()
+    counts = np.array([512, 300, 7, 0], np.int32)
+    swa_counts = np.array([128, 5, 0, 128], np.int32)
+    idx = np.full((n_rows, 512), -1, np.int32)
+    for r in range(n_rows):
+        idx[r, :counts[r]] = np.sort(RNG.permutation(n_entries)[:counts[r]])
+    kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), n_slots=n_rows * n_entries, req_stride=n_entries)
+    wsb = max(lib.csa2_attn_workspace_size(n, h) for n, h in ((4, 64), (2, 64), (4, 16)))
+    assert wsb > 0
+    ws = torch.full((wsb // 4,), float('nan'), dtype=torch.float32, device=DEV)
+    for n, h in ((4, 64), (2, 64), (4, 16), (4, 64)):
+        rows = lib.make_rows(T(np.arange(n, dtype=np.int32)), T(np.full(n, n_entries, np.int32)), n_entries)
+        qd = q[:n, :h].contiguous().to(DEV)
+        args = (kv, rows, qd, T(idx[:n]), T(counts[:n]), T(wc), T(wsc), T(np.arange(n, dtype=np.int64) * 128),
+                T(swa_counts[:n]), SIG)
+        o_reused = torch.empty((n, h, 512), dtype=torch.float32, device=DEV)
+        o_fresh = torch.empty_like(o_reused)
+        lib.csa2_sparse_swa_attn(*args, o_reused, workspace=ws)
+        lib.csa2_sparse_swa_attn(*args, o_fresh, workspace=torch.empty_like(ws))
+        torch.cuda.synchronize()
+        assert torch.equal(o_reused, o_fresh), (n, h)
+        Or = o_reused.cpu().numpy()
+        for r in range(n):
+            fo, _ = oracle.attention(qn[r, :h], K[r * n_entries + idx[r, :counts[r]]],
+                                     W[r * 128:r * 128 + swa_counts[r]], sigma=SIG)
+            assert tolerance_ok(Or[r], fo), (n, h, r, np.abs(Or[r] - fo).max())
+
+
 def test_swa_only_and_alias():
     n_rows, H = 2, 16
     swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
