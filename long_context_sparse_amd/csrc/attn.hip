@@ -268,8 +268,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     }
     bf16x8 qb[8];
     float qa = load_q_operand<QBF16>(a.q, (int64_t)row * a.n_heads + h0 + n, kh, g, qb);
-    qa = fmaxf(qa, shfl_xor_f(qa, 16));
-    qa = fmaxf(qa, shfl_xor_f(qa, 32));
+    qa = max_xor32(max_xor16(qa));
     if (et == 0 && g == 0) sm.qmax[kh][n] = qa;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -352,8 +351,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
                         fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
         m = fmaxf(m, fmaxf(fmaxf(fmaxf(z[2][0], z[2][1]), fmaxf(z[2][2], z[2][3])),
                            fmaxf(fmaxf(z[3][0], z[3][1]), fmaxf(z[3][2], z[3][3]))));
-        m = fmaxf(m, shfl_xor_f(m, 16));
-        m = fmaxf(m, shfl_xor_f(m, 32));
+        m = max_xor32(max_xor16(m));
         const float m_new = fmaxf(m_run, m * cz);         // cz > 0: the scaled maximum
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         float lsum = 0.0f;
@@ -366,8 +364,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
                 lsum += p;
                 pb[t >> 1][4 * (t & 1) + i] = (_Float16)p;
             }
-        lsum += shfl_xor_f(lsum, 16);
-        lsum += shfl_xor_f(lsum, 32);
+        lsum = add_xor32(add_xor16(lsum));
         l_run = l_run * alpha + lsum;
         m_run = m_new;
         const _Float16* vb = sm.v[buf];

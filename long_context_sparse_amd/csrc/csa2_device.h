@@ -122,6 +122,29 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 // ---------------------------------------------------------------- waves
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Max / sum of v over lanes l and l ^ 16 (or l ^ 32), without a trip through
+// LDS: V_PERMLANE16_SWAP_B32 applied to two copies of v leaves rows (0, 0, 2,
+// 2) of 16 lanes in one result and rows (1, 1, 3, 3) in the other
+// (V_PERMLANE32_SWAP_B32: halves (0, 0) and (1, 1)), so combining the two
+// combines every lane with its partner.  Both operations are commutative, so
+// the result equals the shuffle-based form bit for bit.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 __device__ __forceinline__ float shfl_up_f(float v, int d) { return __shfl_up(v, d, 64); }
 
 }  // namespace csa2
