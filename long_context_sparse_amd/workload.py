@@ -264,21 +264,26 @@ class Workload:
     # --------------------------------------------------------------- bytes
     def algorithmic_bytes(self) -> dict:
         """Bytes the method must move per step: indexer keys scored, selected
-        main entries gathered, window entries, queries in, outputs out."""
+        main entries gathered, window entries, queries in, outputs out.  Data
+        that several rows share is counted once: the rows of a chunked
+        prefill read one request's keys (its largest visible prefix) and
+        overlapping windows (rows + window - 1 entries)."""
         cfg = self.cfg
         H = cfg.heads
         n_layers = len(self.layers)
         rows = self.n_rows
+        prefill = cfg.mode == "prefill"
         d = {}
         if self.full:
-            d["index_keys_full"] = int(self.n_vis_host.sum()) * 68
+            keys = int(self.n_vis_host.max()) if prefill else int(self.n_vis_host.sum())
+            d["index_keys_full"] = keys * 68
         reindex_layers = n_layers - 1 if cfg.mode != "reindex" else 1
         if reindex_layers:
             pool_pos = int(np.minimum(self.n_vis_host, 16384).sum()) if cfg.mode != "reindex" else rows * 16384
             d["index_keys_pool"] = reindex_layers * pool_pos * 68
         sel = int(np.minimum(self.n_vis_host, 512).sum())
         d["gathered_main"] = n_layers * sel * 288
-        d["swa"] = n_layers * rows * cfg.window * 544
+        d["swa"] = n_layers * (rows + cfg.window - 1 if prefill else rows * cfg.window) * 544
         d["q"] = n_layers * rows * (H * 512 * 2 + cfg.idx_heads * 128 * 2 + cfg.idx_heads * 4)
         d["out"] = n_layers * rows * H * 512 * 4
         d["total"] = sum(d.values())
