@@ -416,8 +416,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             const int ch = 64 * wave + 16 * ct + 4 * g;
-            *(float4*)(wsO + ps * 512 + ch) = make_float4(oacc[ct][0] * inv, oacc[ct][1] * inv,
-                                                          oacc[ct][2] * inv, oacc[ct][3] * inv);
+            // partials and outputs are written once and read by another kernel:
+            // non-temporal stores stream them out instead of leaving them dirty
+            // in L2 for the end-of-kernel write-back
+            __builtin_nontemporal_store((f32x4){oacc[ct][0] * inv, oacc[ct][1] * inv, oacc[ct][2] * inv, oacc[ct][3] * inv},
+                                        (f32x4*)(wsO + ps * 512 + ch));
         }
         if (wave == 0 && g == 0) { wsM[ps] = m_run; wsL[ps] = l_run; }
         return;
@@ -446,7 +449,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         r.y = (wo * oacc[ct][1] + w_p * pin.y) * inv;
         r.z = (wo * oacc[ct][2] + w_p * pin.z) * inv;
         r.w = (wo * oacc[ct][3] + w_p * pin.w) * inv;
-        *(float4*)(orow + ch) = r;
+        __builtin_nontemporal_store((f32x4){r.x, r.y, r.z, r.w}, (f32x4*)(orow + ch));
     }
     if (a.lse_out && wave == 0 && g == 0)
         a.lse_out[(int64_t)row * a.n_heads + h] = (M == -INFINITY || den == 0.0f) ? -INFINITY : (M + log2f(den)) * LN2;
@@ -500,7 +503,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
         if (sk != -INFINITY) den += __builtin_amdgcn_exp2f(sk - M);
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    *(float4*)(a.out + rh * 512 + c4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    __builtin_nontemporal_store((f32x4){acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv},
+                                (f32x4*)(a.out + rh * 512 + c4));
     if (a.lse_out && c4 == 0) a.lse_out[rh] = den > 0.0f ? (M + log2f(den)) * LN2 : -INFINITY;
 }
 
