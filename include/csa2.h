@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 typedef enum {
     CSA2_OK = 0,
@@ -150,6 +150,23 @@ csa2_status csa2_index_score(const csa2_kv* kv, const csa2_rows* rows,
                              float* scores, int64_t scores_stride,
                              float* block_max, int64_t block_max_stride,
                              void* stream);
+
+/* Chunked prefill: the same full scan for query rows that all belong to ONE
+ * request `req` (host value; rows->req is not read and may be NULL), each row
+ * with its own visible count rows->n_vis[row] (in a causal chunk the later
+ * tokens see more entries).  The rows share the key stream: a workgroup loads
+ * each 16-key tile once and scores it against up to 16 rows, so the scan is
+ * bound by the MFMA and the score writes instead of by re-reading the keys
+ * once per row ('DeepSeek-V4' page, section 2.3.1: the indexer scores every
+ * query token against every preceding compressed entry).  The outputs, their
+ * layout and their bits are those of csa2_index_score's full scan.
+ * 0 <= req < number of requests the cache holds; n_idx_heads in 1..16. */
+csa2_status csa2_index_score_shared(const csa2_kv* kv, const csa2_rows* rows, int32_t req,
+                                    const void* q_idx, csa2_dtype q_dtype, int32_t n_idx_heads,
+                                    const float* w,
+                                    float* scores, int64_t scores_stride,
+                                    float* block_max, int64_t block_max_stride,
+                                    void* stream);
 
 /* ---------------------------------------------------------------- top-k
  * Exact row-wise top-k ('DeepSeek-V4' page, section 2.3.1, top-k selector;

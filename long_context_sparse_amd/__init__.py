@@ -46,6 +46,7 @@ class Rows(ctypes.Structure):
 _lib = None
 EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
+    "csa2_index_score_shared",
     "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
     "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost",
 )
@@ -67,6 +68,8 @@ def lib():
     L.csa2_pack_kv.argtypes = [ctypes.c_int, P, ctypes.c_int, i64, i64, P, P, P, P]
     L.csa2_index_score.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P,
                                    P, i64, P, P, i64, P, i64, P]
+    L.csa2_index_score_shared.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), i32, P, ctypes.c_int, i32, P,
+                                          P, i64, P, i64, P]
     L.csa2_select_topk.argtypes = [P, i64, P, i32, i32, P, i64, i32, i32, i32, i32, P, i64, P, P]
     L.csa2_select_full.argtypes = [P, i64, P, i64, P, i32, i32, i32, i32, P, i64, P, P, i64, P, P]
     L.csa2_attn_workspace_size.restype = ctypes.c_size_t
@@ -124,8 +127,9 @@ def make_kv(main_codes=None, main_scales=None, idx_codes=None, idx_scales=None, 
 
 
 def make_rows(req, n_vis, max_vis):
-    """Host descriptor of the query rows (keeps its tensors alive)."""
-    rows = Rows(_ptr(req), _ptr(n_vis), int(req.shape[0]), int(max_vis))
+    """Host descriptor of the query rows (keeps its tensors alive).  `req` may
+    be None for csa2_index_score_shared, which takes the request as a value."""
+    rows = Rows(_ptr(req), _ptr(n_vis), int(n_vis.shape[0]), int(max_vis))
     rows._refs = (req, n_vis)
     return rows
 
@@ -155,6 +159,17 @@ def csa2_index_score(kv, rows, q_idx, w, scores=None, block_max=None, pool_block
     _check("csa2_index_score", lib().csa2_index_score(
         ctypes.byref(kv), ctypes.byref(rows), _ptr(q_idx), _dtype(q_idx), Hi, _ptr(w),
         _ptr(pool_blocks), 0 if pool_blocks is None else _rstride(pool_blocks), _ptr(pool_count),
+        _ptr(scores), 0 if scores is None else _rstride(scores),
+        _ptr(block_max), 0 if block_max is None else _rstride(block_max), _stream(stream)))
+
+
+def csa2_index_score_shared(kv, rows, req, q_idx, w, scores=None, block_max=None, stream=None):
+    """Full scan for query rows that all belong to request `req` (chunked
+    prefill): each key tile is loaded once per 16 rows.  Same outputs as
+    csa2_index_score's full scan."""
+    Hi = int(q_idx.shape[1])
+    _check("csa2_index_score_shared", lib().csa2_index_score_shared(
+        ctypes.byref(kv), ctypes.byref(rows), int(req), _ptr(q_idx), _dtype(q_idx), Hi, _ptr(w),
         _ptr(scores), 0 if scores is None else _rstride(scores),
         _ptr(block_max), 0 if block_max is None else _rstride(block_max), _stream(stream)))
 

@@ -161,6 +161,46 @@ csa2_status csa2_index_score(const csa2_kv* kv, const csa2_rows* rows, const voi
     return hip_status(csa2::launch_index_score(v, a, (hipStream_t)stream), "csa2_index_score launch");
 }
 
+csa2_status csa2_index_score_shared(const csa2_kv* kv, const csa2_rows* rows, int32_t req, const void* q_idx,
+                                    csa2_dtype q_dtype, int32_t n_idx_heads, const float* w, float* scores,
+                                    int64_t scores_stride, float* block_max, int64_t block_max_stride, void* stream) {
+    csa2::KvView v;
+    csa2_status s = make_view(kv, false, true, &v);
+    if (s != CSA2_OK) return s;
+    if (!rows) return fail(CSA2_ERR_NULL, "rows descriptor is NULL");
+    if (rows->n_rows < 0 || rows->n_rows > 65535) return fail(CSA2_ERR_RANGE, "n_rows must be in 0..65535");
+    if (rows->max_vis < 0 || rows->max_vis > (1 << 30)) return fail(CSA2_ERR_RANGE, "max_vis out of range");
+    if (n_idx_heads < 1 || n_idx_heads > 16) return fail(CSA2_ERR_UNSUPPORTED, "n_idx_heads must be in 1..16 (got %d)", n_idx_heads);
+    if (q_dtype != CSA2_BF16 && q_dtype != CSA2_F32) return fail(CSA2_ERR_UNSUPPORTED, "unknown q dtype");
+    if (req < 0) return fail(CSA2_ERR_RANGE, "req must be >= 0");
+    if (rows->n_rows == 0) return CSA2_OK;
+    if (!rows->n_vis) return fail(CSA2_ERR_NULL, "rows->n_vis is NULL");
+    if (!q_idx || !w) return fail(CSA2_ERR_NULL, "q_idx / w is NULL");
+    if (!aligned(q_idx, 16)) return fail(CSA2_ERR_ALIGN, "q_idx must be 16-byte aligned");
+    if (!scores && !block_max) return fail(CSA2_ERR_NULL, "scores and block_max are both NULL");
+    const int64_t nv8 = ((int64_t)rows->max_vis + 7) & ~(int64_t)7;
+    if (scores && scores_stride < nv8) return fail(CSA2_ERR_SHAPE, "scores_stride %lld < roundup(max_vis, 8)", (long long)scores_stride);
+    if (block_max && block_max_stride < nv8 / 8) return fail(CSA2_ERR_SHAPE, "block_max_stride too small");
+    if (rows->max_vis == 0) return CSA2_OK;
+    csa2::IndexScoreArgs a;
+    a.q_idx = q_idx;
+    a.q_bf16 = q_dtype == CSA2_BF16;
+    a.n_heads = n_idx_heads;
+    a.w = w;
+    a.req = nullptr;
+    a.n_vis = rows->n_vis;
+    a.n_rows = rows->n_rows;
+    a.max_vis = rows->max_vis;
+    a.pool = nullptr;
+    a.pool_stride = 0;
+    a.pool_count = nullptr;
+    a.scores = scores;
+    a.scores_stride = scores_stride;
+    a.block_max = block_max;
+    a.block_max_stride = block_max_stride;
+    return hip_status(csa2::launch_index_score_shared(v, a, req, (hipStream_t)stream), "csa2_index_score_shared launch");
+}
+
 csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_t* n_cols, int32_t cols_mul,
                              int32_t cols_div, const int32_t* pool_blocks, int64_t pool_stride, int32_t keys_by_id,
                              int32_t n_rows, int32_t max_cols, int32_t k, int32_t* out_ids, int64_t out_stride,

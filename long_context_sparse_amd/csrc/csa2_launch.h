@@ -30,6 +30,8 @@ struct IndexScoreArgs {
     int64_t block_max_stride;
 };
 hipError_t launch_index_score(const KvView& kv, const IndexScoreArgs& a, hipStream_t st);
+// rows 0 .. n_rows-1 all read request `req` (full scan only; a.req is not read)
+hipError_t launch_index_score_shared(const KvView& kv, const IndexScoreArgs& a, int req, hipStream_t st);
 
 struct TopkArgs {
     const float* keys;

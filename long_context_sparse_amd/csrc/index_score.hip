@@ -47,13 +47,18 @@ constexpr int IS_TILES = CSA2_IS_TILES;              // 16-key tiles per batch
 constexpr int IS_ITERS = CSA2_IS_ITERS;              // batches per wave (even)
 constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16 * IS_ITERS;   // columns per workgroup
 
-struct QShared {
+// One row's indexer query in MXFP4, its weights and the exactness-guard bounds.
+struct QRow {
     uint8_t codes[16][64];
     uint8_t scales[16][4];
     float w[16];
     int spread;   // max over real heads of (max - min) block scale code
     int smin;     // min block scale code over real heads
     int smax;     // max block scale code over real heads
+};
+
+struct QShared {
+    QRow q;
     int n_fix;    // queued 8-blocks that need the exact path
     int fix[IS_CHUNK];
 };
@@ -121,8 +126,10 @@ __device__ float round_pow2_sum4(const int* S, const int* E) {
     return neg ? -r : r;
 }
 
-// Exact score of one key (used where the MFMA exactness guard fails).
-__device__ float exact_key_score(const QShared& qs, int n_heads, const uint8_t* kc, const uint8_t* ks) {
+// Exact score of one key (used where the MFMA exactness guard fails) against
+// one row's quantised query: codes [16][64], scales [16][4], weights [16].
+__device__ float exact_key_score(const uint8_t (*qcodes)[64], const uint8_t (*qscales)[4], const float* qw,
+                                 int n_heads, const uint8_t* kc, const uint8_t* ks) {
     uint8_t key[64];
     for (int i = 0; i < 64; ++i) key[i] = kc[i];
     int kscale[4];
@@ -133,14 +140,14 @@ __device__ float exact_key_score(const QShared& qs, int n_heads, const uint8_t* 
         for (int g = 0; g < 4; ++g) {
             int s = 0;
             for (int j = 0; j < 16; ++j) {
-                const uint32_t qb = qs.codes[h][16 * g + j], kb = key[16 * g + j];
+                const uint32_t qb = qcodes[h][16 * g + j], kb = key[16 * g + j];
                 s += e2m1_x2(qb & 15u) * e2m1_x2(kb & 15u) + e2m1_x2(qb >> 4) * e2m1_x2(kb >> 4);
             }
             S[g] = s;
-            E[g] = (int)qs.scales[h][g] + kscale[g] - 256;
+            E[g] = (int)qscales[h][g] + kscale[g] - 256;
         }
         const float d = round_pow2_sum4(S, E);
-        acc = fmaf(qs.w[h], d > 0.0f ? d : 0.0f, acc);
+        acc = fmaf(qw[h], d > 0.0f ? d : 0.0f, acc);
     }
     return acc == 0.0f ? 0.0f : acc;
 }
@@ -177,7 +184,7 @@ __device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, 
 // Quantise the row's indexer query to MXFP4 (one lane per (head, block) =
 // exactly the MFMA A-operand layout) and gather the exactness-guard bounds.
 template <bool QBF16>
-__device__ __forceinline__ void prep_query(QShared& qs, const QRaw& r, const float* w, int row, int n_heads) {
+__device__ __forceinline__ void prep_query(QRow& qs, const QRaw& r, const float* w, int row, int n_heads) {
     const int l = threadIdx.x & 63;
     const int m = l & 15, g = l >> 4;
     uint32_t words[4] = {0, 0, 0, 0};
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     if (wave == 0) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads);      // issued before the keys
     KeyBatch A, B;
     load_batch<POOL>(kv, req, pool, nv, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
-    if (wave == 0) prep_query<QBF16>(qs, qraw, a.w, row, a.n_heads);
+    if (wave == 0) prep_query<QBF16>(qs.q, qraw, a.w, row, a.n_heads);
     if (threadIdx.x == 0) qs.n_fix = 0;
     __syncthreads();
 
@@ -318,13 +325,13 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
         const int h = 4 * k + (n & 3);
-        const uint4 v = *(const uint4*)&qs.codes[h][16 * lg];
+        const uint4 v = *(const uint4*)&qs.q.codes[h][16 * lg];
         Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sa[k] = qs.scales[h][lg];
+        sa[k] = qs.q.scales[h][lg];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.w[4 * k + i];   // 0 above n_heads
+        for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.q.w[4 * k + i];   // 0 above n_heads
     }
-    const int qspread = qs.spread, qmin = qs.smin, qmax = qs.smax;
+    const int qspread = qs.q.spread, qmin = qs.q.smin, qmax = qs.q.smax;
     float* srow = a.scores ? a.scores + (int64_t)row * a.scores_stride : nullptr;
     float* brow = (!POOL && a.block_max) ? a.block_max + (int64_t)row * a.block_max_stride : nullptr;
     const int nv8 = (nv + 7) & ~7;
@@ -412,12 +419,184 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             float v = -INFINITY;
             if (pos < nv) {
                 const int64_t e = entry_of(kv, req, pos);
-                v = exact_key_score(qs, a.n_heads, kv.idx_codes + e * 64, kv.idx_scales + e * 4);
+                v = exact_key_score(qs.q.codes, qs.q.scales, qs.q.w, a.n_heads, kv.idx_codes + e * 64, kv.idx_scales + e * 4);
             }
             if (srow) srow[col] = v;                   // col == pos in a full scan
             bm = fmaxf(bm, v);
         }
         if (brow) brow[c8 >> 3] = bm;
+    }
+}
+
+// ---------------------------------------------------------------- rows of one request
+// Chunked prefill: the query rows of one request score the same keys.  A
+// workgroup takes RG groups of 4 rows and the columns of SR_ITERS batches per
+// wave; every 16-key tile is loaded once and scored against all of its rows.
+// MFMA k of row group rg carries row 4 rg + n/4, head 4k + n%4 on its M row n,
+// so lane (n, lg) receives heads 4k .. 4k+3 of (row 4 rg + lg, key n) and
+// folds them in the same order as the single-row kernel: the scores are the
+// same bits.  Rows past the end of the call and columns past a row's visible
+// count are computed but never stored.
+constexpr int SR_ITERS = 16;                           // batches per wave (even)
+constexpr int SR_CHUNK = IS_WAVES * IS_TILES * 16 * SR_ITERS;
+
+template <int RG>
+struct SharedRowsLds {
+    QRow q[4 * RG];
+    int n_fix;
+    int fix_col[4 * RG * SR_CHUNK / 8];               // first column of a queued (row, 8-block)
+    uint8_t fix_row[4 * RG * SR_CHUNK / 8];           // its row within the workgroup
+};
+
+template <bool QBF16, int NM, int RG>
+__global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvView kv, IndexScoreArgs a, int req) {
+    constexpr int R = 4 * RG;
+    __shared__ SharedRowsLds<RG> sh;
+    const int r0 = (int)blockIdx.y * R;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const int n = l & 15, lg = l >> 4;
+    // visible counts of the lane's rows (4 rg + lg); the workgroup scans up to the largest
+    int nvl[RG];
+    int ncols = 0;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        const int r = r0 + 4 * rg + lg;
+        nvl[rg] = r < a.n_rows ? max(0, min(a.n_vis[r], a.max_vis)) : 0;
+        ncols = max(ncols, nvl[rg]);
+    }
+    ncols = max(ncols, __shfl_xor(ncols, 16, 64));
+    ncols = max(ncols, __shfl_xor(ncols, 32, 64));
+    ncols = __builtin_amdgcn_readfirstlane(ncols);
+    if (64 * IS_WAVES * (int)blockIdx.x >= ncols) return;   // uniform over the workgroup
+    const int Gx = gridDim.x;
+    const int wbase = 64 * (IS_WAVES * (int)blockIdx.x + wave);
+    constexpr int TSTRIDE = 16;
+    const int BSTRIDE = 64 * IS_WAVES * Gx;
+
+    KeyBatch A, B;
+    load_batch<false>(kv, req, nullptr, ncols, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
+    {
+        // wave w quantises rows w, w + 4, ...; rows past the end copy the last row
+        constexpr int PER = R / IS_WAVES;
+        QRaw qraw[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) load_query<QBF16>(qraw[j], a.q_idx, min(r0 + wave + IS_WAVES * j, a.n_rows - 1), a.n_heads);
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            prep_query<QBF16>(sh.q[wave + IS_WAVES * j], qraw[j], a.w, min(r0 + wave + IS_WAVES * j, a.n_rows - 1), a.n_heads);
+    }
+    if (threadIdx.x == 0) sh.n_fix = 0;
+    __syncthreads();
+
+    i32x8 Aq[RG][NM];
+    int sa[RG][NM];
+    float wl[RG][4 * NM];
+    int qsp[RG], qmn[RG], qmx[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            const QRow& q = sh.q[4 * rg + (n >> 2)];
+            const int h = 4 * k + (n & 3);
+            const uint4 v = *(const uint4*)&q.codes[h][16 * lg];
+            Aq[rg][k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            sa[rg][k] = q.scales[h][lg];
+        }
+        const QRow& own = sh.q[4 * rg + lg];
+#pragma unroll
+        for (int h = 0; h < 4 * NM; ++h) wl[rg][h] = own.w[h];   // 0 above n_heads
+        qsp[rg] = own.spread;
+        qmn[rg] = own.smin;
+        qmx[rg] = own.smax;
+    }
+
+    auto compute = [&](const KeyBatch& kb, int col_base) {
+#pragma unroll
+        for (int t = 0; t < IS_TILES; ++t) {
+            const int col0 = col_base + TSTRIDE * t;
+            if (col0 >= ncols) break;
+            const i32x8 Bk = {(int)kb.code[t].x, (int)kb.code[t].y, (int)kb.code[t].z, (int)kb.code[t].w, 0, 0, 0, 0};
+            const uint32_t sd = kb.scl[t];
+            const int sb = (int)((sd >> (8 * lg)) & 0xFFu);
+            f32x4 d[RG][NM];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int k = 0; k < NM; ++k) {
+                    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    d[rg][k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[rg][k], Bk, z, 4, 4, 0, sa[rg][k], 0, sb);
+                }
+            // pin every MFMA in wave-uniform control flow (see the single-row kernel)
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int k = 0; k < NM; ++k) asm volatile("" : "+a"(d[rg][k]));
+            const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
+            const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
+            const int col = col0 + n;
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const bool ok = (kmax - kmin + qsp[rg] <= 9) && (qmn[rg] + kmin >= 136) && (qmx[rg] + kmax <= 356);
+                float acc = 0.0f;
+#pragma unroll
+                for (int k = 0; k < NM; ++k)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = fmaf(wl[rg][4 * k + i], d[rg][k][i] > 0.0f ? d[rg][k][i] : 0.0f, acc);
+                acc = (acc == 0.0f) ? 0.0f : acc;
+                const bool vis = col < nvl[rg];
+                const float val = vis ? acc : -INFINITY;
+                const int rl = 4 * rg + lg;                   // the lane's row within the workgroup
+                // an 8-block with an unguarded visible key is queued once (lanes 8j + 7)
+                if (__builtin_expect(__any(vis && !ok), 0)) {
+                    int bad = (vis && !ok) ? 1 : 0;
+                    bad |= __builtin_amdgcn_update_dpp(0, bad, 0x111, 0xF, 0xF, false);   // row_shr:1
+                    bad |= __builtin_amdgcn_update_dpp(0, bad, 0x112, 0xF, 0xF, false);   // row_shr:2
+                    bad |= __builtin_amdgcn_update_dpp(0, bad, 0x114, 0xF, 0xF, false);   // row_shr:4
+                    if ((n & 7) == 7 && bad) {
+                        const int slot = atomicAdd(&sh.n_fix, 1);
+                        sh.fix_col[slot] = col & ~7;
+                        sh.fix_row[slot] = (uint8_t)rl;
+                    }
+                }
+                const int64_t r = r0 + rl;
+                const bool row_ok = r < a.n_rows;
+                if (a.scores && row_ok && col < ((nvl[rg] + 7) & ~7)) a.scores[r * a.scores_stride + col] = val;
+                if (a.block_max) {
+                    float bm = dpp_row_shr_max(val, 1);
+                    bm = dpp_row_shr_max(bm, 2);
+                    bm = dpp_row_shr_max(bm, 4);
+                    if (row_ok && (n & 7) == 7 && (col & ~7) < nvl[rg]) a.block_max[r * a.block_max_stride + (col >> 3)] = bm;
+                }
+            }
+        }
+    };
+
+    // the next batch is always requested (past the end its columns are clamped
+    // into range and not used), so every wait names one batch exactly
+    for (int b = 0; b < SR_ITERS; b += 2) {
+        const int c_a = wbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
+        load_batch<false>(kv, req, nullptr, ncols, ncols, c_b, TSTRIDE, n, lg, B);
+        compute(A, c_a);
+        load_batch<false>(kv, req, nullptr, ncols, ncols, c_b + BSTRIDE, TSTRIDE, n, lg, A);
+        compute(B, c_b);
+    }
+
+    // ---- exact path for the queued (row, 8-block)s
+    __syncthreads();
+    const int nfix = sh.n_fix;
+    for (int i = threadIdx.x; i < nfix; i += blockDim.x) {
+        const int c8 = sh.fix_col[i], rl = sh.fix_row[i];
+        const int64_t r = r0 + rl;
+        const int nv = max(0, min(a.n_vis[r], a.max_vis));
+        const QRow& q = sh.q[rl];
+        float bm = -INFINITY;
+        for (int j = 0; j < 8 && c8 + j < nv; ++j) {
+            const int64_t e = entry_of(kv, req, c8 + j);
+            const float v = exact_key_score(q.codes, q.scales, q.w, a.n_heads, kv.idx_codes + e * 64, kv.idx_scales + e * 4);
+            if (a.scores) a.scores[r * a.scores_stride + c8 + j] = v;
+            bm = fmaxf(bm, v);
+        }
+        if (a.block_max) a.block_max[r * a.block_max_stride + (c8 >> 3)] = bm;
     }
 }
 
@@ -429,6 +608,27 @@ static void launch_nm(int nm, dim3 grid, dim3 block, hipStream_t st, const KvVie
         case 3: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 3>), grid, block, 0, st, kv, a); break;
         default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4>), grid, block, 0, st, kv, a); break;
     }
+}
+
+template <bool QBF16>
+static void launch_shared_nm(int nm, dim3 grid, dim3 block, hipStream_t st, const KvView& kv, const IndexScoreArgs& a,
+                             int req) {
+    switch (nm) {
+        case 1: hipLaunchKernelGGL((index_score_shared_kernel<QBF16, 1, 4>), grid, block, 0, st, kv, a, req); break;
+        case 2: hipLaunchKernelGGL((index_score_shared_kernel<QBF16, 2, 4>), grid, block, 0, st, kv, a, req); break;
+        case 3: hipLaunchKernelGGL((index_score_shared_kernel<QBF16, 3, 2>), grid, block, 0, st, kv, a, req); break;
+        default: hipLaunchKernelGGL((index_score_shared_kernel<QBF16, 4, 2>), grid, block, 0, st, kv, a, req); break;
+    }
+}
+
+hipError_t launch_index_score_shared(const KvView& kv, const IndexScoreArgs& a, int req, hipStream_t st) {
+    const int nm = (a.n_heads + 3) / 4;
+    const int rows_per_wg = nm <= 2 ? 16 : 8;
+    const dim3 grid((unsigned)((a.max_vis + SR_CHUNK - 1) / SR_CHUNK), (unsigned)((a.n_rows + rows_per_wg - 1) / rows_per_wg)),
+        block(IS_WAVES * 64);
+    if (a.q_bf16) launch_shared_nm<true>(nm, grid, block, st, kv, a, req);
+    else launch_shared_nm<false>(nm, grid, block, st, kv, a, req);
+    return hipGetLastError();
 }
 
 hipError_t launch_index_score(const KvView& kv, const IndexScoreArgs& a, hipStream_t st) {

@@ -25,9 +25,10 @@ import torch
 import synth
 from synth.configs import Config
 
-from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_index_score,
-               csa2_attn_workspace_size, csa2_pack_kv, csa2_select_full, csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge,
-               csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform, make_kv, make_rows)
+from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_attn_workspace_size, csa2_index_score,
+               csa2_index_score_shared, csa2_pack_kv, csa2_select_full, csa2_select_topk, csa2_sparse_attn,
+               csa2_sparse_swa_attn, csa2_swa_merge, csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform,
+               make_kv, make_rows)
 
 GEN_CHUNK = 1 << 20   # entries generated per chunk
 
@@ -193,8 +194,13 @@ class Workload:
     def run_full(self, layer: "Layer", kv, stream=None, marks=None):
         m = self._mark
         m(marks, "index_score", 0)
-        csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.scores, block_max=self.block_max,
-                         stream=stream)
+        if self.cfg.mode == "prefill":
+            # the chunk's rows are tokens of request 0: one scan of its keys serves them all
+            csa2_index_score_shared(kv, self.rows, 0, layer.q_idx, layer.w, scores=self.scores,
+                                    block_max=self.block_max, stream=stream)
+        else:
+            csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.scores, block_max=self.block_max,
+                             stream=stream)
         m(marks, "index_score", 1)
         if self.cfg.mode == "prefill":
             m(marks, "select_positions", 0)

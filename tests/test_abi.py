@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lib.EXPORTS)
-    assert L.csa2_abi_version() == 3
+    assert L.csa2_abi_version() == 4
 
 
 def _kv(**over):
@@ -113,6 +113,25 @@ def test_index_score_rejects():
     # pool mode needs pool_count and forbids block_max
     assert f(B(kv), B(rows), 256, 0, 8, 256, 256, 2048, None, 256, 16384, None, 0, None) == 1
     assert f(B(kv), B(rows), 256, 0, 8, 256, 256, 2048, 256, 256, 16384, 256, 2048, None) == 2
+
+
+def test_index_score_shared_rejects():
+    """Argument errors of the shared-request scan return before any launch
+    (every call here is invalid, so nothing is enqueued)."""
+    L = lib.lib()
+    kv, rows = _kv(), _rows()
+    f = L.csa2_index_score_shared
+    B = ctypes.byref
+    assert f(None, B(rows), 0, 256, 0, 8, 256, 256, 104, None, 0, None) == 1            # no cache
+    assert f(B(kv), None, 0, 256, 0, 8, 256, 256, 104, None, 0, None) == 1              # no rows
+    assert f(B(kv), B(rows), -1, 256, 0, 8, 256, 256, 104, None, 0, None) == 3          # req < 0
+    assert f(B(kv), B(rows), 0, 256, 0, 17, 256, 256, 104, None, 0, None) == 5          # 17 heads
+    assert f(B(kv), B(rows), 0, 256, 0, 8, 256, 256, 99, None, 0, None) == 2            # stride
+    assert f(B(kv), B(rows), 0, 256, 0, 8, 256, None, 0, None, 0, None) == 1            # no output
+    assert f(B(kv), B(rows), 0, 300, 0, 8, 256, 256, 104, None, 0, None) == 4           # q alignment
+    assert f(B(kv), B(rows), 0, None, 0, 8, 256, 256, 104, None, 0, None) == 1          # no query
+    assert f(B(kv), B(_rows(n=70000)), 0, 256, 0, 8, 256, 256, 104, None, 0, None) == 3
+    assert L.csa2_last_error()
 
 
 def test_attn_rejects():

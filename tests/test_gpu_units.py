@@ -151,6 +151,69 @@ def test_index_score_full_exact(Hi, spread):
         assert np.all(Bm[r, nb:] == 7.0)
 
 
+@pytest.mark.parametrize("Hi,spread,paged", [(1, False, False), (3, True, False), (8, False, False),
+                                              (8, True, True), (16, True, False)])
+def test_index_score_shared_exact(Hi, spread, paged):
+    """Query rows of one request (a chunked prefill): the shared scan equals
+    the oracle row by row, bit for bit, and the per-row scan too, over
+    ragged visible counts (none, fewer than 8, a partial block, the whole
+    context), 37 rows (partial row groups of 16 and of 8), a request other
+    than the first, wide exponent spreads (the exact path) and a paged cache."""
+    n_req, n, req = 2, 6000, 1
+    n_rows = 37
+    keys, _, _, kc, ks = _score_setup(n_req, n, Hi, spread=spread, zero_groups=spread)
+    q = RNG.standard_normal((n_rows, Hi, 128)).astype(np.float32)
+    if spread:
+        q *= (2.0 ** RNG.integers(-8, 8, (n_rows, Hi, 4))).repeat(32, axis=2).astype(np.float32)
+    q = bf16(q).float().numpy()
+    w = RNG.random((n_rows, Hi)).astype(np.float32)
+    w[:, ::3] *= -1
+    n_vis = RNG.integers(0, n + 1, n_rows).astype(np.int32)
+    n_vis[:8] = [0, 3, 8, 16, 17, 4099, n - 1, n]
+    if paged:
+        P = 64
+        n_pages = n // P + 1
+        table = RNG.permutation(n_req * n_pages).reshape(n_req, n_pages).astype(np.int32)
+        kc2 = np.zeros((n_req * n_pages * P, 64), np.uint8)
+        ks2 = np.zeros((n_req * n_pages * P, 4), np.uint8)
+        for r in range(n_req):
+            for p in range(n_pages):
+                m = min(P, n - p * P)
+                if m > 0:
+                    kc2[table[r, p] * P:table[r, p] * P + m] = kc[r * n + p * P:r * n + p * P + m]
+                    ks2[table[r, p] * P:table[r, p] * P + m] = ks[r * n + p * P:r * n + p * P + m]
+        kv = lib.make_kv(idx_codes=T(kc2), idx_scales=T(ks2), n_slots=len(kc2), page_entries=P, page_table=T(table))
+    else:
+        kv = lib.make_kv(idx_codes=T(kc), idx_scales=T(ks), n_slots=n_req * n, req_stride=n)
+    nv = T(n_vis)
+    nv8 = (n + 7) // 8 * 8
+    out = []
+    for shared in (True, False):
+        scores = torch.full((n_rows, nv8 + 8), 7.0, dtype=torch.float32, device=DEV)
+        bmax = torch.full((n_rows, nv8 // 8 + 4), 7.0, dtype=torch.float32, device=DEV)
+        if shared:
+            rows = lib.make_rows(None, nv, n)
+            lib.csa2_index_score_shared(kv, rows, req, T(q), T(w), scores=scores, block_max=bmax)
+        else:
+            rows = lib.make_rows(T(np.full(n_rows, req, np.int32)), nv, n)
+            lib.csa2_index_score(kv, rows, T(q), T(w), scores=scores, block_max=bmax)
+        torch.cuda.synchronize()
+        out.append((scores.cpu().numpy(), bmax.cpu().numpy()))
+    (S, Bm), (S1, Bm1) = out
+    assert np.array_equal(S, S1) and np.array_equal(Bm, Bm1)
+    qc, qs = oracle.quant_query(q.reshape(-1, 128))
+    for r in range(n_rows):
+        m = int(n_vis[r])
+        ref = oracle.index_score(qc[r * Hi:(r + 1) * Hi], qs[r * Hi:(r + 1) * Hi], w[r],
+                                 kc[req * n:req * n + m], ks[req * n:req * n + m])
+        assert np.array_equal(S[r, :m], ref), (r, m, np.nonzero(S[r, :m] != ref)[0][:5])
+        m8 = (m + 7) // 8 * 8
+        assert np.all(np.isneginf(S[r, m:m8])) and np.all(S[r, m8:] == 7.0), r
+        nb = (m + 7) // 8
+        assert np.array_equal(Bm[r, :nb], oracle.block_max(ref)), r
+        assert np.all(Bm[r, nb:] == 7.0), r
+
+
 def test_index_score_bf16_query_and_fp32_agree():
     keys, q, w, kc, ks = _score_setup(1, 2048, 8)
     kv = lib.make_kv(idx_codes=T(kc), idx_scales=T(ks), n_slots=2048, req_stride=2048)
