@@ -277,6 +277,13 @@ __device__ __forceinline__ void load_batch(const KvView& kv, int req, const int3
     }
 }
 
+// max(x, +0) for finite x as one integer max on the bits: a negative float or
+// -0 reads as a negative integer and becomes +0 (the float max would first
+// quiet its operand, one more instruction per head and key).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// max with the value of lane l - shift of the same 16-lane row (scores are
+// never NaN, so the plain instruction is used without quieting its operands)
 __device__ __forceinline__ float dpp_row_shr_max(float v, int shift) {
     int src = __builtin_bit_cast(int, v);
     int sh;
@@ -285,7 +292,9 @@ __device__ __forceinline__ float dpp_row_shr_max(float v, int shift) {
         case 2: sh = __builtin_amdgcn_update_dpp(src, src, 0x112, 0xF, 0xF, false); break;
         default: sh = __builtin_amdgcn_update_dpp(src, src, 0x114, 0xF, 0xF, false); break;
     }
-    return fmaxf(v, __builtin_bit_cast(float, sh));
+    float r;
+    asm volatile("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(__builtin_bit_cast(float, sh)));
+    return r;
 }
 
 template <bool QBF16, bool POOL, int NM>
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
 #pragma unroll
             for (int k = 0; k < NM; ++k)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = fmaf(wl[4 * k + i], d[k][i] > 0.0f ? d[k][i] : 0.0f, acc);
+                for (int i = 0; i < 4; ++i) acc = fmaf(wl[4 * k + i], relu_bits(d[k][i]), acc);
             acc = (acc == 0.0f) ? 0.0f : acc;
             const int col = col0 + n;
             const bool in_cols = col < ncols;
@@ -541,7 +550,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvVie
 #pragma unroll
                 for (int k = 0; k < NM; ++k)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = fmaf(wl[rg][4 * k + i], d[rg][k][i] > 0.0f ? d[rg][k][i] : 0.0f, acc);
+                    for (int i = 0; i < 4; ++i) acc = fmaf(wl[rg][4 * k + i], relu_bits(d[rg][k][i]), acc);
                 acc = (acc == 0.0f) ? 0.0f : acc;
                 const bool vis = col < nvl[rg];
                 const float val = vis ? acc : -INFINITY;
