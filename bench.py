@@ -191,7 +191,7 @@ def main():
 
     # ---- per-kernel breakdown (separate, untimed pass)
     names = ["index_score", "select", "attention"]
-    if cfg.mode != "full" and cfg.mode != "mixed":
+    if cfg.mode == "reindex":
         names = ["index_score", "select_positions", "attention"]
     per = {n: [] for n in names}
     for i in range(20):

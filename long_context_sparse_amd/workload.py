@@ -157,6 +157,10 @@ class Workload:
             self.pool = torch.empty((self.n_rows, 2048), dtype=torch.int32, device=dev)
             self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
             self.pool_scores = torch.empty((self.n_rows, 16384), dtype=torch.float32, device=dev)
+        elif mode == "prefill":
+            # the selection's 512-block pool (an intermediate of the prefill step)
+            self.pool = torch.empty((self.n_rows, 512), dtype=torch.int32, device=dev)
+            self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
         ws = csa2_attn_workspace_size(self.n_rows, cfg.heads)
         self.workspace = torch.empty(max(ws, 256) // 4, dtype=torch.float32, device=dev) if ws else None
         if mode == "reindex":
@@ -203,10 +207,14 @@ class Workload:
                              stream=stream)
         m(marks, "index_score", 1)
         if self.cfg.mode == "prefill":
-            m(marks, "select_positions", 0)
-            csa2_select_topk(self.scores, 512, layer.idx, layer.idx_count, n_cols=self.n_vis,
-                             max_cols=self.max_vis, stream=stream)
-            m(marks, "select_positions", 1)
+            # a row's top-512 positions lie in its 512 best blocks (a block ranked
+            # above a top-512 position's block holds a distinct better position),
+            # so the fused selection with a pool of 512 blocks returns exactly
+            # the top-512 of all visible scores
+            m(marks, "select", 0)
+            csa2_select_full(self.block_max, self.scores, self.n_vis, self.max_vis, self.pool, self.pool_count,
+                             layer.idx, layer.idx_count, n_pool_blocks=512, k=512, stream=stream)
+            m(marks, "select", 1)
         elif self.two_call_select:
             m(marks, "select_blocks", 0)
             csa2_select_topk(self.block_max, 2048, self.pool, self.pool_count, n_cols=self.n_vis, cols_div=8,
