@@ -151,23 +151,27 @@ def test_index_score_full_exact(Hi, spread):
         assert np.all(Bm[r, nb:] == 7.0)
 
 
-@pytest.mark.parametrize("Hi,spread,paged", [(1, False, False), (3, True, False), (8, False, False),
-                                              (8, True, True), (16, True, False)])
-def test_index_score_shared_exact(Hi, spread, paged):
+@pytest.mark.parametrize("Hi,spread,paged,qdt", [(1, False, False, "bf16"), (3, True, False, "bf16"),
+                                                  (8, False, False, "bf16"), (8, True, True, "bf16"),
+                                                  (16, True, False, "bf16"), (8, True, False, "f32")])
+def test_index_score_shared_exact(Hi, spread, paged, qdt):
     """Query rows of one request (a chunked prefill): the shared scan equals
     the oracle row by row, bit for bit, and the per-row scan too, over
     ragged visible counts (none, fewer than 8, a partial block, the whole
     context), 37 rows (partial row groups of 16 and of 8), a request other
-    than the first, wide exponent spreads (the exact path) and a paged cache."""
+    than the first, wide exponent spreads (the exact path), a paged cache, and
+    bf16 and fp32 queries (both quantised to MXFP4 on the way in)."""
     n_req, n, req = 2, 6000, 1
     n_rows = 37
     keys, _, _, kc, ks = _score_setup(n_req, n, Hi, spread=spread, zero_groups=spread)
     q = RNG.standard_normal((n_rows, Hi, 128)).astype(np.float32)
     if spread:
         q *= (2.0 ** RNG.integers(-8, 8, (n_rows, Hi, 4))).repeat(32, axis=2).astype(np.float32)
-    q = bf16(q).float().numpy()
+    if qdt == "bf16":
+        q = bf16(q).float().numpy()
     w = RNG.random((n_rows, Hi)).astype(np.float32)
     w[:, ::3] *= -1
+    qd = T(q).to(torch.bfloat16) if qdt == "bf16" else T(q)    # bf16: the values are bf16-exact
     n_vis = RNG.integers(0, n + 1, n_rows).astype(np.int32)
     n_vis[:8] = [0, 3, 8, 16, 17, 4099, n - 1, n]
     if paged:
@@ -193,10 +197,10 @@ def test_index_score_shared_exact(Hi, spread, paged):
         bmax = torch.full((n_rows, nv8 // 8 + 4), 7.0, dtype=torch.float32, device=DEV)
         if shared:
             rows = lib.make_rows(None, nv, n)
-            lib.csa2_index_score_shared(kv, rows, req, T(q), T(w), scores=scores, block_max=bmax)
+            lib.csa2_index_score_shared(kv, rows, req, qd, T(w), scores=scores, block_max=bmax)
         else:
             rows = lib.make_rows(T(np.full(n_rows, req, np.int32)), nv, n)
-            lib.csa2_index_score(kv, rows, T(q), T(w), scores=scores, block_max=bmax)
+            lib.csa2_index_score(kv, rows, qd, T(w), scores=scores, block_max=bmax)
         torch.cuda.synchronize()
         out.append((scores.cpu().numpy(), bmax.cpu().numpy()))
     (S, Bm), (S1, Bm1) = out
