@@ -335,8 +335,58 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     auto bemit = [&](int col, uint32_t slot, uint32_t key) {
         sh.pool[slot] = (key & thr_mask) >= thr_val ? col : (int32_t)((uint32_t)col | 0x80000000u);
     };
-    const uint32_t np = nb <= TK_SWEEP ? select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val)
-                                       : select_row<0>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
+    uint32_t np;
+    if (nb <= TK_SWEEP) {
+        np = select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
+    } else if (nb <= 8 * TK_SWEEP) {
+        // Longer rows, in registers: the top n_pool blocks lie in the top
+        // n_pool super-blocks of 8 blocks ranked by their maximum (a super-
+        // block ranked above the one of a top block holds a distinct block
+        // ranked above it: its maximum, on equal values with a lower id).
+        // Thread t takes super-blocks 16t .. 16t+15 (blocks 128t .. 128t+127).
+        const int nsb = (nb + 7) >> 3;
+        auto skeys = [&](int, uint32_t* u) {
+#pragma unroll
+            for (int j = 0; j < TK_ITEMS / 2; ++j) {
+                uint32_t b[TK_ITEMS];
+                load_cols(brow, nb, 128 * (int)threadIdx.x + 16 * j, b);
+                uint32_t m0 = 0u, m1 = 0u;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { m0 = max(m0, b[i]); m1 = max(m1, b[8 + i]); }
+                u[2 * j] = m0;
+                u[2 * j + 1] = m1;
+                // at most 64 block maxima in flight per thread (all 128 would spill)
+                if (j == TK_ITEMS / 4 - 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto semit = [&](int col, uint32_t slot, uint32_t) { sh.pool[slot] = col; };
+        uint32_t s_mask, s_val;
+        const uint32_t nsp = select_row<1>(sh, nsb, a.n_pool, skeys, semit, 0u, s_mask, s_val);
+        __syncthreads();                              // the chosen super-blocks, ascending, are in sh.pool
+        // candidate column c is block 8 * super[c / 8] + c % 8; thread t's
+        // columns belong to super-blocks 2t and 2t + 1 of the list (read here,
+        // before the selection below rewrites sh.pool at its end)
+        const int sb0 = 2 * (int)threadIdx.x < (int)nsp ? sh.pool[2 * threadIdx.x] : -1;
+        const int sb1 = 2 * (int)threadIdx.x + 1 < (int)nsp ? sh.pool[2 * threadIdx.x + 1] : -1;
+        auto ckeys = [&](int, uint32_t* u) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int sb = h ? sb1 : sb0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int blk = 8 * sb + i;
+                    u[8 * h + i] = (sb >= 0 && blk < nb) ? order_key(brow[blk]) : 0u;
+                }
+            }
+        };
+        auto cemit = [&](int col, uint32_t slot, uint32_t key) {
+            const int blk = 8 * ((col & 8) ? sb1 : sb0) + (col & 7);
+            sh.pool[slot] = (key & thr_mask) >= thr_val ? blk : (int32_t)((uint32_t)blk | 0x80000000u);
+        };
+        np = select_row<1>(sh, 8 * (int)nsp, a.n_pool, ckeys, cemit, (uint32_t)a.k, thr_mask, thr_val);
+    } else {
+        np = select_row<0>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
+    }
     __syncthreads();                                  // the pool is complete in LDS
 
     // ---- positions: column c is position 8 * pool[c/8] + c%8 (-inf past n_vis)
