@@ -64,7 +64,7 @@ typedef enum {
     CSA2_ERR_SHAPE = 2,       /* inconsistent sizes or strides */
     CSA2_ERR_RANGE = 3,       /* a size or count outside its allowed range */
     CSA2_ERR_ALIGN = 4,       /* a pointer or stride is not aligned as required */
-    CSA2_ERR_UNSUPPORTED = 5, /* a head count or dtype this build does not handle */
+    CSA2_ERR_UNSUPPORTED = 5, /* a head count or dtype the library does not handle */
     CSA2_ERR_WORKSPACE = 6,   /* reserved: no entry point of this version returns it */
     CSA2_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
 } csa2_status;
