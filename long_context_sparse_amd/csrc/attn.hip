@@ -40,6 +40,7 @@
 //     scaled conversion instructions (V_CVT_SCALEF32_PK_F16_FP4 / _FP8) apply
 //     the power of two as they convert.  The scalings are undone on the fp32
 //     scores and outputs.
+#include <atomic>
 #include <type_traits>
 
 #include "csa2_device.h"
@@ -520,14 +521,21 @@ size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits) {
     return (size_t)n_rows * n_heads * n_splits * (512 + 2) * sizeof(float);
 }
 
-static bool g_attr_set = false;
+// The kernels' dynamic LDS above 64 KB is allowed once per device (the flag
+// per device is set only after both attributes succeeded; a race between two
+// host threads on a new device repeats the same idempotent calls).
+constexpr int AT_MAX_DEVICES = 64;
+static std::atomic<bool> g_attr_set[AT_MAX_DEVICES];
 
 static hipError_t set_lds_attrs() {
-    if (g_attr_set) return hipSuccess;
-    hipError_t e;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < AT_MAX_DEVICES;
+    if (cached && g_attr_set[dev].load(std::memory_order_acquire)) return hipSuccess;
     if ((e = hipFuncSetAttribute((const void*)attn_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
     if ((e = hipFuncSetAttribute((const void*)attn_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
-    g_attr_set = true;
+    if (cached) g_attr_set[dev].store(true, std::memory_order_release);
     return hipSuccess;
 }
 
