@@ -61,6 +61,9 @@ struct QShared {
     QRow q;
     int n_fix;    // queued 8-blocks that need the exact path
     int fix[IS_CHUNK];
+    // pool mode: the pool entries of this workgroup's blocks (batch b of every
+    // wave: slots 32 b .. 32 b + 31) and the row's entry 0 (slot IS_CHUNK / 8)
+    int pool_l[IS_CHUNK / 8 + 1];
 };
 
 // Doubled E2M1 value of a code, as an integer in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}.
@@ -246,9 +249,11 @@ typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 // count outstanding loads exactly and never waits on a prefetched batch).
 // Full scan: a 16-column tile lies inside one page, so its page-table entry
 // is one wave-uniform load.
+// Pool mode: the pool entry of a column comes from global memory (lpool NULL)
+// or from the workgroup's LDS copy (slots lbase + block mod 32).
 template <bool POOL>
-__device__ __forceinline__ void load_batch(const KvView& kv, int req, const int32_t* pool, int nv, int ncols,
-                                           int col_base, int tstride, int n, int lg, KeyBatch& kb) {
+__device__ __forceinline__ void load_batch(const KvView& kv, int req, const int32_t* pool, const int* lpool, int lbase,
+                                           int nv, int ncols, int col_base, int tstride, int n, int lg, KeyBatch& kb) {
 #pragma unroll
     for (int t = 0; t < IS_TILES; ++t) {
         const int col0 = col_base + tstride * t;         // wave-uniform
@@ -256,8 +261,10 @@ __device__ __forceinline__ void load_batch(const KvView& kv, int req, const int3
         if (POOL) {
             const int c0 = col0 < ncols ? col0 : 0;      // column 0 is always valid when ncols > 0
             const int col = col0 + n < ncols ? col0 + n : c0;
-            int ld = 8 * pool[col >> 3] + (col & 7);
-            if (ld >= nv) ld = 8 * pool[col >> 3];       // a visible position of the same block
+            const int pe = !lpool ? pool[col >> 3]
+                                  : lpool[col0 < ncols ? lbase + ((col >> 3) & 31) : IS_CHUNK / 8];
+            int ld = 8 * pe + (col & 7);
+            if (ld >= nv) ld = 8 * pe;                   // a visible position of the same block
             e = entry_of(kv, req, ld);
         } else {
             const int t0 = col0 < ncols ? col0 : 0;
@@ -310,6 +317,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     // compact run of consecutive batches.
     const int Gx = gridDim.x;
     static_assert(IS_TILES == 4, "a batch is one tile per lane group");
+    static_assert(8 * IS_WAVES == 32 && IS_CHUNK / 8 <= IS_WAVES * 64, "a batch spans 32 blocks of the LDS pool copy");
     if (64 * IS_WAVES * (int)blockIdx.x >= ncols) return;   // uniform over the workgroup
     const int req = a.req[row];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -322,7 +330,13 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     QRaw qraw;
     if (wave == 0) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads);      // issued before the keys
     KeyBatch A, B;
-    load_batch<POOL>(kv, req, pool, nv, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
+    load_batch<POOL>(kv, req, pool, nullptr, 0, nv, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
+    if (POOL && (int)threadIdx.x <= IS_CHUNK / 8) {
+        // batch b's blocks of every wave: 32 (IS_WAVES x + Gx IS_WAVES b) / 4 + 0 .. 31
+        const int t = threadIdx.x;
+        const int gi = t == IS_CHUNK / 8 ? 0 : 8 * IS_WAVES * ((int)blockIdx.x + Gx * (t >> 5)) + (t & 31);
+        qs.pool_l[t] = gi < (ncols >> 3) ? pool[gi] : 0;
+    }
     if (wave == 0) prep_query<QBF16>(qs.q, qraw, a.w, row, a.n_heads);
     if (threadIdx.x == 0) qs.n_fix = 0;
     __syncthreads();
@@ -350,7 +364,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     // each row group; lane l keeps the one of tile l / 16, so the batch's 64
     // scores leave in one coalesced 256-B store, and its 8 block maxima in one
     // 32-B store.
-    auto compute = [&](const KeyBatch& kb, int col_base) {
+    auto compute = [&](const KeyBatch& kb, int col_base, int lbase) {
         float vt[IS_TILES];
 #pragma unroll
         for (int t = 0; t < IS_TILES; ++t) {
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             const int col = col0 + n;
             const bool in_cols = col < ncols;
             // full scan: the position is the column (padding up to a multiple of 8 gets -inf)
-            const int pos = POOL ? (in_cols ? col_pos<POOL>(pool, col) : 0x7FFFFFFF) : col;
+            const int pos = POOL ? (in_cols ? 8 * qs.pool_l[lbase + ((col >> 3) & 31)] + (col & 7) : 0x7FFFFFFF) : col;
             if (__builtin_expect(__any(!ok), 0)) {
                 if (writer && !ok && in_cols && pos < nv) qs.fix[atomicAdd(&qs.n_fix, 1)] = col & ~7;
             }
@@ -408,11 +422,11 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
 #pragma unroll
     for (int b = 0; b < IS_ITERS; b += 2) {
         const int c_a = wbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
-        load_batch<POOL>(kv, req, pool, nv, ncols, c_b, TSTRIDE, n, lg, B);
-        compute(A, c_a);
+        load_batch<POOL>(kv, req, pool, qs.pool_l, 32 * (b + 1), nv, ncols, c_b, TSTRIDE, n, lg, B);
+        compute(A, c_a, 32 * b);
         const int c_n = c_b + BSTRIDE;
-        if (b + 2 < IS_ITERS) load_batch<POOL>(kv, req, pool, nv, ncols, c_n, TSTRIDE, n, lg, A);
-        compute(B, c_b);
+        if (b + 2 < IS_ITERS) load_batch<POOL>(kv, req, pool, qs.pool_l, 32 * (b + 2), nv, ncols, c_n, TSTRIDE, n, lg, A);
+        compute(B, c_b, 32 * (b + 1));
     }
 
     // ---- exact path for the queued 8-blocks (first column of each)
@@ -483,7 +497,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvVie
     const int BSTRIDE = 64 * IS_WAVES * Gx;
 
     KeyBatch A, B;
-    load_batch<false>(kv, req, nullptr, ncols, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
+    load_batch<false>(kv, req, nullptr, nullptr, 0, ncols, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
     {
         // wave w quantises rows w, w + 4, ...; rows past the end copy the last row
         constexpr int PER = R / IS_WAVES;
@@ -584,9 +598,9 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvVie
     // into range and not used), so every wait names one batch exactly
     for (int b = 0; b < SR_ITERS; b += 2) {
         const int c_a = wbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
-        load_batch<false>(kv, req, nullptr, ncols, ncols, c_b, TSTRIDE, n, lg, B);
+        load_batch<false>(kv, req, nullptr, nullptr, 0, ncols, ncols, c_b, TSTRIDE, n, lg, B);
         compute(A, c_a);
-        load_batch<false>(kv, req, nullptr, ncols, ncols, c_b + BSTRIDE, TSTRIDE, n, lg, A);
+        load_batch<false>(kv, req, nullptr, nullptr, 0, ncols, ncols, c_b + BSTRIDE, TSTRIDE, n, lg, A);
         compute(B, c_b);
     }
 
