@@ -244,6 +244,61 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
     return gt_base + min(eq_base, need);
 }
 
+// The first radix pass alone, over keys held in registers (u[i] is column
+// 16 t + i of thread t; 0 = absent): (thr_mask, thr_val) such that the keys
+// with (u & thr_mask) >= thr_val are the k largest and the other keys of the
+// histogram bin that holds the k-th largest (every present key when there
+// are at most k).  Leaves the histogram cleared.
+__device__ __forceinline__ void kth_bin(TkShared& sh, const uint32_t* u, uint32_t k, uint32_t& thr_mask,
+                                        uint32_t& thr_val) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
+#pragma unroll
+    for (int i = 0; i < TK_ITEMS; ++i)
+        if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
+    for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
+    cnt = __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
+    umin = wave_min(umin);
+    umax = wave_max(umax);
+    if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = umin; sh.red[2][wave] = umax; }
+    __syncthreads();
+    uint32_t n_present = 0;
+    umin = 0xFFFFFFFFu; umax = 0u;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+        n_present += sh.red[0][w];
+        umin = min(umin, sh.red[1][w]);
+        umax = max(umax, sh.red[2][w]);
+    }
+    thr_mask = 0u;
+    thr_val = 0u;
+    const uint32_t diff = umin ^ umax;
+    if (n_present <= k || !diff) return;          // every present key (all of them equal in the second case)
+    const int hb = 31 - __clz(diff);
+    const uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+    const uint32_t prefix = umin & mask;
+    const int shift = hb >= 11 ? hb - 11 : 0;
+    const uint32_t dmask = (1u << (hb - shift + 1)) - 1u;
+#pragma unroll
+    for (int i = 0; i < TK_ITEMS; ++i)
+        if (u[i] != 0u) atomicAdd(&sh.hist[(u[i] >> shift) & dmask], 1u);
+    __syncthreads();
+    const int b0 = TK_BINS - 4 - 4 * threadIdx.x;
+    const uint4 hv = *(const uint4*)&sh.hist[b0];
+    *(uint4*)&sh.hist[b0] = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t hb4[4] = {hv.w, hv.z, hv.y, hv.x};
+    uint32_t tot;
+    uint32_t before = block_excl_scan(hb4[0] + hb4[1] + hb4[2] + hb4[3], sh.part[0], tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (hb4[j] != 0u && before < k && k <= before + hb4[j]) sh.digit = (uint32_t)(b0 + 3 - j);
+        before += hb4[j];
+    }
+    __syncthreads();
+    thr_mask = mask | (dmask << shift);
+    thr_val = prefix | (sh.digit << shift);
+}
+
 // Keys of 16 consecutive columns c0 .. c0+15 of a row (absent past ncols).
 __device__ __forceinline__ void load_cols(const float* krow, int ncols, int c0, uint32_t* u) {
     if (c0 + TK_ITEMS <= ncols && ((uintptr_t)(krow + c0) & 15) == 0) {
@@ -314,9 +369,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
 
 // The Full layer's selection for one row: the pool (top n_pool blocks by
 // block maximum) and then the top k positions among the pool's scores.
+//
+// With a grid of two workgroups per row (rows of at most 16,384 blocks,
+// k <= n_pool) the two results are computed side by side: workgroup y = 0
+// selects the pool; y = 1 selects the positions without waiting for it.
+// The top k positions lie in the top k blocks (below), hence in the pool and
+// among the blocks whose maximum reaches the histogram bin of the k-th largest
+// block maximum; y = 1 gathers the scores of those blocks only (if there are
+// more than the pool size, of the top k blocks) and selects among them.
 __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs a) {
     __shared__ TkShared sh;
     const int row = blockIdx.x;
+    const bool split = gridDim.y > 1;
     const int nv = max(0, min(a.n_vis[row], a.max_vis));
     const int nb = (nv + 7) >> 3;
     const float* brow = a.block_max + (int64_t)row * a.block_max_stride;
@@ -336,7 +400,41 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         sh.pool[slot] = (key & thr_mask) >= thr_val ? col : (int32_t)((uint32_t)col | 0x80000000u);
     };
     uint32_t np;
-    if (nb <= TK_SWEEP) {
+    if (split && blockIdx.y == 0) {
+        // the pool alone
+        auto pemit0 = [&](int col, uint32_t slot, uint32_t) { sh.pool[slot] = col; };
+        uint32_t m, v;
+        np = select_row<1>(sh, nb, a.n_pool, bkeys, pemit0, 0u, m, v);
+        __syncthreads();
+        for (int j = threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = j < (int)np ? sh.pool[j] : -1;
+        if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
+        return;
+    } else if (split) {
+        // candidate blocks for the positions, ascending, in sh.pool
+        uint32_t u[TK_ITEMS];
+        bkeys(0, u);
+        kth_bin(sh, u, (uint32_t)a.k, thr_mask, thr_val);
+        uint32_t flags = 0u, c = 0u;
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; ++i) {
+            const bool cand = u[i] != 0u && (u[i] & thr_mask) >= thr_val;
+            flags |= (uint32_t)cand << i;
+            c += cand;
+        }
+        uint32_t tot;
+        uint32_t slot = block_excl_scan(c, sh.part[1], tot);
+        if (tot <= (uint32_t)TK_POOL) {
+#pragma unroll
+            for (int i = 0; i < TK_ITEMS; ++i)
+                if ((flags >> i) & 1u) sh.pool[slot++] = TK_ITEMS * (int)threadIdx.x + i;
+            np = tot;
+        } else {
+            __syncthreads();
+            auto temit = [&](int col, uint32_t s2, uint32_t) { sh.pool[s2] = col; };
+            uint32_t m, v;
+            np = select_row<1>(sh, nb, a.k, bkeys, temit, 0u, m, v);
+        }
+    } else if (nb <= TK_SWEEP) {
         np = select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
     } else if (nb <= 8 * TK_SWEEP) {
         // Longer rows, in registers: the top n_pool blocks lie in the top
@@ -409,9 +507,12 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     __syncthreads();
 
     // ---- outputs, from LDS in coalesced runs (no barrier waits on these stores)
-    for (int j = threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = j < (int)np ? (sh.pool[j] & 0x7FFFFFFF) : -1;
+    if (!split) {
+        for (int j = threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = j < (int)np ? (sh.pool[j] & 0x7FFFFFFF) : -1;
+        if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
+    }
     for (int j = threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = j < (int)ni ? (int32_t)sh.hist[j] : -1;
-    if (threadIdx.x == 0) { a.pool_count[row] = (int32_t)np; a.idx_count[row] = (int32_t)ni; }
+    if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
@@ -420,7 +521,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows), dim3(TK_THREADS), 0, st, a);
+    // two workgroups per row while the doubled grid still fits the 256 CUs
+    // once (a workgroup fills a CU); larger launches keep one per row
+    const bool split = a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && 2 * a.n_rows <= 256;
+    hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows, split ? 2u : 1u), dim3(TK_THREADS), 0, st, a);
     return hipGetLastError();
 }
 
