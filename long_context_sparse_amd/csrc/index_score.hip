@@ -31,6 +31,9 @@
 //     16 keys hand each lane all heads of its key, and the sequential fma fold
 //     runs inside the lane with no cross-lane traffic.  The block maximum over
 //     8 aligned keys uses DPP row shifts.
+#include <algorithm>
+#include <type_traits>
+
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -45,7 +48,8 @@ namespace csa2 {
 constexpr int IS_WAVES = 4;
 constexpr int IS_TILES = CSA2_IS_TILES;              // 16-key tiles per batch
 constexpr int IS_ITERS = CSA2_IS_ITERS;              // batches per wave (even)
-constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16 * IS_ITERS;   // columns per workgroup
+constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16 * IS_ITERS;   // columns of one slice of a workgroup
+constexpr int IS_MAX_SLICES = 8;                     // slices of a row per workgroup, at most
 
 // One row's indexer query in MXFP4, its weights and the exactness-guard bounds.
 struct QRow {
@@ -60,7 +64,7 @@ struct QRow {
 struct QShared {
     QRow q;
     int n_fix;    // queued 8-blocks that need the exact path
-    int fix[IS_CHUNK];
+    int fix[IS_MAX_SLICES * IS_CHUNK / 8];
     // pool mode: the pool entries of this workgroup's blocks (batch b of every
     // wave: slots 32 b .. 32 b + 31) and the row's entry 0 (slot IS_CHUNK / 8)
     int pool_l[IS_CHUNK / 8 + 1];
@@ -251,9 +255,12 @@ typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 // is one wave-uniform load.
 // Pool mode: the pool entry of a column comes from global memory (lpool NULL)
 // or from the workgroup's LDS copy (slots lbase + block mod 32).
-template <bool POOL>
+// PTE (paged full scan): tile t's page-table entry was loaded ahead into lane
+// lbase + t of pte (see slice_pte).
+template <bool POOL, bool PTE = false>
 __device__ __forceinline__ void load_batch(const KvView& kv, int req, const int32_t* pool, const int* lpool, int lbase,
-                                           int nv, int ncols, int col_base, int tstride, int n, int lg, KeyBatch& kb) {
+                                           int nv, int ncols, int col_base, int tstride, int n, int lg, KeyBatch& kb,
+                                           int pte = 0) {
 #pragma unroll
     for (int t = 0; t < IS_TILES; ++t) {
         const int col0 = col_base + tstride * t;         // wave-uniform
@@ -271,8 +278,11 @@ __device__ __forceinline__ void load_batch(const KvView& kv, int req, const int3
             const int off = min(n, ncols - 1 - t0);      // stays inside the tile
             int64_t base;
             if (kv.page_shift < 0) base = (int64_t)req * kv.req_stride + t0;
-            else base = ((int64_t)kv.page_table[(int64_t)req * kv.max_pages + (t0 >> kv.page_shift)] << kv.page_shift) +
-                        (t0 & ((1 << kv.page_shift) - 1));
+            else {
+                const int pg = PTE ? __builtin_amdgcn_readlane(pte, lbase + t)
+                                   : kv.page_table[(int64_t)req * kv.max_pages + (t0 >> kv.page_shift)];
+                base = ((int64_t)pg << kv.page_shift) + (t0 & ((1 << kv.page_shift) - 1));
+            }
             e = base + off;
         }
         // the key stream is read once per scan: non-temporal loads keep it from
@@ -304,7 +314,23 @@ __device__ __forceinline__ float dpp_row_shr_max(float v, int shift) {
     return r;
 }
 
-template <bool QBF16, bool POOL, int NM>
+// Paged full scan: the page-table entries of the IS_ITERS x IS_TILES tiles of
+// a wave's slice, tile t of batch b in lane 4 b + t (lanes 16 .. 63 repeat
+// them), loaded one slice ahead so that no key load waits for one.  Columns
+// past ncols use page 0, as load_batch does.
+__device__ __forceinline__ int slice_pte(const KvView& kv, int req, int ncols, int sbase, int bstride, int tstride,
+                                         int l) {
+    static_assert(IS_ITERS * IS_TILES <= 64, "one lane per tile of a slice");
+    if (kv.page_shift < 0) return 0;
+    const int j = l % (IS_ITERS * IS_TILES);
+    const int col0 = sbase + (j / IS_TILES) * bstride + tstride * (j % IS_TILES);
+    const int t0 = col0 < ncols ? col0 : 0;
+    return kv.page_table[(int64_t)req * kv.max_pages + (t0 >> kv.page_shift)];
+}
+
+// MULTI: a full scan whose workgroups take more than one slice of their row;
+// PTE: a full scan of a paged cache (page-table entries loaded ahead)
+template <bool QBF16, bool POOL, int NM, bool MULTI, bool PTE>
 __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, IndexScoreArgs a) {
     __shared__ QShared qs;
     const int row = blockIdx.y;
@@ -330,7 +356,8 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     QRaw qraw;
     if (wave == 0) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads);      // issued before the keys
     KeyBatch A, B;
-    load_batch<POOL>(kv, req, pool, nullptr, 0, nv, ncols, wbase, TSTRIDE, n, lg, A);   // in flight during the query prep
+    int pte = PTE && !POOL ? slice_pte(kv, req, ncols, wbase, BSTRIDE, TSTRIDE, l) : 0;
+    load_batch<POOL, PTE && !POOL>(kv, req, pool, nullptr, 0, nv, ncols, wbase, TSTRIDE, n, lg, A, pte);   // in flight during the query prep
     if (POOL && (int)threadIdx.x <= IS_CHUNK / 8) {
         // batch b's blocks of every wave: 32 (IS_WAVES x + Gx IS_WAVES b) / 4 + 0 .. 31
         const int t = threadIdx.x;
@@ -398,8 +425,13 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             const bool in_cols = col < ncols;
             // full scan: the position is the column (padding up to a multiple of 8 gets -inf)
             const int pos = POOL ? (in_cols ? 8 * qs.pool_l[lbase + ((col >> 3) & 31)] + (col & 7) : 0x7FFFFFFF) : col;
+            // an 8-block with an unguarded visible key is queued once (lanes 8j + 7)
             if (__builtin_expect(__any(!ok), 0)) {
-                if (writer && !ok && in_cols && pos < nv) qs.fix[atomicAdd(&qs.n_fix, 1)] = col & ~7;
+                int bad = (!ok && in_cols && pos < nv) ? 1 : 0;
+                bad |= __builtin_amdgcn_update_dpp(0, bad, 0x111, 0xF, 0xF, false);   // row_shr:1
+                bad |= __builtin_amdgcn_update_dpp(0, bad, 0x112, 0xF, 0xF, false);   // row_shr:2
+                bad |= __builtin_amdgcn_update_dpp(0, bad, 0x114, 0xF, 0xF, false);   // row_shr:4
+                if (writer && (n & 7) == 7 && bad) qs.fix[atomicAdd(&qs.n_fix, 1)] = col & ~7;
             }
             vt[t] = (in_cols && pos < nv) ? acc : -INFINITY;
         }
@@ -419,15 +451,36 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
         }
     };
 
+    // One slice: IS_ITERS batches per wave, the next batch always in flight;
+    // MORE also fetches the first batch of the next slice.
+    // lbase: pool mode, the batch's slots in the LDS pool copy; paged full
+    // scan, its tiles' lanes in pte (pte_next: those of the next slice)
+    auto slice = [&](auto more, const int sbase, const int pte_next) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < IS_ITERS; b += 2) {
-        const int c_a = wbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
-        load_batch<POOL>(kv, req, pool, qs.pool_l, 32 * (b + 1), nv, ncols, c_b, TSTRIDE, n, lg, B);
-        compute(A, c_a, 32 * b);
-        const int c_n = c_b + BSTRIDE;
-        if (b + 2 < IS_ITERS) load_batch<POOL>(kv, req, pool, qs.pool_l, 32 * (b + 2), nv, ncols, c_n, TSTRIDE, n, lg, A);
-        compute(B, c_b, 32 * (b + 1));
+        for (int b = 0; b < IS_ITERS; b += 2) {
+            const int c_a = sbase + b * BSTRIDE, c_b = c_a + BSTRIDE;
+            load_batch<POOL, PTE && !POOL>(kv, req, pool, qs.pool_l, POOL ? 32 * (b + 1) : IS_TILES * (b + 1), nv, ncols, c_b,
+                                    TSTRIDE, n, lg, B, pte);
+            compute(A, c_a, 32 * b);
+            const int c_n = c_b + BSTRIDE;
+            if (b + 2 < IS_ITERS || decltype(more)::value)
+                load_batch<POOL, PTE && !POOL>(kv, req, pool, qs.pool_l,
+                                        POOL ? 32 * ((b + 2) % IS_ITERS) : IS_TILES * ((b + 2) % IS_ITERS), nv, ncols,
+                                        c_n, TSTRIDE, n, lg, A, b + 2 < IS_ITERS ? pte : pte_next);
+            compute(B, c_b, 32 * (b + 1));
+        }
+    };
+    // slices s = 0 .. nsl-1 of this workgroup start SSTRIDE columns apart
+    // (pool mode: one slice covers the largest pool; without MULTI the grid
+    // gives every slice its own workgroup)
+    const int SSTRIDE = IS_ITERS * BSTRIDE;
+    const int nsl = MULTI && !POOL ? (ncols - 64 * IS_WAVES * (int)blockIdx.x + SSTRIDE - 1) / SSTRIDE : 1;
+    for (int s = 0; s + 1 < nsl; ++s) {
+        const int pn = PTE ? slice_pte(kv, req, ncols, wbase + (s + 1) * SSTRIDE, BSTRIDE, TSTRIDE, l) : 0;
+        slice(std::true_type(), wbase + s * SSTRIDE, pn);
+        pte = pn;
     }
+    slice(std::false_type(), wbase + (nsl - 1) * SSTRIDE, pte);
 
     // ---- exact path for the queued 8-blocks (first column of each)
     __syncthreads();
@@ -623,13 +676,25 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvVie
     }
 }
 
-template <bool QBF16, bool POOL>
+template <bool QBF16, bool POOL, bool MULTI = false, bool PTE = false>
 static void launch_nm(int nm, dim3 grid, dim3 block, hipStream_t st, const KvView& kv, const IndexScoreArgs& a) {
     switch (nm) {
-        case 1: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 1>), grid, block, 0, st, kv, a); break;
-        case 2: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 2>), grid, block, 0, st, kv, a); break;
-        case 3: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 3>), grid, block, 0, st, kv, a); break;
-        default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4>), grid, block, 0, st, kv, a); break;
+        case 1: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 1, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+        case 2: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 2, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+        case 3: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 3, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+        default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+    }
+}
+
+template <bool QBF16>
+static void launch_full(bool multi, bool paged, int nm, dim3 grid, dim3 block, hipStream_t st, const KvView& kv,
+                        const IndexScoreArgs& a) {
+    if (multi) {
+        if (paged) launch_nm<QBF16, false, true, true>(nm, grid, block, st, kv, a);
+        else launch_nm<QBF16, false, true, false>(nm, grid, block, st, kv, a);
+    } else {
+        if (paged) launch_nm<QBF16, false, false, true>(nm, grid, block, st, kv, a);
+        else launch_nm<QBF16, false, false, false>(nm, grid, block, st, kv, a);
     }
 }
 
@@ -658,13 +723,24 @@ hipError_t launch_index_score(const KvView& kv, const IndexScoreArgs& a, hipStre
     const bool pool = a.pool != nullptr;
     const int cols = pool ? 8 * 2048 : a.max_vis;
     const int nm = (a.n_heads + 3) / 4;
-    const dim3 grid((unsigned)((cols + IS_CHUNK - 1) / IS_CHUNK), (unsigned)a.n_rows), block(IS_WAVES * 64);
+    // A full scan gives a row at most IS_MAX_SLICES slices per workgroup and
+    // otherwise as many workgroups as one slice each needs, or fewer while
+    // the grid still has about 2,048 of them: rows far shorter than max_vis
+    // then leave few workgroups with nothing to do.
+    const int chunks = (cols + IS_CHUNK - 1) / IS_CHUNK;
+    int gx = chunks;
+    if (!pool) {
+        const int per_row = (2048 + a.n_rows - 1) / a.n_rows;
+        gx = std::min(chunks, std::max((chunks + IS_MAX_SLICES - 1) / IS_MAX_SLICES, per_row));
+    }
+    if ((chunks + gx - 1) / gx > IS_MAX_SLICES) return hipErrorInvalidValue;   // the fix queue holds 8 slices
+    const dim3 grid((unsigned)gx, (unsigned)a.n_rows), block(IS_WAVES * 64);
     if (a.q_bf16) {
         if (pool) launch_nm<true, true>(nm, grid, block, st, kv, a);
-        else launch_nm<true, false>(nm, grid, block, st, kv, a);
+        else launch_full<true>(gx < chunks, kv.page_shift >= 0, nm, grid, block, st, kv, a);
     } else {
         if (pool) launch_nm<false, true>(nm, grid, block, st, kv, a);
-        else launch_nm<false, false>(nm, grid, block, st, kv, a);
+        else launch_full<false>(gx < chunks, kv.page_shift >= 0, nm, grid, block, st, kv, a);
     }
     return hipGetLastError();
 }

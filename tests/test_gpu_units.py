@@ -151,6 +151,58 @@ def test_index_score_full_exact(Hi, spread):
         assert np.all(Bm[r, nb:] == 7.0)
 
 
+@pytest.mark.parametrize("spread,paged", [(False, False), (True, False), (True, True)])
+def test_index_score_multi_slice_exact(spread, paged):
+    """128 rows of up to 131,072 keys: the launch gives each workgroup up to
+    8 slices of its row (the largest number it allows), queuing the exact
+    path's 8-blocks of every slice.  Sampled rows equal the oracle bit for
+    bit, and every row equals the same rows scanned 16 at a time (one slice
+    per workgroup); ragged counts include none, fewer than 8, one past a slice
+    and the whole context.  The paged case uses pages of 16 entries in a
+    random order (every tile of a batch on its own page)."""
+    Hi, n, n_rows = 8, 131072, 128
+    _, _, _, kc, ks = _score_setup(1, n, Hi, spread=spread, zero_groups=spread)
+    q = RNG.standard_normal((n_rows, Hi, 128)).astype(np.float32)
+    if spread:
+        q *= (2.0 ** RNG.integers(-8, 8, (n_rows, Hi, 4))).repeat(32, axis=2).astype(np.float32)
+    q = bf16(q).float().numpy()
+    w = RNG.random((n_rows, Hi)).astype(np.float32)
+    w[:, ::3] *= -1
+    n_vis = RNG.integers(0, n + 1, n_rows).astype(np.int32)
+    n_vis[:8] = [n, 0, 17, 1023, 1025, n - 1, 8 * 1024 * 16 // 2 + 1, 5]
+    if paged:
+        P = 16
+        table = RNG.permutation(n // P).astype(np.int32)[None, :]
+        slots = (table[0][np.arange(n) // P].astype(np.int64) * P + np.arange(n) % P)
+        kc2, ks2 = np.zeros_like(kc), np.zeros_like(ks)
+        kc2[slots], ks2[slots] = kc, ks
+        kv = lib.make_kv(idx_codes=T(kc2), idx_scales=T(ks2), n_slots=n, page_entries=P, page_table=T(table))
+    else:
+        kv = lib.make_kv(idx_codes=T(kc), idx_scales=T(ks), n_slots=n, req_stride=n)
+    req = T(np.zeros(n_rows, np.int32))
+    nv = T(n_vis)
+    scores = torch.full((n_rows, n), 7.0, dtype=torch.float32, device=DEV)
+    bmax = torch.full((n_rows, n // 8), 7.0, dtype=torch.float32, device=DEV)
+    lib.csa2_index_score(kv, lib.make_rows(req, nv, n), T(q), T(w), scores=scores, block_max=bmax)
+    s16 = torch.full_like(scores, 7.0)
+    b16 = torch.full_like(bmax, 7.0)
+    for r0 in range(0, n_rows, 16):
+        lib.csa2_index_score(kv, lib.make_rows(req[r0:r0 + 16], nv[r0:r0 + 16], n), T(q[r0:r0 + 16]),
+                             T(w[r0:r0 + 16]), scores=s16[r0:r0 + 16], block_max=b16[r0:r0 + 16])
+    torch.cuda.synchronize()
+    S, Bm = scores.cpu().numpy(), bmax.cpu().numpy()
+    assert np.array_equal(S, s16.cpu().numpy()) and np.array_equal(Bm, b16.cpu().numpy())
+    qc, qs = oracle.quant_query(q.reshape(-1, 128))
+    for r in [0, 1, 2, 3, 4, 5, 6, 7, 77]:
+        m = int(n_vis[r])
+        ref = oracle.index_score(qc[r * Hi:(r + 1) * Hi], qs[r * Hi:(r + 1) * Hi], w[r], kc[:m], ks[:m])
+        assert np.array_equal(S[r, :m], ref), (r, np.nonzero(S[r, :m] != ref)[0][:5])
+        m8 = (m + 7) // 8 * 8
+        assert np.all(np.isneginf(S[r, m:m8])) and np.all(S[r, m8:] == 7.0)
+        nb = (m + 7) // 8
+        assert np.array_equal(Bm[r, :nb], oracle.block_max(ref)) and np.all(Bm[r, nb:] == 7.0)
+
+
 @pytest.mark.parametrize("Hi,spread,paged,qdt", [(1, False, False, "bf16"), (3, True, False, "bf16"),
                                                   (8, False, False, "bf16"), (8, True, True, "bf16"),
                                                   (16, True, False, "bf16"), (8, True, False, "f32")])
@@ -337,14 +389,22 @@ def test_topk_block_counts_and_pool_ids():
         assert int(icnt2[r]) == len(ref2) and np.array_equal(idx2[r, :len(ref2)].cpu().numpy(), ref2)
 
 
+@pytest.mark.parametrize("rows", ["two_sweeps", "split"])
 @pytest.mark.parametrize("ties,k", [(False, 512), (True, 512), (False, 37), (True, 37), (True, 2048)])
-def test_select_full_exact(ties, k):
+def test_select_full_exact(ties, k, rows):
     """The fused Full-layer selection equals the oracle's pool + top-k and
     the two-call form, on rows with no entry, a partial block, fewer than
     2,048 blocks and more than 16,384 blocks (two sweeps).  With k below the
     pool size only the pool blocks at or above the histogram bin of the k-th
-    block are read again; heavy ties put many blocks into that bin."""
-    n_vis = np.array([0, 13, 5003, 16384 * 8 + 21], np.int32)
+    block are read again; heavy ties put many blocks into that bin.  Rows of
+    at most 131,072 entries ("split") take two workgroups per row, the
+    positions' one reading only the blocks at or above the k-th block's bin;
+    a row of equal scores puts every block into that bin (more than the pool
+    holds), and the top k blocks are selected first."""
+    if rows == "split":
+        n_vis = np.array([0, 13, 5003, 131072, 100003, 40000], np.int32)
+    else:
+        n_vis = np.array([0, 13, 5003, 16384 * 8 + 21], np.int32)
     n_rows, n = len(n_vis), int(n_vis.max())
     nv8 = (n + 7) // 8 * 8
     sc = np.full((n_rows, nv8), -np.inf, np.float32)
@@ -353,6 +413,8 @@ def test_select_full_exact(ties, k):
         v = RNG.standard_normal(m).astype(np.float32) * 10
         if ties:
             v = np.round(v * 2) / 2                     # many equal scores
+        if rows == "split" and r == n_rows - 1:
+            v = np.full(m, 1.5, np.float32)             # one value: every block ties
         sc[r, :m] = v
     bm = np.stack([np.concatenate([oracle.block_max(sc[r, :n_vis[r]]),
                                    np.full(nv8 // 8 - (int(n_vis[r]) + 7) // 8, -np.inf, np.float32)])
