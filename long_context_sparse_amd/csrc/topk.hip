@@ -47,6 +47,7 @@ struct __align__(16) TkShared {
     uint32_t part[2][TK_WAVES];
     uint32_t red[3][TK_WAVES];
     uint32_t digit, above, count, digit2;
+    uint32_t ovf[TK_WAVES];            // split selection: a wave had more candidate blocks than its list holds
     int32_t pool[TK_POOL];             // fused selection: the row's pool, ascending
 };
 
@@ -410,10 +411,18 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
         return;
     } else if (split) {
-        // candidate blocks for the positions, ascending, in sh.pool
+        // Candidate blocks: those at or above the k-th block maximum's bin.
+        // Wave w holds blocks 1024 w .. 1024 w + 1023; it lists its candidates
+        // (ascending) in sh.pool[128 w ..] with a wave-level prefix sum and
+        // lane j gathers the scores of its list entries 2j and 2j + 1, so
+        // thread order then item order is position order and no workgroup-wide
+        // step is needed before the positions' selection.  A wave with more
+        // than 128 candidates (ties) raises its flag; the selection is then
+        // redone from the top k blocks.
         uint32_t u[TK_ITEMS];
         bkeys(0, u);
         kth_bin(sh, u, (uint32_t)a.k, thr_mask, thr_val);
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         uint32_t flags = 0u, c = 0u;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
@@ -421,19 +430,57 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
             flags |= (uint32_t)cand << i;
             c += cand;
         }
-        uint32_t tot;
-        uint32_t slot = block_excl_scan(c, sh.part[1], tot);
-        if (tot <= (uint32_t)TK_POOL) {
+        const uint32_t incl = wave_incl_sum(c);
+        const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
+        int32_t* wlist = sh.pool + 128 * wave;
+        uint32_t slot = incl - c;
 #pragma unroll
-            for (int i = 0; i < TK_ITEMS; ++i)
-                if ((flags >> i) & 1u) sh.pool[slot++] = TK_ITEMS * (int)threadIdx.x + i;
-            np = tot;
-        } else {
-            __syncthreads();
-            auto temit = [&](int col, uint32_t s2, uint32_t) { sh.pool[s2] = col; };
-            uint32_t m, v;
-            np = select_row<1>(sh, nb, a.k, bkeys, temit, 0u, m, v);
+        for (int i = 0; i < TK_ITEMS; ++i) {
+            if (((flags >> i) & 1u) && slot < 128u) wlist[slot] = TK_ITEMS * (int)threadIdx.x + i;
+            slot += (flags >> i) & 1u;
         }
+        if (lane == 0) sh.ovf[wave] = wtot > 128u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int cb0 = 2 * lane < (int)wtot ? wlist[2 * lane] : -1;
+        const int cb1 = 2 * lane + 1 < (int)wtot && 2 * lane + 1 < 128 ? wlist[2 * lane + 1] : -1;
+        uint32_t v[TK_ITEMS];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int cb = h ? cb1 : cb0;
+            const float4* p = (const float4*)(srow + 8 * (cb >= 0 ? cb : 0));
+            const float4 v0 = p[0], v1 = p[1];
+            const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t key = cb >= 0 && 8 * cb + i < nv ? order_key(f[i]) : 0u;
+                v[8 * h + i] = (key & thr_mask) >= thr_val ? key : 0u;
+            }
+        }
+        auto rkeys = [&](int, uint32_t* uu) {
+#pragma unroll
+            for (int i = 0; i < TK_ITEMS; ++i) uu[i] = v[i];
+        };
+        auto remit = [&](int col, uint32_t s2, uint32_t) {
+            sh.hist[s2] = (uint32_t)(8 * ((col & 8) ? cb1 : cb0) + (col & 7));
+        };
+        uint32_t m2, v2;
+        const uint32_t ni = select_row<1>(sh, TK_SWEEP, a.k, rkeys, remit, 0u, m2, v2);
+        // the flags were written before the selection's first barrier
+        bool ovf_any = false;
+#pragma unroll
+        for (int w = 0; w < TK_WAVES; ++w) ovf_any |= sh.ovf[w] != 0u;
+        if (!ovf_any) {
+            __syncthreads();
+            for (int j = threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = j < (int)ni ? (int32_t)sh.hist[j] : -1;
+            if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
+            return;
+        }
+        __syncthreads();
+        auto temit = [&](int col, uint32_t s2, uint32_t) { sh.pool[s2] = col; };
+        uint32_t m, vv;
+        np = select_row<1>(sh, nb, a.k, bkeys, temit, 0u, m, vv);
     } else if (nb <= TK_SWEEP) {
         np = select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
     } else if (nb <= 8 * TK_SWEEP) {
@@ -523,7 +570,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st) {
     // two workgroups per row while the doubled grid still fits the 256 CUs
     // once (a workgroup fills a CU); larger launches keep one per row
-    const bool split = a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && 2 * a.n_rows <= 256;
+    const bool split = a.max_vis > 0 && a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && 2 * a.n_rows <= 256;
     hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows, split ? 2u : 1u), dim3(TK_THREADS), 0, st, a);
     return hipGetLastError();
 }
