@@ -245,17 +245,18 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
     return gt_base + min(eq_base, need);
 }
 
-// The first radix pass alone, over keys held in registers (u[i] is column
-// 16 t + i of thread t; 0 = absent): (thr_mask, thr_val) such that the keys
-// with (u & thr_mask) >= thr_val are the k largest and the other keys of the
+// The first radix pass alone, over N keys per thread held in registers
+// (0 = absent): (thr_mask, thr_val) such that the keys with
+// (u & thr_mask) >= thr_val are the k largest and the other keys of the
 // histogram bin that holds the k-th largest (every present key when there
 // are at most k).  Leaves the histogram cleared.
+template <int N>
 __device__ __forceinline__ void kth_bin(TkShared& sh, const uint32_t* u, uint32_t k, uint32_t& thr_mask,
                                         uint32_t& thr_val) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
 #pragma unroll
-    for (int i = 0; i < TK_ITEMS; ++i)
+    for (int i = 0; i < N; ++i)
         if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
     for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
     cnt = __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
@@ -281,7 +282,7 @@ __device__ __forceinline__ void kth_bin(TkShared& sh, const uint32_t* u, uint32_
     const int shift = hb >= 11 ? hb - 11 : 0;
     const uint32_t dmask = (1u << (hb - shift + 1)) - 1u;
 #pragma unroll
-    for (int i = 0; i < TK_ITEMS; ++i)
+    for (int i = 0; i < N; ++i)
         if (u[i] != 0u) atomicAdd(&sh.hist[(u[i] >> shift) & dmask], 1u);
     __syncthreads();
     const int b0 = TK_BINS - 4 - 4 * threadIdx.x;
@@ -411,7 +412,11 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
         return;
     } else if (split) {
-        // Candidate blocks: those at or above the k-th block maximum's bin.
+        // Candidate blocks: those at or above the histogram bin of the k-th
+        // largest maximum of the super-blocks of 8 blocks (the k largest
+        // super-block maxima are k distinct block maxima, so that bin's lower
+        // edge bounds the k-th block maximum from below; the radix pass runs
+        // over 2 keys per thread instead of 16).
         // Wave w holds blocks 1024 w .. 1024 w + 1023; it lists its candidates
         // (ascending) in sh.pool[128 w ..] with a wave-level prefix sum and
         // lane j gathers the scores of its list entries 2j and 2j + 1, so
@@ -421,7 +426,10 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         // redone from the top k blocks.
         uint32_t u[TK_ITEMS];
         bkeys(0, u);
-        kth_bin(sh, u, (uint32_t)a.k, thr_mask, thr_val);
+        uint32_t sbk[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { sbk[0] = max(sbk[0], u[i]); sbk[1] = max(sbk[1], u[8 + i]); }
+        kth_bin<2>(sh, sbk, (uint32_t)a.k, thr_mask, thr_val);
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         uint32_t flags = 0u, c = 0u;
 #pragma unroll
