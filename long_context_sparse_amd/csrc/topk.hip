@@ -470,9 +470,9 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
 #pragma unroll
             for (int i = 0; i < TK_ITEMS; ++i) uu[i] = v[i];
         };
-        auto remit = [&](int col, uint32_t s2, uint32_t) {
-            sh.hist[s2] = (uint32_t)(8 * ((col & 8) ? cb1 : cb0) + (col & 7));
-        };
+        // positions go straight to the output row (the fallback below rewrites
+        // every slot of it)
+        auto remit = [&](int col, uint32_t s2, uint32_t) { irow[s2] = 8 * ((col & 8) ? cb1 : cb0) + (col & 7); };
         uint32_t m2, v2;
         const uint32_t ni = select_row<1>(sh, TK_SWEEP, a.k, rkeys, remit, 0u, m2, v2);
         // the flags were written before the selection's first barrier
@@ -480,8 +480,7 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
 #pragma unroll
         for (int w = 0; w < TK_WAVES; ++w) ovf_any |= sh.ovf[w] != 0u;
         if (!ovf_any) {
-            __syncthreads();
-            for (int j = threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = j < (int)ni ? (int32_t)sh.hist[j] : -1;
+            for (int j = (int)ni + threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = -1;
             if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
             return;
         }
