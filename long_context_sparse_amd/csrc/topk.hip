@@ -117,9 +117,15 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
 // k2-th largest key, and (thr_mask, thr_val) are set so that the keys u with
 // (u & thr_mask) >= thr_val are those of that bin and above: a superset of
 // the top k2.  Otherwise every key passes (thr_mask = thr_val = 0).
-template <int NSW, class KEYS, class EMIT>
+//
+// HINT (one sweep only): every present key lies in [hint_min, hint_max] and
+// the histogram is already clear, so the opening count / min / max round is
+// skipped; the count of present keys comes from the first pass's histogram.
+template <int NSW, class KEYS, class EMIT, bool HINT = false>
 __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit,
-                                               uint32_t k2, uint32_t& thr_mask, uint32_t& thr_val) {
+                                               uint32_t k2, uint32_t& thr_mask, uint32_t& thr_val,
+                                               uint32_t hint_min = 0u, uint32_t hint_max = 0u) {
+    static_assert(!HINT || NSW == 1, "a range hint is for keys held in registers");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsweep = NSW ? NSW : (ncols + TK_SWEEP - 1) / TK_SWEEP;
     uint32_t u[TK_ITEMS];
@@ -127,26 +133,33 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
     for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
 
     // ---- count, min and max of the present keys; clear the histogram
-    uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
-    for (int s = 0; s < nsweep; ++s) {
-        keys(s, u);
+    uint32_t n_present = 0xFFFFFFFFu, umin = hint_min, umax = hint_max;
+    if (HINT) {
+        keys(0, u);
+    } else {
+        uint32_t cnt = 0;
+        umin = 0xFFFFFFFFu;
+        umax = 0u;
+        for (int s = 0; s < nsweep; ++s) {
+            keys(s, u);
 #pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i)
-            if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
-    }
-    for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
-    cnt = __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
-    umin = wave_min(umin);
-    umax = wave_max(umax);
-    if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = umin; sh.red[2][wave] = umax; }
-    __syncthreads();
-    uint32_t n_present = 0;
-    umin = 0xFFFFFFFFu; umax = 0u;
+            for (int i = 0; i < TK_ITEMS; ++i)
+                if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
+        }
+        for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
+        cnt = __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
+        umin = wave_min(umin);
+        umax = wave_max(umax);
+        if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = umin; sh.red[2][wave] = umax; }
+        __syncthreads();
+        n_present = 0;
+        umin = 0xFFFFFFFFu; umax = 0u;
 #pragma unroll
-    for (int w = 0; w < TK_WAVES; ++w) {
-        n_present += sh.red[0][w];
-        umin = min(umin, sh.red[1][w]);
-        umax = max(umax, sh.red[2][w]);
+        for (int w = 0; w < TK_WAVES; ++w) {
+            n_present += sh.red[0][w];
+            umin = min(umin, sh.red[1][w]);
+            umax = max(umax, sh.red[2][w]);
+        }
     }
 
     // ---- radix select: prefix/mask describe the bits decided so far
@@ -184,6 +197,12 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
             uint32_t tot;
             uint32_t before = block_excl_scan(h, sh.part[pb], tot);
             pb ^= 1;
+            if (HINT && pass == 0 && tot <= rem) {
+                // at most k present keys: every one is taken
+                mask = 0u;
+                prefix = 0u;
+                break;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (hb4[j] != 0u && before < rem && rem <= before + hb4[j]) {
@@ -249,10 +268,10 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
 // (0 = absent): (thr_mask, thr_val) such that the keys with
 // (u & thr_mask) >= thr_val are the k largest and the other keys of the
 // histogram bin that holds the k-th largest (every present key when there
-// are at most k).  Leaves the histogram cleared.
+// are at most k), and the largest key.  Leaves the histogram cleared.
 template <int N>
 __device__ __forceinline__ void kth_bin(TkShared& sh, const uint32_t* u, uint32_t k, uint32_t& thr_mask,
-                                        uint32_t& thr_val) {
+                                        uint32_t& thr_val, uint32_t& key_max) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t cnt = 0, umin = 0xFFFFFFFFu, umax = 0u;
 #pragma unroll
@@ -272,6 +291,7 @@ __device__ __forceinline__ void kth_bin(TkShared& sh, const uint32_t* u, uint32_
         umin = min(umin, sh.red[1][w]);
         umax = max(umax, sh.red[2][w]);
     }
+    key_max = umax;
     thr_mask = 0u;
     thr_val = 0u;
     const uint32_t diff = umin ^ umax;
@@ -403,12 +423,11 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     };
     uint32_t np;
     if (split && blockIdx.y == 0) {
-        // the pool alone
-        auto pemit0 = [&](int col, uint32_t slot, uint32_t) { sh.pool[slot] = col; };
+        // the pool alone, emitted straight into the output row
+        auto pemit0 = [&](int col, uint32_t slot, uint32_t) { prow[slot] = col; };
         uint32_t m, v;
         np = select_row<1>(sh, nb, a.n_pool, bkeys, pemit0, 0u, m, v);
-        __syncthreads();
-        for (int j = threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = j < (int)np ? sh.pool[j] : -1;
+        for (int j = (int)np + threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = -1;
         if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
         return;
     } else if (split) {
@@ -429,7 +448,8 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         uint32_t sbk[2] = {0u, 0u};
 #pragma unroll
         for (int i = 0; i < 8; ++i) { sbk[0] = max(sbk[0], u[i]); sbk[1] = max(sbk[1], u[8 + i]); }
-        kth_bin<2>(sh, sbk, (uint32_t)a.k, thr_mask, thr_val);
+        uint32_t key_max;
+        kth_bin<2>(sh, sbk, (uint32_t)a.k, thr_mask, thr_val, key_max);
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         uint32_t flags = 0u, c = 0u;
 #pragma unroll
@@ -473,9 +493,13 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         // positions go straight to the output row (the fallback below rewrites
         // every slot of it)
         auto remit = [&](int col, uint32_t s2, uint32_t) { irow[s2] = 8 * ((col & 8) ? cb1 : cb0) + (col & 7); };
+        // every present key lies in [thr_val, key_max] (no score exceeds the
+        // largest block maximum) and kth_bin left the histogram clear
         uint32_t m2, v2;
-        const uint32_t ni = select_row<1>(sh, TK_SWEEP, a.k, rkeys, remit, 0u, m2, v2);
-        // the flags were written before the selection's first barrier
+        const uint32_t ni = select_row<1, decltype(rkeys), decltype(remit), true>(sh, TK_SWEEP, a.k, rkeys, remit, 0u,
+                                                                               m2, v2, thr_val, key_max);
+        // the flags were written before the selection's first barrier (its
+        // first pass's)
         bool ovf_any = false;
 #pragma unroll
         for (int w = 0; w < TK_WAVES; ++w) ovf_any |= sh.ovf[w] != 0u;
