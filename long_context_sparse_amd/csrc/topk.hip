@@ -430,6 +430,15 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         for (int j = (int)np + threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = -1;
         if (threadIdx.x == 0) a.pool_count[row] = (int32_t)np;
         return;
+    } else if (split && nv <= TK_SWEEP) {
+        // a short row: its top k positions directly, among all its scores
+        auto skeys2 = [&](int, uint32_t* uu) { load_cols(srow, nv, TK_ITEMS * (int)threadIdx.x, uu); };
+        auto semit2 = [&](int col, uint32_t s2, uint32_t) { irow[s2] = col; };
+        uint32_t m2, v2;
+        const uint32_t ni = select_row<1>(sh, nv, a.k, skeys2, semit2, 0u, m2, v2);
+        for (int j = (int)ni + threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = -1;
+        if (threadIdx.x == 0) a.idx_count[row] = (int32_t)ni;
+        return;
     } else if (split) {
         // Candidate blocks: those at or above the histogram bin of the k-th
         // largest maximum of the super-blocks of 8 blocks (the k largest
@@ -600,8 +609,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 
 hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st) {
     // two workgroups per row while the doubled grid still fits the 256 CUs
-    // once (a workgroup fills a CU); larger launches keep one per row
-    const bool split = a.max_vis > 0 && a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && 2 * a.n_rows <= 256;
+    // once (a workgroup fills a CU), for rows of more than 8 k blocks (fewer
+    // super-blocks than k would make every block a candidate); larger
+    // launches and shorter rows keep one workgroup per row
+    const bool split = a.max_vis > 64 * a.k && a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && 2 * a.n_rows <= 256;
     hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows, split ? 2u : 1u), dim3(TK_THREADS), 0, st, a);
     return hipGetLastError();
 }
