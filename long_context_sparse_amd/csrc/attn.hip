@@ -253,22 +253,29 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int cb = split * ctot / S, ce = (split + 1) * ctot / S;   // this split's chunks
     const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
-    // cache slots of the selected entries (the index is read before its count
-    // is known: one dependent load less); the query and its per-head scale;
-    // the exponent range of the row's window scales
-    const int32_t my_idx = a.idx ? a.idx[(int64_t)row * a.idx_stride + min((int64_t)threadIdx.x, a.idx_stride - 1)] : 0;
-    if ((int)threadIdx.x < nsp) sm.ent[threadIdx.x] = entry_of(kv, a.req[row], my_idx);
+    // The cache slots of the selected entries (the index is read before its
+    // count is known: one dependent load less), the query and its per-head
+    // scale, the exponent range of the row's window scales.  Every load is
+    // issued before any is used, from a valid address (a dummy one where it is
+    // not needed): a load under a branch makes the compiler wait for it where
+    // the branch joins, which would put three memory round trips in a row.
+    const int32_t* idx_p = a.idx ? a.idx + (int64_t)row * a.idx_stride + min((int64_t)threadIdx.x, a.idx_stride - 1)
+                                 : (const int32_t*)a.q;
+    const int32_t idx_raw = *idx_p;
+    const int req_r = *(a.req ? a.req + row : (const int32_t*)a.q);
+    const bool has_sc = (int)threadIdx.x * 8 < nsw * 32;
+    const uint2 scv = *(const uint2*)(has_sc ? a.swa_scales + swa0 * 32 + 8 * threadIdx.x : (const uint8_t*)a.q);
+    bf16x8 qb[8];
+    float qa = load_q_operand<QBF16>(a.q, (int64_t)row * a.n_heads + h0 + n, kh, g, qb);
+    if ((int)threadIdx.x < nsp) sm.ent[threadIdx.x] = entry_of(kv, req_r, idx_raw);   // paged: one more load
     int wmax = 0, wmin = 255;                       // over nonzero scale codes (all-zero groups have code 0)
-    if ((int)threadIdx.x * 8 < nsw * 32) {
-        const uint2 v = *(const uint2*)(a.swa_scales + swa0 * 32 + 8 * threadIdx.x);
+    if (has_sc) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = (int)(((i < 4 ? v.x : v.y) >> (8 * (i & 3))) & 0xFFu);
+            const int c = (int)(((i < 4 ? scv.x : scv.y) >> (8 * (i & 3))) & 0xFFu);
             if (c) { wmax = max(wmax, c); wmin = min(wmin, c); }
         }
     }
-    bf16x8 qb[8];
-    float qa = load_q_operand<QBF16>(a.q, (int64_t)row * a.n_heads + h0 + n, kh, g, qb);
     qa = max_xor32(max_xor16(qa));
     if (et == 0 && g == 0) sm.qmax[kh][n] = qa;
 #pragma unroll
