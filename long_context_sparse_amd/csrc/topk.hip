@@ -610,9 +610,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st) {
     // two workgroups per row while the doubled grid still fits the 256 CUs
     // once (a workgroup fills a CU), for rows of more than 8 k blocks (fewer
-    // super-blocks than k would make every block a candidate); larger
-    // launches and shorter rows keep one workgroup per row
-    const bool split = a.max_vis > 64 * a.k && a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && 2 * a.n_rows <= 256;
+    // super-blocks than k would make every block a candidate) and k <= 1,024
+    // (about k candidates share the 16 waves' lists of 128); larger launches,
+    // shorter rows and larger k keep one workgroup per row
+    const bool split = a.max_vis > 64 * a.k && a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && a.k <= 1024 &&
+                       2 * a.n_rows <= 256;
     hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows, split ? 2u : 1u), dim3(TK_THREADS), 0, st, a);
     return hipGetLastError();
 }
