@@ -25,8 +25,11 @@
 // barriers.
 //
 // The Full layer's two selections (2,048 blocks by their maxima, then 512
-// positions among those blocks' scores) also run fused in one workgroup per
-// row, with the pool kept in LDS between them.
+// positions among those blocks' scores) run fused in one workgroup per row,
+// with the pool kept in LDS between them, or, for launches of few long rows,
+// side by side in two workgroups per row: the top 512 positions lie in the
+// top 512 blocks, so they are selected from the blocks at or above a radix
+// bin of the block maxima without waiting for the pool.
 #include "csa2.h"
 #include "csa2_device.h"
 #include "csa2_launch.h"
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int cb0 = 2 * lane < (int)wtot ? wlist[2 * lane] : -1;
-        const int cb1 = 2 * lane + 1 < (int)wtot && 2 * lane + 1 < 128 ? wlist[2 * lane + 1] : -1;
+        const int cb1 = 2 * lane + 1 < (int)wtot ? wlist[2 * lane + 1] : -1;
         uint32_t v[TK_ITEMS];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
