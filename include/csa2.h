@@ -141,7 +141,7 @@ csa2_status csa2_pack_kv(csa2_kind kind, const void* src, csa2_dtype src_dtype, 
  *   scored; column 8j+i of `scores` holds the score of position
  *   8*pool_blocks[..j] + i, or -inf if that position is >= n_vis.
  *   block_max must be NULL.
- * n_idx_heads in 1..16.  Requires kv->idx_codes / idx_scales. */
+ * n_idx_heads in 1..64.  Requires kv->idx_codes / idx_scales. */
 csa2_status csa2_index_score(const csa2_kv* kv, const csa2_rows* rows,
                              const void* q_idx, csa2_dtype q_dtype, int32_t n_idx_heads,
                              const float* w,

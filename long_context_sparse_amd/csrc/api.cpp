@@ -123,7 +123,7 @@ csa2_status csa2_index_score(const csa2_kv* kv, const csa2_rows* rows, const voi
     csa2_status s = make_view(kv, false, true, &v);
     if (s != CSA2_OK) return s;
     if ((s = check_rows(rows)) != CSA2_OK) return s;
-    if (n_idx_heads < 1 || n_idx_heads > 16) return fail(CSA2_ERR_UNSUPPORTED, "n_idx_heads must be in 1..16 (got %d)", n_idx_heads);
+    if (n_idx_heads < 1 || n_idx_heads > 64) return fail(CSA2_ERR_UNSUPPORTED, "n_idx_heads must be in 1..64 (got %d)", n_idx_heads);
     if (q_dtype != CSA2_BF16 && q_dtype != CSA2_F32) return fail(CSA2_ERR_UNSUPPORTED, "unknown q dtype");
     if (rows->n_rows == 0) return CSA2_OK;
     if (!q_idx || !w) return fail(CSA2_ERR_NULL, "q_idx / w is NULL");

@@ -52,17 +52,23 @@ constexpr int IS_CHUNK = IS_WAVES * IS_TILES * 16 * IS_ITERS;   // columns of on
 constexpr int IS_MAX_SLICES = 8;                     // slices of a row per workgroup, at most
 
 // One row's indexer query in MXFP4, its weights and the exactness-guard bounds.
-struct QRow {
-    uint8_t codes[16][64];
-    uint8_t scales[16][4];
-    float w[16];
+// A row's quantised indexer query for up to MH heads.
+template <int MH>
+struct QRowT {
+    uint8_t codes[MH][64];
+    uint8_t scales[MH][4];
+    float w[MH];
     int spread;   // max over real heads of (max - min) block scale code
     int smin;     // min block scale code over real heads
     int smax;     // max block scale code over real heads
 };
+typedef QRowT<16> QRow;
+constexpr int IS_MAX_HEADS = 64;                     // indexer heads of the single-row scan (16 per group)
 
+template <int MH>
 struct QShared {
-    QRow q;
+    QRowT<MH> q;
+    int st[4][3];  // more than 16 heads: each wave's (spread, min, max) over its group
     int n_fix;    // queued 8-blocks that need the exact path
     int fix[IS_MAX_SLICES * IS_CHUNK / 8];
     // pool mode: the pool entries of this workgroup's blocks (batch b of every
@@ -134,7 +140,7 @@ __device__ float round_pow2_sum4(const int* S, const int* E) {
 }
 
 // Exact score of one key (used where the MFMA exactness guard fails) against
-// one row's quantised query: codes [16][64], scales [16][4], weights [16].
+// one row's quantised query: codes [heads][64], scales [heads][4], weights.
 __device__ float exact_key_score(const uint8_t (*qcodes)[64], const uint8_t (*qscales)[4], const float* qw,
                                  int n_heads, const uint8_t* kc, const uint8_t* ks) {
     uint8_t key[64];
@@ -165,10 +171,11 @@ struct QRaw {
     uint32_t w[32];
 };
 
+// Lane (head hoff + l % 16, block l / 16).
 template <bool QBF16>
-__device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, int n_heads) {
+__device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, int n_heads, int hoff = 0) {
     const int l = threadIdx.x & 63;
-    const int m = l & 15, g = l >> 4;
+    const int m = hoff + (l & 15), g = l >> 4;
     if (m >= n_heads) return;
     const int64_t off = ((int64_t)row * n_heads + m) * 128 + 32 * g;
     if (QBF16) {
@@ -188,12 +195,14 @@ __device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, 
     }
 }
 
-// Quantise the row's indexer query to MXFP4 (one lane per (head, block) =
-// exactly the MFMA A-operand layout) and gather the exactness-guard bounds.
-template <bool QBF16>
-__device__ __forceinline__ void prep_query(QRow& qs, const QRaw& r, const float* w, int row, int n_heads) {
+// Quantise heads hoff .. hoff+15 of the row's indexer query to MXFP4 (one
+// lane per (head, block) = exactly the MFMA A-operand layout) and gather
+// their exactness-guard bounds (spread, min, max; returned in every lane).
+template <bool QBF16, class QR>
+__device__ __forceinline__ void prep_query(QR& qs, const QRaw& r, const float* w, int row, int n_heads, int hoff,
+                                           int& spread_out, int& smin_out, int& smax_out) {
     const int l = threadIdx.x & 63;
-    const int m = l & 15, g = l >> 4;
+    const int m = hoff + (l & 15), g = l >> 4;
     uint32_t words[4] = {0, 0, 0, 0};
     int sc = 127;
     const bool real = m < n_heads;
@@ -219,7 +228,7 @@ __device__ __forceinline__ void prep_query(QRow& qs, const QRaw& r, const float*
     }
     *(uint4*)&qs.codes[m][16 * g] = make_uint4(words[0], words[1], words[2], words[3]);
     qs.scales[m][g] = (uint8_t)sc;
-    if (l < 16) qs.w[l] = (l < n_heads) ? w[(int64_t)row * n_heads + l] : 0.0f;
+    if (l < 16) qs.w[hoff + l] = (hoff + l < n_heads) ? w[(int64_t)row * n_heads + hoff + l] : 0.0f;
     // per-head spread over its 4 blocks (lanes m, m+16, m+32, m+48)
     int mn = real ? sc : 1 << 20, mx = real ? sc : -(1 << 20);
     mn = min(mn, __shfl_xor(mn, 16, 64)); mx = max(mx, __shfl_xor(mx, 16, 64));
@@ -231,7 +240,9 @@ __device__ __forceinline__ void prep_query(QRow& qs, const QRaw& r, const float*
         smin = min(smin, __shfl_xor(smin, d, 64));
         smax = max(smax, __shfl_xor(smax, d, 64));
     }
-    if (l == 0) { qs.spread = spread; qs.smin = smin; qs.smax = smax; }
+    spread_out = spread;
+    smin_out = smin;
+    smax_out = smax;
 }
 
 // Keys of one batch (IS_TILES tiles of 16) for one lane: 16 code bytes and the
@@ -329,10 +340,15 @@ __device__ __forceinline__ int slice_pte(const KvView& kv, int req, int ncols, i
 }
 
 // MULTI: a full scan whose workgroups take more than one slice of their row;
-// PTE: a full scan of a paged cache (page-table entries loaded ahead)
+// PTE: a full scan of a paged cache (page-table entries loaded ahead).
+// NM = ceil(heads / 4) MFMAs per tile with the query operands in registers,
+// for up to 16 heads; NM = 0: more than 16 heads, in groups of 16 whose
+// operands are read from LDS for each tile, folded in head order.
 template <bool QBF16, bool POOL, int NM, bool MULTI, bool PTE>
 __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, IndexScoreArgs a) {
-    __shared__ QShared qs;
+    constexpr bool GROUPED = NM == 0;
+    constexpr int NMR = GROUPED ? 4 : NM;             // MFMAs per head group
+    __shared__ QShared<GROUPED ? IS_MAX_HEADS : 16> qs;
     const int row = blockIdx.y;
     const int nv = min(a.n_vis[row], a.max_vis);
     const int64_t pool_cap = a.pool_stride < 2048 ? a.pool_stride : 2048;
@@ -354,7 +370,8 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     const int BSTRIDE = 64 * IS_WAVES * Gx;            // columns between a wave's batches
 
     QRaw qraw;
-    if (wave == 0) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads);      // issued before the keys
+    const int ng = GROUPED ? (a.n_heads + 15) >> 4 : 1;   // head groups of 16; wave w prepares group w
+    if (wave < ng) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads, 16 * wave);   // issued before the keys
     KeyBatch A, B;
     int pte = PTE && !POOL ? slice_pte(kv, req, ncols, wbase, BSTRIDE, TSTRIDE, l) : 0;
     load_batch<POOL, PTE && !POOL>(kv, req, pool, nullptr, 0, nv, ncols, wbase, TSTRIDE, n, lg, A, pte);   // in flight during the query prep
@@ -364,24 +381,42 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
         const int gi = t == IS_CHUNK / 8 ? 0 : 8 * IS_WAVES * ((int)blockIdx.x + Gx * (t >> 5)) + (t & 31);
         qs.pool_l[t] = gi < (ncols >> 3) ? pool[gi] : 0;
     }
-    if (wave == 0) prep_query<QBF16>(qs.q, qraw, a.w, row, a.n_heads);
+    if (wave < ng) {
+        int sp, mn, mx;
+        prep_query<QBF16>(qs.q, qraw, a.w, row, a.n_heads, 16 * wave, sp, mn, mx);
+        if (l == 0) {
+            if (GROUPED) { qs.st[wave][0] = sp; qs.st[wave][1] = mn; qs.st[wave][2] = mx; }
+            else { qs.q.spread = sp; qs.q.smin = mn; qs.q.smax = mx; }
+        }
+    }
     if (threadIdx.x == 0) qs.n_fix = 0;
     __syncthreads();
 
     // MFMA k takes heads 4k .. 4k+3 on every row group: row n carries head 4k + (n & 3)
-    i32x8 Aq[NM];
-    int sa[NM];
-    float wl[4 * NM];
+    i32x8 Aq[NMR];
+    int sa[NMR];
+    float wl[4 * NMR];
+    auto group_operands = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < NM; ++k) {
-        const int h = 4 * k + (n & 3);
-        const uint4 v = *(const uint4*)&qs.q.codes[h][16 * lg];
-        Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sa[k] = qs.q.scales[h][lg];
+        for (int k = 0; k < NMR; ++k) {
+            const int h = 16 * g + 4 * k + (n & 3);
+            const uint4 v = *(const uint4*)&qs.q.codes[h][16 * lg];
+            Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            sa[k] = qs.q.scales[h][lg];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.q.w[4 * k + i];   // 0 above n_heads
+            for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.q.w[16 * g + 4 * k + i];   // 0 above n_heads
+        }
+    };
+    if (!GROUPED) group_operands(0);
+    int qspread, qmin, qmax;
+    if (GROUPED) {
+        qspread = 0; qmin = 1 << 20; qmax = -(1 << 20);
+        for (int g = 0; g < ng; ++g) {
+            qspread = max(qspread, qs.st[g][0]); qmin = min(qmin, qs.st[g][1]); qmax = max(qmax, qs.st[g][2]);
+        }
+    } else {
+        qspread = qs.q.spread; qmin = qs.q.smin; qmax = qs.q.smax;
     }
-    const int qspread = qs.q.spread, qmin = qs.q.smin, qmax = qs.q.smax;
     float* srow = a.scores ? a.scores + (int64_t)row * a.scores_stride : nullptr;
     float* brow = (!POOL && a.block_max) ? a.block_max + (int64_t)row * a.block_max_stride : nullptr;
     const int nv8 = (nv + 7) & ~7;
@@ -401,25 +436,29 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             const i32x8 Bk = {(int)kb.code[t].x, (int)kb.code[t].y, (int)kb.code[t].z, (int)kb.code[t].w, 0, 0, 0, 0};
             const uint32_t sd = kb.scl[t];
             const int sb = (int)((sd >> (8 * lg)) & 0xFFu);
-            f32x4 d[NM];
+            float acc = 0.0f;
+            // heads in groups of 16 (one group below 17 heads), folded in order
+            for (int g = 0; g < ng; ++g) {
+                if (GROUPED) group_operands(g);
+                f32x4 d[NMR];
 #pragma unroll
-            for (int k = 0; k < NM; ++k) {
-                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[k], Bk, z, 4, 4, 0, sa[k], 0, sb);
+                for (int k = 0; k < NMR; ++k) {
+                    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[k], Bk, z, 4, 4, 0, sa[k], 0, sb);
+                }
+                // An MFMA takes operands from all 64 lanes: an opaque use pins it in
+                // wave-uniform control flow (the compiler may otherwise sink it into
+                // a lane-masked branch, where it returns wrong sums).
+#pragma unroll
+                for (int k = 0; k < NMR; ++k) asm volatile("" : "+a"(d[k]));
+#pragma unroll
+                for (int k = 0; k < NMR; ++k)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = fmaf(wl[4 * k + i], relu_bits(d[k][i]), acc);
             }
-            // An MFMA takes operands from all 64 lanes: an opaque use pins it in
-            // wave-uniform control flow (the compiler may otherwise sink it into
-            // a lane-masked branch, where it returns wrong sums).
-#pragma unroll
-            for (int k = 0; k < NM; ++k) asm volatile("" : "+a"(d[k]));
             const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
             const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
             const bool ok = (kmax - kmin + qspread <= 9) && (qmin + kmin >= 136) && (qmax + kmax <= 356);
-            float acc = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NM; ++k)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = fmaf(wl[4 * k + i], relu_bits(d[k][i]), acc);
             acc = (acc == 0.0f) ? 0.0f : acc;
             const int col = col0 + n;
             const bool in_cols = col < ncols;
@@ -558,8 +597,12 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvVie
 #pragma unroll
         for (int j = 0; j < PER; ++j) load_query<QBF16>(qraw[j], a.q_idx, min(r0 + wave + IS_WAVES * j, a.n_rows - 1), a.n_heads);
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-            prep_query<QBF16>(sh.q[wave + IS_WAVES * j], qraw[j], a.w, min(r0 + wave + IS_WAVES * j, a.n_rows - 1), a.n_heads);
+        for (int j = 0; j < PER; ++j) {
+            QRow& qr = sh.q[wave + IS_WAVES * j];
+            int sp, mn, mx;
+            prep_query<QBF16>(qr, qraw[j], a.w, min(r0 + wave + IS_WAVES * j, a.n_rows - 1), a.n_heads, 0, sp, mn, mx);
+            if (l == 0) { qr.spread = sp; qr.smin = mn; qr.smax = mx; }
+        }
     }
     if (threadIdx.x == 0) sh.n_fix = 0;
     __syncthreads();
@@ -682,7 +725,8 @@ static void launch_nm(int nm, dim3 grid, dim3 block, hipStream_t st, const KvVie
         case 1: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 1, MULTI, PTE>), grid, block, 0, st, kv, a); break;
         case 2: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 2, MULTI, PTE>), grid, block, 0, st, kv, a); break;
         case 3: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 3, MULTI, PTE>), grid, block, 0, st, kv, a); break;
-        default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+        case 4: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+        default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 0, MULTI, PTE>), grid, block, 0, st, kv, a); break;
     }
 }
 

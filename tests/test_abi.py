@@ -102,7 +102,7 @@ def test_index_score_rejects():
     f = L.csa2_index_score
     B = ctypes.byref
     assert f(None, B(rows), 256, 0, 8, 256, None, 0, None, 256, 104, None, 0, None) == 1
-    assert f(B(kv), B(rows), 256, 0, 17, 256, None, 0, None, 256, 104, None, 0, None) == 5
+    assert f(B(kv), B(rows), 256, 0, 65, 256, None, 0, None, 256, 104, None, 0, None) == 5    # 65 heads
     assert f(B(kv), B(rows), 256, 0, 0, 256, None, 0, None, 256, 104, None, 0, None) == 5
     assert f(B(kv), B(rows), 256, 0, 8, 256, None, 0, None, 256, 99, None, 0, None) == 2
     assert f(B(kv), B(rows), 256, 0, 8, 256, None, 0, None, None, 0, None, 0, None) == 1

@@ -122,9 +122,12 @@ def _score_setup(n_rows, n, Hi, spread=False, zero_groups=False):
     return keys, q, w, kc, ks
 
 
-@pytest.mark.parametrize("Hi", [1, 3, 8, 16])
+@pytest.mark.parametrize("Hi", [1, 3, 8, 16, 17, 24, 32, 64])
 @pytest.mark.parametrize("spread", [False, True])
 def test_index_score_full_exact(Hi, spread):
+    """Full scan, bit-exact against the oracle for 1 .. 64 indexer heads (more
+    than 16 run in groups of 16 folded in head order), with and without wide
+    exponent spreads (the exact path), ragged visible counts."""
     n_rows, n = 3, 5000
     keys, q, w, kc, ks = _score_setup(n_rows, n, Hi, spread=spread, zero_groups=spread)
     n_vis = np.array([n, 4093, 17], np.int32)
@@ -282,12 +285,13 @@ def test_index_score_bf16_query_and_fp32_agree():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("paged", [False, True])
-@pytest.mark.parametrize("spread", [False, True])
-def test_index_score_pool_exact(paged, spread):
+@pytest.mark.parametrize("paged,spread,Hi", [(False, False, 8), (False, True, 8), (True, False, 8), (True, True, 8),
+                                             (False, False, 64), (True, True, 40)])
+def test_index_score_pool_exact(paged, spread, Hi):
     """Pool re-scoring.  Without the exponent spread every key takes the MFMA
-    path (a full 2,048-block pool on row 0); with it most take the exact one."""
-    n_rows, n, Hi = 2, 17000, 8
+    path (a full 2,048-block pool on row 0); with it most take the exact one.
+    40 and 64 heads run in groups of 16."""
+    n_rows, n = 2, 17000
     keys, q, w, kc, ks = _score_setup(n_rows, n, Hi, spread=spread)
     n_vis = np.array([17000, 8997], np.int32)
     pools = np.full((n_rows, 2048), -1, np.int32)
