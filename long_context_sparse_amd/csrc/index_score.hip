@@ -29,8 +29,9 @@
 //   * Each MFMA row group (rows 4g..4g+3) is given the same 4 query heads, so
 //     every lane receives those 4 heads of its key; ceil(n_heads/4) MFMAs per
 //     16 keys hand each lane all heads of its key, and the sequential fma fold
-//     runs inside the lane with no cross-lane traffic.  The block maximum over
-//     8 aligned keys uses DPP row shifts.
+//     runs inside the lane with no cross-lane traffic (more than 16 heads: in
+//     groups of 16, the fold continuing from group to group).  The block
+//     maximum over 8 aligned keys uses DPP row shifts.
 #include <algorithm>
 #include <type_traits>
 
@@ -165,7 +166,7 @@ __device__ float exact_key_score(const uint8_t (*qcodes)[64], const uint8_t (*qs
     return acc == 0.0f ? 0.0f : acc;
 }
 
-// The row's indexer query, raw: lane (head m = l%16, block g = l/16) holds
+// The row's indexer query, raw: lane (head hoff + l%16, block g = l/16) holds
 // the 32 channels it will quantise, as 16 bf16 pairs or 32 floats.
 struct QRaw {
     uint32_t w[32];
