@@ -230,7 +230,12 @@ csa2_status csa2_select_full(const float* block_max, int64_t block_max_stride,
  * 256-B aligned, no initialisation, not kept between calls.  With it, a call
  * with few rows spreads each row's entry list over several workgroups and
  * joins their partial results in a second pass; without it (or when the size
- * is 0) every row and group of 16 heads is one workgroup. */
+ * is 0) every row and group of 16 heads is one workgroup.  Either way a row's
+ * outputs are the same bits, whatever the other rows of the call: its entry
+ * list (selected entries padded to a multiple of 64, then the window) is cut
+ * into units of 192 entries whose softmax max and sum start afresh, and the
+ * units are joined left to right by one fixed sequence of operations
+ * (bitwise batch invariance, 'DeepSeek-V4' page, section 3.3). */
 size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads);
 
 /* Selected entries only: o_partial / lse of the sparse branch. */

@@ -12,15 +12,21 @@
 // MI355X mapping
 //   * A row's entry list is its selected FP4 entries padded to a multiple of
 //     64, then its window entries; it is walked in chunks of 64 with an
-//     online softmax.  One workgroup takes (row, group of 16 heads, split):
-//     without a workspace there is one split and the workgroup writes the
-//     final output; with one, a launch with few rows gives each (row, group)
-//     up to 8 splits of consecutive chunks (so the grid reaches about 256
-//     workgroups), each split writes its normalised partial output with its
-//     running max and sum, and attn_merge_kernel joins the splits (and, in the
-//     two-call form, the other branch's partial and the sink) in a fixed
-//     order.  Workgroups are numbered so that a row's workgroups share one
-//     XCD and its gathered entries one L2.
+//     online softmax.  Every 3 chunks form a unit (at most 4 per row) whose
+//     max, sum and output start afresh; the units are joined left to right
+//     by one fold.  One workgroup takes (row, group of 16 heads, split):
+//     without a workspace there is one split, which folds its units as it
+//     goes and writes the final output; with one, a launch with few rows
+//     gives each (row, group) up to 4 splits of consecutive units (so the
+//     grid reaches about 256 workgroups), each writes its units' partials,
+//     and attn_merge_kernel folds them in unit order (then joins, in the
+//     two-call form, the other branch's partial, and the sink) with the same
+//     operations.  A row's result therefore depends neither on the other
+//     rows of the call nor on the split count: the bitwise batch invariance
+//     of the decode step ['DeepSeek-V4' page, section 3.3, "Batch
+//     Invariance": a split form keeps the accumulation order of the
+//     single-workgroup form].  Workgroups are numbered so that a row's
+//     workgroups share one XCD and its gathered entries one L2.
 //   * 8 waves: wave w dequantises entries 16(w%4)..+15 of the chunk over the
 //     channel half w/4 straight into registers as the A operand of
 //     S^T = K q^T (V_MFMA_F32_16X16X32_F16), and stores the same values
@@ -55,7 +61,9 @@ constexpr int AT_WAVES = 8;
 constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int V_LD = 512 + 16;          // fp16 elements per entry row of V in LDS (32 B pad spreads the banks)
 constexpr int AT_MAX_SEL = 512;
-constexpr int AT_MAX_SPLITS = 8;        // workgroups sharing one (row, head group)
+constexpr int AT_UNIT = 3;              // chunks per unit of the fixed fold
+constexpr int AT_MAX_UNITS = (AT_MAX_SEL / AT_ENT + 128 / AT_ENT + AT_UNIT - 1) / AT_UNIT;   // 4
+constexpr int AT_MAX_SPLITS = AT_MAX_UNITS;   // workgroups sharing one (row, head group)
 
 struct AttnSmem {
     _Float16 v[2][AT_ENT * V_LD];       // the chunk's dequantised entries [entry][channel], double-buffered
@@ -234,6 +242,54 @@ __device__ __forceinline__ int xcd_order(int b, int total) {
     return base + k;
 }
 
+// Units of a row's entry list: ceil(chunks / 3), chunks = ceil(selected / 64)
+// + ceil(window / 64).
+__device__ __forceinline__ int row_units(const AttnArgs& a, int nsp_raw, int nsw_raw) {
+    const int nsp = a.idx ? min(max(nsp_raw, 0), AT_MAX_SEL) : 0;
+    const int nsw = a.swa_codes ? min(max(nsw_raw, 0), 128) : 0;
+    const int ctot = (nsp + AT_ENT - 1) / AT_ENT + (nsw + AT_ENT - 1) / AT_ENT;
+    return (ctot + AT_UNIT - 1) / AT_UNIT;
+}
+
+// The fold of one unit (base-2 max m, sum l, output o = sum of 2^(z - m) E,
+// unnormalised) into the running (M, L, O), in unit order:
+//   M' = max(M, m),  L' = 2^(m - M') l + 2^(M - M') L,  O' likewise.
+// attn_kernel and attn_merge_kernel both call these two functions, with
+// explicit fma so that no contraction differs between them.
+struct FoldW { float wa, wb; };
+__device__ __forceinline__ FoldW fold_unit(float& M, float& L, float m, float l) {
+    const float Mn = fmaxf(M, m);
+    const float wa = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float wb = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - Mn);
+    L = fmaf(wb, l, wa * L);
+    M = Mn;
+    return {wa, wb};
+}
+__device__ __forceinline__ f32x4 fold_out(const FoldW& f, f32x4 O, f32x4 o) {
+    return (f32x4){fmaf(f.wb, o[0], f.wa * O[0]), fmaf(f.wb, o[1], f.wa * O[1]), fmaf(f.wb, o[2], f.wa * O[2]),
+                   fmaf(f.wb, o[3], f.wa * O[3])};
+}
+
+// The end of a row and head: the folded units (M, L, O), an external partial
+// (lse_p, o_in: base-2 log-sum-exp and normalised output) and the sink sk
+// (base 2) in one denominator:
+//   out = (2^(M - X) O + 2^(lse_p - X) o_in) / (2^(M - X) L + 2^(lse_p - X) + 2^(sk - X)),
+// X the largest of the three; lse2 the base-2 log-sum-exp (-inf if empty).
+struct FinalW { float wo, wp, inv, lse2; };
+__device__ __forceinline__ FinalW final_weights(float M, float L, float lse_p, float sk) {
+    const float X = fmaxf(fmaxf(M, lse_p), sk);
+    const float wo = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - X);
+    const float wp = lse_p == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lse_p - X);
+    const float ws = sk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sk - X);
+    const float den = fmaf(wo, L, wp) + ws;
+    const bool empty = X == -INFINITY || den == 0.0f;
+    return {wo, wp, empty ? 0.0f : 1.0f / den, empty ? -INFINITY : X + log2f(den)};
+}
+__device__ __forceinline__ f32x4 final_out(const FinalW& f, f32x4 O, float4 pin) {
+    return (f32x4){fmaf(f.wo, O[0], f.wp * pin.x) * f.inv, fmaf(f.wo, O[1], f.wp * pin.y) * f.inv,
+                   fmaf(f.wo, O[2], f.wp * pin.z) * f.inv, fmaf(f.wo, O[3], f.wp * pin.w) * f.inv};
+}
+
 template <bool QBF16>
 __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a) {
     extern __shared__ __align__(16) uint8_t at_smem[];
@@ -250,7 +306,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int nsw = a.swa_codes ? min(max(a.swa_count[row], 0), 128) : 0;
     const int csp = (nsp + AT_ENT - 1) / AT_ENT;
     const int ctot = csp + (nsw + AT_ENT - 1) / AT_ENT;
-    const int cb = split * ctot / S, ce = (split + 1) * ctot / S;   // this split's chunks
+    const int U = (ctot + AT_UNIT - 1) / AT_UNIT;
+    const int ub = split * U / S, ue = (split + 1) * U / S;         // this split's units
+    const int cb = AT_UNIT * ub, ce = min(AT_UNIT * ue, ctot);      // and chunks
+    if (S > 1 && ue == ub) return;                                  // a short row: no unit here
     const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
     // The cache slots of the selected entries (the index is read before its
@@ -322,7 +381,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     f32x4 oacc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;            // base-2 running max and sum
+    float m_run = -INFINITY, l_run = 0.0f;            // base-2 running max and sum of the unit
     const int chb = 256 * kh + 64 * g;               // first of this lane's 64 dequant channels
     const int v_lane = (16 * et + n) * V_LD + chb;  // this lane's entry row and channels in LDS
 
@@ -398,11 +457,46 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         __syncthreads();
     };
 
+    // The end of unit u: with several splits its partial (output without the
+    // 2^tw, unnormalised, and its max and sum) goes to the workspace, else it
+    // is folded into (Mf, Lf, Of); the next unit starts afresh.
+    const int h = h0 + n;
+    const float pw = __uint_as_float((uint32_t)(127 - tw) << 23);   // 2^-tw (exact)
+    float Mf = -INFINITY, Lf = 0.0f;
+    f32x4 Of[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) Of[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    auto end_unit = [&](const int u) __attribute__((always_inline)) {
+        if (S > 1) {
+            const size_t ps = ((size_t)row * a.n_heads + h) * AT_MAX_UNITS + u;
+            float* wsO = a.ws;
+            float* wsM = wsO + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS * 512;
+            float* wsL = wsM + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                // partials are written once and read by another kernel:
+                // non-temporal stores stream them out instead of leaving them
+                // dirty in L2 for the end-of-kernel write-back
+                __builtin_nontemporal_store(oacc[ct] * pw, (f32x4*)(wsO + ps * 512 + 64 * wave + 16 * ct + 4 * g));
+            if (wave == 0 && g == 0) { wsM[ps] = m_run; wsL[ps] = l_run; }
+        } else {
+            const FoldW f = fold_unit(Mf, Lf, m_run, l_run);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) Of[ct] = fold_out(f, Of[ct], oacc[ct] * pw);
+        }
+        m_run = -INFINITY;
+        l_run = 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    static_assert(AT_UNIT == 3, "a unit is one turn of the three-step loop");
     if (ce > cb) {
         if (cb < csp) stage_a(SEL, cb, raw0);
         else stage_a(WIN, cb, raw0);
         __syncthreads();
         for (int c = cb;; c += 3) {
+            if (c > cb) end_unit(c / AT_UNIT - 1);    // c starts a unit
             if (c + 1 >= ce) { stage_b(c); break; }
             step(c, raw1);
             if (c + 2 >= ce) { stage_b(c + 1); break; }
@@ -410,110 +504,67 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
             if (c + 3 >= ce) { stage_b(c + 2); break; }
             step(c + 2, raw0);
         }
+        end_unit((ce - 1) / AT_UNIT);
     }
-
-    const int h = h0 + n;
-    if (S > 1) {
-        // ---- one split of several: its normalised partial (fp32, without the
-        // 2^tw) and its base-2 max and sum; attn_merge_kernel joins them
-        const size_t ps = ((size_t)row * a.n_heads + h) * S + split;
-        float* wsO = a.ws;
-        float* wsM = wsO + (size_t)a.n_rows * a.n_heads * S * 512;
-        float* wsL = wsM + (size_t)a.n_rows * a.n_heads * S;
-        const float inv = l_run > 0.0f ? ldexpf(1.0f / l_run, -tw) : 0.0f;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const int ch = 64 * wave + 16 * ct + 4 * g;
-            // partials and outputs are written once and read by another kernel:
-            // non-temporal stores stream them out instead of leaving them dirty
-            // in L2 for the end-of-kernel write-back
-            __builtin_nontemporal_store((f32x4){oacc[ct][0] * inv, oacc[ct][1] * inv, oacc[ct][2] * inv, oacc[ct][3] * inv},
-                                        (f32x4*)(wsO + ps * 512 + ch));
-        }
-        if (wave == 0 && g == 0) { wsM[ps] = m_run; wsL[ps] = l_run; }
-        return;
-    }
-
-    // ---- epilogue: join an external partial (o_in, lse_in) and the sink; write
-    // O^T[64*wave + 16ct + 4g + i][head h0 + n].  Natural-log terms become
-    // base 2 with log2(e); oacc carries the entries' 2^tw.
+    if (S > 1) return;
+    // ---- epilogue: the folded units, an external partial (o_in, lse_in) and
+    // the sink in one denominator; write O^T[64*wave + 16ct + 4g + i][head
+    // h0 + n].  Natural-log terms become base 2 with log2(e).
     const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * a.n_heads + h] * LOG2E : -INFINITY;
     const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
-    const float M = fmaxf(fmaxf(m_run, lse_p), sk);
-    const float w_run = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-    const float w_p = (lse_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lse_p - M);
-    const float w_s = (sk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sk - M);
-    const float den = w_run * l_run + w_p + w_s;
-    const float inv = (M == -INFINITY || den == 0.0f) ? 0.0f : 1.0f / den;
-    const float wo = ldexpf(w_run, -tw);
+    const FinalW fw = final_weights(Mf, Lf, lse_p, sk);
     const float* oin = a.o_in ? a.o_in + ((int64_t)row * a.n_heads + h) * 512 : nullptr;
     float* orow = a.out + ((int64_t)row * a.n_heads + h) * 512;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         const int ch = 64 * wave + 16 * ct + 4 * g;
         const float4 pin = oin ? *(const float4*)(oin + ch) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        float4 r;
-        r.x = (wo * oacc[ct][0] + w_p * pin.x) * inv;
-        r.y = (wo * oacc[ct][1] + w_p * pin.y) * inv;
-        r.z = (wo * oacc[ct][2] + w_p * pin.z) * inv;
-        r.w = (wo * oacc[ct][3] + w_p * pin.w) * inv;
-        __builtin_nontemporal_store((f32x4){r.x, r.y, r.z, r.w}, (f32x4*)(orow + ch));
+        __builtin_nontemporal_store(final_out(fw, Of[ct], pin), (f32x4*)(orow + ch));
     }
-    if (a.lse_out && wave == 0 && g == 0)
-        a.lse_out[(int64_t)row * a.n_heads + h] = (M == -INFINITY || den == 0.0f) ? -INFINITY : (M + log2f(den)) * LN2;
+    if (a.lse_out && wave == 0 && g == 0) a.lse_out[(int64_t)row * a.n_heads + h] = fw.lse2 * LN2;
 }
 
-// Joins the splits of every (row, head): out = (sum_s 2^(m_s - M) l_s o_s
-// + e^(lse_in - M') o_in) / (sum_s 2^(m_s - M) l_s + e^(lse_in) + e^(sink)),
-// all in base 2.  One thread per (row, head, 4 channels); every load is
-// issued before any is used.
+// Folds the unit partials of every (row, head) in unit order, then joins the
+// external partial and the sink: the same operations as the epilogue of a
+// single-split attn_kernel.  One thread per (row, head, 4 channels); every
+// load is issued before any is used (slots past the row's unit count are
+// read but not folded).
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
-    const int S = a.n_splits;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (int64_t)a.n_rows * a.n_heads * 128) return;
     const int64_t rh = t >> 7;                        // row * n_heads + head
     const int c4 = (int)(t & 127) * 4;
-    const int h = (int)(rh % a.n_heads);
+    const int row = (int)(rh / a.n_heads), h = (int)(rh - (int64_t)row * a.n_heads);
     const float* wsO = a.ws;
-    const float* wsM = wsO + (size_t)a.n_rows * a.n_heads * S * 512;
-    const float* wsL = wsM + (size_t)a.n_rows * a.n_heads * S;
-    float m[AT_MAX_SPLITS], lw[AT_MAX_SPLITS];
-    float4 o[AT_MAX_SPLITS];
+    const float* wsM = wsO + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS * 512;
+    const float* wsL = wsM + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS;
+    const int nsp_raw = a.idx ? a.idx_count[row] : 0;
+    const int nsw_raw = a.swa_codes ? a.swa_count[row] : 0;
+    float m[AT_MAX_UNITS], lw[AT_MAX_UNITS];
+    f32x4 o[AT_MAX_UNITS];
 #pragma unroll
-    for (int s = 0; s < AT_MAX_SPLITS; ++s) {
-        const int sc = s < S ? s : S - 1;             // loads stay unconditional
-        m[s] = wsM[rh * S + sc];
-        lw[s] = wsL[rh * S + sc];
-        o[s] = *(const float4*)(wsO + (rh * S + sc) * 512 + c4);
+    for (int u = 0; u < AT_MAX_UNITS; ++u) {
+        m[u] = wsM[rh * AT_MAX_UNITS + u];
+        lw[u] = wsL[rh * AT_MAX_UNITS + u];
+        o[u] = *(const f32x4*)(wsO + (rh * AT_MAX_UNITS + u) * 512 + c4);
     }
     const float lse_p = a.lse_in ? a.lse_in[rh] * LOG2E : -INFINITY;
     const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
-    float M = fmaxf(lse_p, sk);
+    const float4 pin = a.o_in ? *(const float4*)(a.o_in + rh * 512 + c4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int U = row_units(a, nsp_raw, nsw_raw);
+    float M = -INFINITY, L = 0.0f;
+    f32x4 O = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < AT_MAX_SPLITS; ++s) if (s < S) M = fmaxf(M, m[s]);
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float den = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int s = 0; s < AT_MAX_SPLITS; ++s) {
-            if (s >= S || m[s] == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f(m[s] - M) * lw[s];
-            den += w;
-            acc.x += w * o[s].x; acc.y += w * o[s].y; acc.z += w * o[s].z; acc.w += w * o[s].w;
+    for (int u = 0; u < AT_MAX_UNITS; ++u) {
+        if (u < U) {
+            const FoldW f = fold_unit(M, L, m[u], lw[u]);
+            O = fold_out(f, O, o[u]);
         }
-        if (lse_p != -INFINITY) {
-            const float w = __builtin_amdgcn_exp2f(lse_p - M);
-            const float4 pin = *(const float4*)(a.o_in + rh * 512 + c4);
-            den += w;
-            acc.x += w * pin.x; acc.y += w * pin.y; acc.z += w * pin.z; acc.w += w * pin.w;
-        }
-        if (sk != -INFINITY) den += __builtin_amdgcn_exp2f(sk - M);
     }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    __builtin_nontemporal_store((f32x4){acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv},
-                                (f32x4*)(a.out + rh * 512 + c4));
-    if (a.lse_out && c4 == 0) a.lse_out[rh] = den > 0.0f ? (M + log2f(den)) * LN2 : -INFINITY;
+    const FinalW fw = final_weights(M, L, lse_p, sk);
+    __builtin_nontemporal_store(final_out(fw, O, pin), (f32x4*)(a.out + rh * 512 + c4));
+    if (a.lse_out && c4 == 0) a.lse_out[rh] = fw.lse2 * LN2;
 }
 
 int attn_splits(int n_rows, int n_heads) {
@@ -523,9 +574,10 @@ int attn_splits(int n_rows, int n_heads) {
     return s < 2 ? 1 : (s > AT_MAX_SPLITS ? AT_MAX_SPLITS : s);
 }
 
+// one partial per unit, whatever the split count
 size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits) {
     if (n_splits <= 1) return 0;
-    return (size_t)n_rows * n_heads * n_splits * (512 + 2) * sizeof(float);
+    return (size_t)n_rows * n_heads * AT_MAX_UNITS * (512 + 2) * sizeof(float);
 }
 
 // The kernels' dynamic LDS above 64 KB is allowed once per device (the flag

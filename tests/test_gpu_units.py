@@ -623,6 +623,75 @@ def test_attention_workspace_reuse():
             assert tolerance_ok(Or[r], fo), (n, h, r, np.abs(Or[r] - fo).max())
 
 
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_batch_invariant(H):
+    """A row's output and log-sum-exp are the same bits whatever the other
+    rows of the call, the split count and whether a workspace is given
+    ('DeepSeek-V4' page, section 3.3, batch invariance): 16 ragged rows with a
+    sink, in the one-pass form, alone, in calls of 16, 32, 80 and 300 rows
+    (4, 4 or 2, 3 or 1, 1 splits) and without a workspace; the two-call form
+    likewise; and within the tolerance of the oracle."""
+    n_all, n_entries = 300, 520
+    lat = bf16(RNG.standard_normal((n_all * n_entries, 512)).astype(np.float32)).float().numpy()
+    mc, ms = oracle.pack_main(lat)
+    swa = bf16(RNG.standard_normal((n_all * 128, 512)).astype(np.float32)).float().numpy()
+    wc, wsc = oracle.pack_swa(swa)
+    q = bf16(RNG.standard_normal((n_all, H, 512)).astype(np.float32) * 2)
+    counts = RNG.integers(0, 513, n_all).astype(np.int32)
+    swa_counts = RNG.integers(0, 129, n_all).astype(np.int32)
+    counts[:16] = [512, 300, 0, 64, 1, 129, 448, 192, 512, 0, 65, 511, 384, 193, 2, 512]
+    swa_counts[:16] = [128, 0, 70, 1, 128, 64, 65, 0, 127, 0, 128, 3, 128, 128, 1, 64]
+    idx = np.full((n_all, 512), -1, np.int32)
+    for r in range(n_all):
+        idx[r, :counts[r]] = np.sort(RNG.permutation(n_entries)[:counts[r]])
+    sk = T((RNG.standard_normal(H) * 3).astype(np.float32))
+    kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), n_slots=n_all * n_entries, req_stride=n_entries)
+    qd, idx_d, cnt_d = q.to(DEV), T(idx), T(counts)
+    wc_d, wsc_d = T(wc), T(wsc)
+    first_d, swc_d = T(np.arange(n_all, dtype=np.int64) * 128), T(swa_counts)
+
+    def call(r0, n, use_ws):
+        """Rows r0 .. r0 + n - 1 in one call of each form: (out, lse, two-call out, sparse o, sparse lse)."""
+        rows = lib.make_rows(T(np.arange(r0, r0 + n, dtype=np.int32)), T(np.full(n, n_entries, np.int32)), n_entries)
+        wsb = lib.csa2_attn_workspace_size(n, H) if use_ws else 0
+        ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV) if wsb else None
+        sl = slice(r0, r0 + n)
+        out = torch.empty((n, H, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((n, H), dtype=torch.float32, device=DEV)
+        lib.csa2_sparse_swa_attn(kv, rows, qd[sl].contiguous(), idx_d[sl].contiguous(), cnt_d[sl].contiguous(), wc_d,
+                                 wsc_d, first_d[sl].contiguous(), swc_d[sl].contiguous(), SIG, out, sink=sk, lse=lse,
+                                 workspace=ws)
+        o_p = torch.empty((n, H, 512), dtype=torch.float32, device=DEV)
+        l_p = torch.empty((n, H), dtype=torch.float32, device=DEV)
+        lib.csa2_sparse_attn(kv, rows, qd[sl].contiguous(), idx_d[sl].contiguous(), cnt_d[sl].contiguous(), SIG, o_p,
+                             l_p, workspace=ws)
+        out2 = torch.empty((n, H, 512), dtype=torch.float32, device=DEV)
+        lib.csa2_swa_merge(wc_d, wsc_d, first_d[sl].contiguous(), swc_d[sl].contiguous(), qd[sl].contiguous(), SIG,
+                           out2, sink=sk, o_partial=o_p, lse=l_p, workspace=ws)
+        torch.cuda.synchronize()
+        return [t.cpu() for t in (out, lse, out2, o_p, l_p)]
+
+    ref = call(0, 16, True)
+    cases = {"no workspace": call(0, 16, False), "32 rows": call(0, 32, True), "80 rows": call(0, 80, True),
+             "300 rows": call(0, n_all, True)}
+    for r in (0, 2, 5, 9, 13):
+        one = call(r, 1, True)
+        ref_r = [t[r:r + 1] for t in ref]
+        for k, (a, b) in enumerate(zip(one, ref_r)):
+            assert torch.equal(a, b), (r, k)
+    for name, got in cases.items():
+        for k, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a[:16], b), (name, k)
+    K = oracle.dequant_main(mc, ms)
+    W = oracle.dequant_swa(wc, wsc)
+    qn, skn = q.float().numpy(), sk.cpu().numpy()
+    for r in (0, 3, 11):
+        fo, fl = oracle.attention(qn[r], K[r * n_entries + idx[r, :counts[r]]], W[r * 128:r * 128 + swa_counts[r]],
+                                  sink=skn, sigma=SIG)
+        assert tolerance_ok(ref[0][r].numpy(), fo), (r, np.abs(ref[0][r].numpy() - fo).max())
+        assert np.allclose(ref[1][r].numpy(), fl, rtol=1e-5, atol=1e-5)
+
+
 def test_swa_only_and_alias():
     n_rows, H = 2, 16
     swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
