@@ -13,8 +13,10 @@ the 143 MB key stream from one step to the next.
 Prints one JSON line: the whole-step throughput in (request x head) decodes
 per second, the per-kernel breakdown, the roofline object of the indexer scan
 (algorithmic bytes per launch over its event-timed average duration, and the
-HBM bytes the counter runs measured for it) and the oracle's CPU rate on a
-bounded sample of the same workload.
+HBM bytes the counter runs measured for it), the rate of a plain streaming
+read of the same key bytes on the same buffers (the ceiling the indexer is
+compared with) and the oracle's CPU rate on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -208,6 +210,25 @@ def main():
             per[n].append(a.elapsed_ms(b) * 1e3)
     kernels_us = {n: round(float(np.median(v)), 2) for n, v in per.items()}
 
+    # ---- streaming-read ceiling (separate, untimed): the plain non-temporal
+    # read of the indexer's key-code plane, the same rotated buffers, one
+    # launch each, HIP events as for the indexer
+    planes = [kv._refs[2] for kv in wl.kvs]
+    xo = torch.zeros(lib.STREAM_XOR_WORDS, dtype=torch.int32, device=dev)
+    for i in range(4):
+        lib.csa2_stream_xor(planes[i % len(planes)], xo)
+    rd = []
+    for i in range(20):
+        a, b = HipEvent(), HipEvent()
+        a.record()
+        lib.csa2_stream_xor(planes[i % len(planes)], xo)
+        b.record()
+        rd.append((a, b))
+    torch.cuda.synchronize()
+    rd_us = float(np.mean([a.elapsed_ms(b) for a, b in rd])) * 1e3
+    rd_bytes = planes[0].numel() * planes[0].element_size()
+    rd_gbs = rd_bytes / (rd_us * 1e-6) / 1e9
+
     ms = dt * 1e3 / args.steps
     steps_s = args.steps / dt
     k2_bytes = algo.get("index_keys_full", algo.get("index_keys_pool", 0))
@@ -247,6 +268,15 @@ def main():
             "algorithmic_bytes_per_launch": k2_bytes,
             "avg_launch_us": round(k2_ms * 1e3, 2),
             "launches_timed": len(ev),
+            "frac_of_read_ceiling": round(k2_gbs / rd_gbs, 4),
+        },
+        "read_ceiling": {
+            "kernel": "stream_xor_kernel",
+            "what": "plain streaming read (16-B non-temporal loads) of the indexer's key-code plane, same rotated buffers",
+            "bytes_per_launch": rd_bytes,
+            "avg_launch_us": round(rd_us, 2),
+            "gbs": round(rd_gbs, 1),
+            "frac_of_peak": round(rd_gbs / PEAK_HBM_GBS, 4),
         },
     }
     if not args.no_cpu:

@@ -266,6 +266,18 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
                                  float softmax_scale, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- streaming-read reference
+ * Not a step of the method: the plain streaming read that the indexer scan's
+ * HBM rate is measured against.  Reads the n_bytes of buf once (16-B
+ * non-temporal loads, as the scan reads its keys, by 1,024 workgroups
+ * striding over the buffer); out[g], g < CSA2_STREAM_XOR_WORDS, receives the
+ * XOR of the 32-bit words workgroup g read (0 if none), so the XOR of all
+ * out words is the XOR of the buffer's words.  buf 16-B aligned, n_bytes a
+ * multiple of 16 (0: nothing to do, out untouched), out 4-B aligned with
+ * room for CSA2_STREAM_XOR_WORDS words; device memory owned by the caller. */
+#define CSA2_STREAM_XOR_WORDS 1024
+csa2_status csa2_stream_xor(const void* buf, int64_t n_bytes, uint32_t* out, void* stream);
+
 /* ---------------------------------------------------------------- synthetic inputs
  * Counter-based generator for seeded synthetic inputs (SplitMix64; Steele,
  * Lea & Flood 2014): base = mix64(seed * 0x9E3779B97F4A7C15 + tensor_id),

@@ -48,7 +48,7 @@ EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
     "csa2_index_score_shared",
     "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
-    "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost",
+    "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost", "csa2_stream_xor",
 )
 
 
@@ -82,6 +82,7 @@ def lib():
     L.csa2_synth_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, ctypes.c_int, P, P]
     L.csa2_synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, P, P]
     L.csa2_synth_boost.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, i32, P, P]
+    L.csa2_stream_xor.argtypes = [P, i64, P, P]
     for name in EXPORTS:
         if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_attn_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
@@ -235,6 +236,20 @@ def csa2_synth_normal(seed, tensor_id, first, out, stream=None):
     n = int(out.numel())
     _check("csa2_synth_normal", lib().csa2_synth_normal(int(seed), int(tensor_id), int(first), n,
                                                         _dtype(out), _ptr(out), _stream(stream)))
+
+
+STREAM_XOR_WORDS = 1024
+
+
+def csa2_stream_xor(buf, out, stream=None):
+    """Streaming read of `buf` (device tensor, contiguous, 16-B aligned, size a multiple of 16 B): out[g]
+    (a 32-bit device tensor of STREAM_XOR_WORDS elements) receives the XOR of the words workgroup g read."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if out.numel() * out.element_size() < 4 * STREAM_XOR_WORDS:
+        raise ValueError(f"out must hold {STREAM_XOR_WORDS} 32-bit words")
+    _check("csa2_stream_xor", lib().csa2_stream_xor(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(out),
+                                                    _stream(stream)))
 
 
 def csa2_synth_uniform(seed, tensor_id, first, out, stream=None):

@@ -412,6 +412,15 @@ csa2_status csa2_synth_normal(uint64_t seed, uint32_t tensor_id, int64_t first, 
                       "csa2_synth_normal launch");
 }
 
+csa2_status csa2_stream_xor(const void* buf, int64_t n_bytes, uint32_t* out, void* stream) {
+    if (n_bytes < 0) return fail(CSA2_ERR_RANGE, "n_bytes must be >= 0");
+    if (n_bytes % 16) return fail(CSA2_ERR_SHAPE, "n_bytes must be a multiple of 16");
+    if (n_bytes == 0) return CSA2_OK;
+    if (!buf || !out) return fail(CSA2_ERR_NULL, "buf / out is NULL");
+    if (!aligned(buf, 16) || !aligned(out, 4)) return fail(CSA2_ERR_ALIGN, "buf must be 16-B and out 4-B aligned");
+    return hip_status(csa2::launch_stream_xor(buf, n_bytes, out, (hipStream_t)stream), "csa2_stream_xor launch");
+}
+
 csa2_status csa2_synth_uniform(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n, float* out, void* stream) {
     if (n < 0 || first < 0) return fail(CSA2_ERR_RANGE, "first / n must be >= 0");
     if (n == 0) return CSA2_OK;

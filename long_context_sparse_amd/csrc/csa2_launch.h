@@ -94,6 +94,8 @@ int attn_splits(int n_rows, int n_heads);
 size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits);
 hipError_t launch_attn(const KvView& kv, const AttnArgs& a, size_t ws_bytes, hipStream_t st);
 
+hipError_t launch_stream_xor(const void* buf, int64_t n_bytes, uint32_t* out, hipStream_t st);
+
 hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,
                                void* out, hipStream_t st);
 hipError_t launch_synth_uniform(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, float* out,

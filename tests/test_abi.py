@@ -159,3 +159,16 @@ def test_attn_rejects():
              None) == 4
     assert h(B(kv), B(rows), 256, 0, 24, 256, 512, 256, 256, 256, 10, 256, 256, None, F, 256, None, None, 0,
              None) == 5
+
+
+def test_stream_xor_rejects():
+    """Host checks of the streaming-read reference (no launch on failure; a
+    zero-byte call does nothing and succeeds)."""
+    f = lib.lib().csa2_stream_xor
+    assert f(256, 0, 256, None) == 0                 # nothing to read
+    assert f(256, -16, 256, None) == 3               # range
+    assert f(256, 24, 256, None) == 2                # not a multiple of 16
+    assert f(None, 32, 256, None) == 1               # buf
+    assert f(256, 32, None, None) == 1               # out
+    assert f(264, 32, 256, None) == 4                # buf alignment
+    assert f(256, 32, 258, None) == 4                # out alignment

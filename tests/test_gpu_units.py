@@ -692,6 +692,22 @@ def test_attention_batch_invariant(H):
         assert np.allclose(ref[1][r].numpy(), fl, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("n_bytes", [16, 4096 + 16, (1 << 20) + 48, 3 * 2048 * 256 * 4 * 16 + 32])
+def test_stream_xor(n_bytes):
+    """The streaming-read reference XORs every 32-bit word of the buffer once
+    (ragged sizes: one word, a partial workgroup, a grid-stride tail past the
+    1,024-workgroup grid)."""
+    host = RNG.integers(0, 2 ** 32, n_bytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = T(host.view(np.int32))
+    out = torch.full((lib.STREAM_XOR_WORDS,), 0x1234, dtype=torch.int32, device=DEV)
+    lib.csa2_stream_xor(buf, out)
+    torch.cuda.synchronize()
+    words = out.cpu().numpy().view(np.uint32)
+    assert np.bitwise_xor.reduce(words) == np.bitwise_xor.reduce(host)
+    if n_bytes <= 4096 + 16:                          # workgroups past the buffer write 0
+        assert not words[n_bytes // 16:].any()
+
+
 def test_swa_only_and_alias():
     n_rows, H = 2, 16
     swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
