@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+LLC_BYTES = 256 << 20             # MI355X Infinity Cache
 METRIC = "CSA2 decode steps/s (batch×heads) at 128K ctx; achieved HBM GB/s vs peak"
 DOMINANT = "index_score"          # the kernel the roofline object describes
 DOMINANT_SRC = os.path.join(ROOT, "long_context_sparse_amd", "csrc", "index_score.hip")
@@ -228,6 +229,9 @@ def main():
     rd_us = float(np.mean([a.elapsed_ms(b) for a, b in rd])) * 1e3
     rd_bytes = planes[0].numel() * planes[0].element_size()
     rd_gbs = rd_bytes / (rd_us * 1e-6) / 1e9
+    # a ceiling of HBM only when the rotated planes exceed the 256 MB
+    # last-level cache (the small workloads' planes are served from it)
+    rd_hbm = sum({p.data_ptr(): p.numel() * p.element_size() for p in planes}.values()) > LLC_BYTES
 
     ms = dt * 1e3 / args.steps
     steps_s = args.steps / dt
@@ -268,9 +272,9 @@ def main():
             "algorithmic_bytes_per_launch": k2_bytes,
             "avg_launch_us": round(k2_ms * 1e3, 2),
             "launches_timed": len(ev),
-            "frac_of_read_ceiling": round(k2_gbs / rd_gbs, 4),
+            "frac_of_read_ceiling": round(k2_gbs / rd_gbs, 4) if rd_hbm else None,
         },
-        "read_ceiling": {
+        "read_ceiling": None if not rd_hbm else {
             "kernel": "stream_xor_kernel",
             "what": "plain streaming read (16-B non-temporal loads) of the indexer's key-code plane, same rotated buffers",
             "bytes_per_launch": rd_bytes,
