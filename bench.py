@@ -214,7 +214,7 @@ def main():
     # ---- streaming-read ceiling (separate, untimed): the plain non-temporal
     # read of the indexer's key-code plane, the same rotated buffers, one
     # launch each, HIP events as for the indexer
-    planes = [kv._refs[2] for kv in wl.kvs]
+    planes = [idx[0] for (_, idx) in wl.kv_copies]      # (codes, scales) of each copy's INDEX entries
     xo = torch.zeros(lib.STREAM_XOR_WORDS, dtype=torch.int32, device=dev)
     for i in range(4):
         lib.csa2_stream_xor(planes[i % len(planes)], xo)

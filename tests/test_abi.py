@@ -172,3 +172,14 @@ def test_stream_xor_rejects():
     assert f(256, 32, None, None) == 1               # out
     assert f(264, 32, 256, None) == 4                # buf alignment
     assert f(256, 32, 258, None) == 4                # out alignment
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: asked for more it exits with status 2 and
+    says why, before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout
