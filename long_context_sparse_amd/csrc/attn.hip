@@ -290,7 +290,10 @@ __device__ __forceinline__ f32x4 final_out(const FinalW& f, f32x4 O, float4 pin)
                    fmaf(f.wo, O[2], f.wp * pin.z) * f.inv, fmaf(f.wo, O[3], f.wp * pin.w) * f.inv};
 }
 
-template <bool QBF16>
+// SPLIT: the launch has several splits per (row, group) (their partials go to
+// the workspace); without it the workgroup folds its units itself, and only
+// that form holds the folded output in registers.
+template <bool QBF16, bool SPLIT>
 __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a) {
     extern __shared__ __align__(16) uint8_t at_smem[];
     AttnSmem& sm = *(AttnSmem*)at_smem;
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int U = (ctot + AT_UNIT - 1) / AT_UNIT;
     const int ub = split * U / S, ue = (split + 1) * U / S;         // this split's units
     const int cb = AT_UNIT * ub, ce = min(AT_UNIT * ue, ctot);      // and chunks
-    if (S > 1 && ue == ub) return;                                  // a short row: no unit here
+    if (SPLIT && ue == ub) return;                                  // a short row: no unit here
     const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
     // The cache slots of the selected entries (the index is read before its
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) Of[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     auto end_unit = [&](const int u) __attribute__((always_inline)) {
-        if (S > 1) {
+        if constexpr (SPLIT) {
             const size_t ps = ((size_t)row * a.n_heads + h) * AT_MAX_UNITS + u;
             float* wsO = a.ws;
             float* wsM = wsO + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS * 512;
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         }
         end_unit((ce - 1) / AT_UNIT);
     }
-    if (S > 1) return;
+    if constexpr (SPLIT) return;
     // ---- epilogue: the folded units, an external partial (o_in, lse_in) and
     // the sink in one denominator; write O^T[64*wave + 16ct + 4g + i][head
     // h0 + n].  Natural-log terms become base 2 with log2(e).
@@ -592,8 +595,10 @@ static hipError_t set_lds_attrs() {
     if (e != hipSuccess) return e;
     const bool cached = dev >= 0 && dev < AT_MAX_DEVICES;
     if (cached && g_attr_set[dev].load(std::memory_order_acquire)) return hipSuccess;
-    if ((e = hipFuncSetAttribute((const void*)attn_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void*)attn_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
+    const void* kernels[4] = {(const void*)attn_kernel<true, false>, (const void*)attn_kernel<false, false>,
+                              (const void*)attn_kernel<true, true>, (const void*)attn_kernel<false, true>};
+    for (const void* k : kernels)
+        if ((e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
     if (cached) g_attr_set[dev].store(true, std::memory_order_release);
     return hipSuccess;
 }
@@ -605,8 +610,11 @@ hipError_t launch_attn(const KvView& kv, const AttnArgs& a_in, size_t ws_bytes, 
     a.n_splits = attn_splits(a.n_rows, a.n_heads);
     if (!a.ws || ws_bytes < attn_workspace_bytes(a.n_rows, a.n_heads, a.n_splits)) a.n_splits = 1;
     const unsigned blocks = (unsigned)a.n_rows * (unsigned)(a.n_heads >> 4) * (unsigned)a.n_splits;
-    if (a.q_bf16) hipLaunchKernelGGL(attn_kernel<true>, dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
-    else hipLaunchKernelGGL(attn_kernel<false>, dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    const bool split = a.n_splits > 1;
+    if (a.q_bf16 && split) hipLaunchKernelGGL((attn_kernel<true, true>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else if (a.q_bf16) hipLaunchKernelGGL((attn_kernel<true, false>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else if (split) hipLaunchKernelGGL((attn_kernel<false, true>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else hipLaunchKernelGGL((attn_kernel<false, false>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
     if ((e = hipGetLastError()) != hipSuccess || a.n_splits == 1) return e;
     const int64_t threads = (int64_t)a.n_rows * a.n_heads * 128;
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
