@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 typedef enum {
     CSA2_OK = 0,
@@ -174,20 +174,31 @@ csa2_status csa2_index_score_shared(const csa2_kv* kv, const csa2_rows* rows, in
  * their maximum, ties to the lower position).
  * Row r has c_r = ceil(n_cols[r] * cols_mul / cols_div) candidate columns
  * (n_cols NULL: max_cols), c_r <= max_cols.  Column c has id
- *   id(c) = c                                          (pool_blocks NULL)
- *   id(c) = 8 * pool_blocks[r * pool_stride + c/8] + c%8   (otherwise)
+ *   id(c) = c                                          (ids and pool_blocks NULL)
+ *   id(c) = ids[r * ids_stride + c]                    (ids given)
+ *   id(c) = 8 * pool_blocks[r * pool_stride + c/8] + c%8   (pool_blocks given)
  * and key keys[r * key_stride + (keys_by_id ? id(c) : c)].  Keys equal to
  * -inf are absent.  The min(k, present) columns first in (key descending,
- * column ascending) are selected; column order must be id order (pool blocks
- * ascending).  Their ids are written ascending to out_ids[r * out_stride ..],
- * the rest of the k slots get -1, and out_count[r] the number selected.
- * 1 <= k <= 2,048; max_cols <= 2^24; cols_mul, cols_div in 1..8. */
+ * id ascending) are selected.  Column order must be id order: a row's ids
+ * strictly ascending over its c_r columns, its pool blocks ascending (not
+ * checked).  The selected ids are written ascending to
+ * out_ids[r * out_stride ..], the rest of the k slots get -1, and
+ * out_count[r] the number selected.
+ * 1 <= k <= 2,048; max_cols <= 2^24; cols_mul, cols_div in 1..8; ids and
+ * pool_blocks are exclusive; keys_by_id needs pool_blocks; ids_stride >=
+ * max_cols.
+ * workspace: device scratch of csa2_select_topk_workspace(n_rows, max_cols, k)
+ * bytes, 256-B aligned.  This version keeps its whole selection in LDS and
+ * registers, so the size is 0 for every shape and the workspace may be NULL;
+ * a non-zero size passed with a NULL pointer is an error. */
+size_t csa2_select_topk_workspace(int32_t n_rows, int32_t max_cols, int32_t k);
 csa2_status csa2_select_topk(const float* keys, int64_t key_stride,
+                             const int32_t* ids, int64_t ids_stride,
                              const int32_t* n_cols, int32_t cols_mul, int32_t cols_div,
                              const int32_t* pool_blocks, int64_t pool_stride, int32_t keys_by_id,
                              int32_t n_rows, int32_t max_cols, int32_t k,
                              int32_t* out_ids, int64_t out_stride, int32_t* out_count,
-                             void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* The Full layer's selection in one pass per row (V4.1-Flash architecture
  * page, hierarchical sparse indexer: the first Full layer keeps up to 2,048

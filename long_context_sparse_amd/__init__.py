@@ -47,7 +47,7 @@ _lib = None
 EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
     "csa2_index_score_shared",
-    "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
+    "csa2_select_topk_workspace", "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
     "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost", "csa2_stream_xor",
 )
 
@@ -70,7 +70,10 @@ def lib():
                                    P, i64, P, P, i64, P, i64, P]
     L.csa2_index_score_shared.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), i32, P, ctypes.c_int, i32, P,
                                           P, i64, P, i64, P]
-    L.csa2_select_topk.argtypes = [P, i64, P, i32, i32, P, i64, i32, i32, i32, i32, P, i64, P, P]
+    L.csa2_select_topk_workspace.restype = ctypes.c_size_t
+    L.csa2_select_topk_workspace.argtypes = [i32, i32, i32]
+    L.csa2_select_topk.argtypes = [P, i64, P, i64, P, i32, i32, P, i64, i32, i32, i32, i32, P, i64, P, P,
+                                   ctypes.c_size_t, P]
     L.csa2_select_full.argtypes = [P, i64, P, i64, P, i32, i32, i32, i32, P, i64, P, P, i64, P, P]
     L.csa2_attn_workspace_size.restype = ctypes.c_size_t
     L.csa2_attn_workspace_size.argtypes = [i32, i32]
@@ -84,7 +87,8 @@ def lib():
     L.csa2_synth_boost.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, i32, P, P]
     L.csa2_stream_xor.argtypes = [P, i64, P, P]
     for name in EXPORTS:
-        if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_attn_workspace_size"):
+        if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_attn_workspace_size",
+                        "csa2_select_topk_workspace"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -175,15 +179,22 @@ def csa2_index_score_shared(kv, rows, req, q_idx, w, scores=None, block_max=None
         _ptr(block_max), 0 if block_max is None else _rstride(block_max), _stream(stream)))
 
 
+def csa2_select_topk_workspace(n_rows, max_cols, k) -> int:
+    return int(lib().csa2_select_topk_workspace(int(n_rows), int(max_cols), int(k)))
+
+
 def csa2_select_topk(keys, k, out_ids, out_count, n_cols=None, cols_mul=1, cols_div=1, pool_blocks=None,
-                     keys_by_id=False, max_cols=None, stream=None):
+                     keys_by_id=False, max_cols=None, ids=None, workspace=None, stream=None):
+    """Row-wise top-k; `ids` (int32 [rows, >= max_cols], ascending per row)
+    gives each column its id, else the column index or its pool position."""
     n_rows = int(out_ids.shape[0])
     if max_cols is None:
         max_cols = int(keys.shape[1]) if not keys_by_id else 8 * int(pool_blocks.shape[1])
     _check("csa2_select_topk", lib().csa2_select_topk(
-        _ptr(keys), _rstride(keys), _ptr(n_cols), cols_mul, cols_div, _ptr(pool_blocks),
-        0 if pool_blocks is None else _rstride(pool_blocks), int(bool(keys_by_id)), n_rows,
-        int(max_cols), int(k), _ptr(out_ids), _rstride(out_ids), _ptr(out_count), _stream(stream)))
+        _ptr(keys), _rstride(keys), _ptr(ids), 0 if ids is None else _rstride(ids), _ptr(n_cols), cols_mul,
+        cols_div, _ptr(pool_blocks), 0 if pool_blocks is None else _rstride(pool_blocks), int(bool(keys_by_id)),
+        n_rows, int(max_cols), int(k), _ptr(out_ids), _rstride(out_ids), _ptr(out_count), *_ws(workspace),
+        _stream(stream)))
 
 
 def csa2_select_full(block_max, scores, n_vis, max_vis, pool, pool_count, idx, idx_count, n_pool_blocks=2048,

@@ -201,11 +201,21 @@ csa2_status csa2_index_score_shared(const csa2_kv* kv, const csa2_rows* rows, in
     return hip_status(csa2::launch_index_score_shared(v, a, req, (hipStream_t)stream), "csa2_index_score_shared launch");
 }
 
-csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_t* n_cols, int32_t cols_mul,
-                             int32_t cols_div, const int32_t* pool_blocks, int64_t pool_stride, int32_t keys_by_id,
-                             int32_t n_rows, int32_t max_cols, int32_t k, int32_t* out_ids, int64_t out_stride,
-                             int32_t* out_count, void* stream) {
+size_t csa2_select_topk_workspace(int32_t n_rows, int32_t max_cols, int32_t k) {
+    (void)n_rows;
+    (void)max_cols;
+    (void)k;
+    return 0;   // the selection lives in LDS and registers
+}
+
+csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_t* ids, int64_t ids_stride,
+                             const int32_t* n_cols, int32_t cols_mul, int32_t cols_div, const int32_t* pool_blocks,
+                             int64_t pool_stride, int32_t keys_by_id, int32_t n_rows, int32_t max_cols, int32_t k,
+                             int32_t* out_ids, int64_t out_stride, int32_t* out_count, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     if (n_rows < 0 || n_rows > 65535) return fail(CSA2_ERR_RANGE, "n_rows out of range");
+    if (workspace_bytes && !workspace) return fail(CSA2_ERR_NULL, "workspace_bytes > 0 with a NULL workspace");
+    if (workspace && !aligned(workspace, 256)) return fail(CSA2_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (k < 1 || k > CSA2_MAX_SELECT) return fail(CSA2_ERR_RANGE, "k must be in 1..%d (got %d)", CSA2_MAX_SELECT, k);
     if (max_cols < 0 || max_cols > (1 << 24)) return fail(CSA2_ERR_RANGE, "max_cols out of range");
     if (cols_mul < 1 || cols_mul > 8 || cols_div < 1 || cols_div > 8) return fail(CSA2_ERR_RANGE, "cols_mul / cols_div must be in 1..8");
@@ -216,11 +226,15 @@ csa2_status csa2_select_topk(const float* keys, int64_t key_stride, const int32_
     if (keys_by_id && (!aligned(keys, 16) || key_stride % 4))
         return fail(CSA2_ERR_ALIGN, "keys_by_id needs 16-byte aligned keys and key_stride % 4 == 0");
     if (pool_blocks && pool_stride < 1) return fail(CSA2_ERR_SHAPE, "pool_stride must be >= 1");
+    if (ids && pool_blocks) return fail(CSA2_ERR_SHAPE, "ids and pool_blocks are exclusive");
+    if (ids && ids_stride < max_cols) return fail(CSA2_ERR_SHAPE, "ids_stride < max_cols");
     if (!keys_by_id && key_stride < max_cols) return fail(CSA2_ERR_SHAPE, "key_stride < max_cols");
     if (pool_blocks && (int64_t)max_cols > 8 * pool_stride) return fail(CSA2_ERR_SHAPE, "max_cols exceeds 8 * pool_stride");
     csa2::TopkArgs a;
     a.keys = keys;
     a.key_stride = key_stride;
+    a.ids = ids;
+    a.ids_stride = ids_stride;
     a.n_cols = n_cols;
     a.cols_mul = cols_mul;
     a.cols_div = cols_div;

@@ -39,13 +39,17 @@
 //     bytes are in flight while the current one is processed: one barrier
 //     per chunk.
 //   * Both matmuls run in fp16 with exact operands: the query is scaled by a
-//     power of two per head so its largest component sits in [2^14, 2^15);
-//     every entry of a row is scaled by one power of two 2^tw chosen from the
-//     row's window scales, so FP4 x E4M3 values (at most 6 significant bits,
-//     in [2^-10, 2688]) and E4M3 x 2^e window values are exact in fp16.  The
-//     scaled conversion instructions (V_CVT_SCALEF32_PK_F16_FP4 / _FP8) apply
-//     the power of two as they convert.  The scalings are undone on the fp32
-//     scores and outputs.
+//     power of two per head so its largest component sits in [2^14, 2^15).
+//     Selected entries carry the fixed factor 2^4: FP4 x E4M3 values have at
+//     most 6 significant bits and lie in [2^-10, 2688], so times 2^4 they are
+//     normal fp16 numbers, exact, below 65504.  Window entries carry their
+//     row's own factor 2^tw, chosen so that the row's largest window group
+//     reaches the top of the fp16 range: E4M3 x 2^e values are exact for
+//     every group within 22 octaves of it.  The scaled conversion
+//     instructions (V_CVT_SCALEF32_PK_F16_FP4 / _FP8) apply the power of two
+//     as they convert.  The scalings are undone on the fp32 scores and
+//     outputs; a running output that crosses from selected to window chunks
+//     is rescaled by 2^(tw - 4) at the crossing (exact in fp32).
 #include <atomic>
 #include <type_traits>
 
@@ -64,6 +68,10 @@ constexpr int AT_MAX_SEL = 512;
 constexpr int AT_UNIT = 3;              // chunks per unit of the fixed fold
 constexpr int AT_MAX_UNITS = (AT_MAX_SEL / AT_ENT + 128 / AT_ENT + AT_UNIT - 1) / AT_UNIT;   // 4
 constexpr int AT_MAX_SPLITS = AT_MAX_UNITS;   // workgroups sharing one (row, head group)
+constexpr int AT_TW_SEL = 4;            // power of two on every dequantised selected entry
+// bounds of the window's power of two: the crossing factor 2^(tw - AT_TW_SEL)
+// and its inverse stay normal fp32 numbers
+constexpr int AT_TW_WIN_MIN = -120, AT_TW_WIN_MAX = 100;
 
 struct AttnSmem {
     _Float16 v[2][AT_ENT * V_LD];       // the chunk's dequantised entries [entry][channel], double-buffered
@@ -112,15 +120,15 @@ __device__ __forceinline__ void load_raw(const KvView& kv, const AttnArgs& a, co
 }
 
 // Selected entry: dequantise the lane's 64 channels into the QK A operand
-// and into V^T, both fp16 and both carrying the row's exact factor 2^tw
-// (-14 <= tw <= 4).  V_CVT_SCALEF32_PK_F16_FP4 expands two E2M1 codes (low
-// nibble first) times the power of two of its f32 scale operand, here
-// 2^(tw+8); the E4M3 scale byte shifted into fp16 position reads as
-// scale * 2^-8 (normal and subnormal alike) and one packed fp16 multiply
-// applies it.  FP4 x E4M3 values have at most 6 significant bits and lie in
-// [2^-10, 2688], so times 2^tw they are exact in fp16.  K-step ks holds
-// channels 8ks .. 8ks+7 of the lane and is also stored to the entry's row in
-// LDS at vrow + 8ks.
+// and into V^T, both fp16 and both carrying the exact factor 2^AT_TW_SEL.
+// V_CVT_SCALEF32_PK_F16_FP4 expands two E2M1 codes (low nibble first) times
+// the power of two of its f32 scale operand, here 2^(AT_TW_SEL + 8); the
+// E4M3 scale byte shifted into fp16 position reads as scale * 2^-8 (normal
+// and subnormal alike) and one packed fp16 multiply applies it.  FP4 x E4M3
+// values have at most 6 significant bits and lie in [2^-10, 2688], so times
+// 2^4 they are normal fp16 numbers (at most 43008): exact for every input.
+// K-step ks holds channels 8ks .. 8ks+7 of the lane and is also stored to the
+// entry's row in LDS at vrow + 8ks.
 __device__ __forceinline__ void dequant_main(const RawChunk& r, float cvt_scale, _Float16* vrow, f16x8* kop) {
     const uint32_t words[8] = {r.c[0].x, r.c[0].y, r.c[0].z, r.c[0].w, r.c[1].x, r.c[1].y, r.c[1].z, r.c[1].w};
 #pragma unroll
@@ -138,16 +146,19 @@ __device__ __forceinline__ void dequant_main(const RawChunk& r, float cvt_scale,
 }
 
 // Window entry: E4M3 codes times the E8M0 scale 2^e of their 16 channels,
-// times the row's 2^tw, in fp16 (V_CVT_SCALEF32_PK_F16_FP8 converts two E4M3
-// bytes and multiplies by the power of two of its f32 scale operand).
-// E4M3 * 2^(e + tw) is exact in fp16 while -15 <= e + tw <= 7.
+// times the row's window factor 2^tw, in fp16 (V_CVT_SCALEF32_PK_F16_FP8
+// converts two E4M3 bytes and multiplies by the power of two of its f32
+// scale operand).  E4M3 * 2^(e + tw) is exact in fp16 while
+// -15 <= e + tw <= 7; the row's largest group sits at e + tw = 7 (unless the
+// window is tinier than 2^-85), groups more than 133 octaves below it
+// convert to zero.
 __device__ __forceinline__ void dequant_swa(const RawChunk& r, int tw, _Float16* vrow, f16x8* kop) {
     const uint32_t words[16] = {r.c[0].x, r.c[0].y, r.c[0].z, r.c[0].w, r.c[1].x, r.c[1].y, r.c[1].z, r.c[1].w,
                                 r.c[2].x, r.c[2].y, r.c[2].z, r.c[2].w, r.c[3].x, r.c[3].y, r.c[3].z, r.c[3].w};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
         int ef = (int)((r.s >> (8 * (ks >> 1))) & 0xFFu) + tw;    // biased exponent of 2^(e + tw)
-        ef = ef < 0 ? 0 : (ef > 254 ? 254 : ef);                   // only all-zero groups reach the clamps
+        ef = ef < 0 ? 0 : (ef > 254 ? 254 : ef);                   // e + tw <= 7: the upper clamp is never reached
         const float sc = __uint_as_float((uint32_t)ef << 23);
         f16x2 b[4];
         b[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(words[2 * ks], sc, false);
@@ -356,17 +367,20 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     wmin = 255;
 #pragma unroll
     for (int w = 0; w < AT_WAVES; ++w) { wmax = max(wmax, sm.wrange[0][w]); wmin = min(wmin, sm.wrange[1][w]); }
-    // The row's power of two 2^tw on every dequantised entry: selected entries
-    // are exact in fp16 for -14 <= tw <= 4, window ones while the exponents
-    // e + tw of their groups stay in [-15, 7]; tw brings the largest window
-    // group as close to 7 as the selected range allows (window groups more than
-    // 22 octaves below the largest one would be rounded).
+    // The window's power of two 2^tw: its largest group (biased scale code
+    // wmax, e = wmax - 127) lands at e + tw = 7, the top of the exact fp16
+    // range; groups within 22 octaves of it are exact, smaller ones rounded
+    // (an absolute change of at most 2^-40 of the window's largest value).
+    // Selected entries always carry 2^AT_TW_SEL.
     int tw = wmax ? 134 - wmax : 0;
-    tw = tw < -14 ? -14 : (tw > 4 ? 4 : tw);
-    // logits in base 2: z2 = S' * cz with S' = S * 2^(kq + tw)
+    tw = tw < AT_TW_WIN_MIN ? AT_TW_WIN_MIN : (tw > AT_TW_WIN_MAX ? AT_TW_WIN_MAX : tw);
+    // logits in base 2: z2 = S' * cz with S' = S * 2^(kq + factor), per entry kind
     constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
-    const float cz = ldexpf(a.scale * LOG2E, -kq - tw);
-    const float cvt_sel = __uint_as_float((uint32_t)(127 + tw + 8) << 23);     // 2^(tw + 8)
+    const float cz_sel = ldexpf(a.scale * LOG2E, -kq - AT_TW_SEL);
+    const float cz_win = ldexpf(a.scale * LOG2E, -kq - tw);
+    constexpr float cvt_sel = (float)(1 << (AT_TW_SEL + 8));                    // 2^(AT_TW_SEL + 8)
+    // a running output crossing from selected to window chunks: 2^(tw - AT_TW_SEL)
+    const float cross = __uint_as_float((uint32_t)(127 + tw - AT_TW_SEL) << 23);
 
     // Software pipeline, one barrier per chunk: while a wave turns the scores of
     // chunk c into probabilities and accumulates P.V (LDS buffers c & 1), it
@@ -422,28 +436,43 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         m = fmaxf(m, fmaxf(fmaxf(fmaxf(z[2][0], z[2][1]), fmaxf(z[2][2], z[2][3])),
                            fmaxf(fmaxf(z[3][0], z[3][1]), fmaxf(z[3][2], z[3][3]))));
         m = max_xor32(max_xor16(m));
+        const bool win = c >= csp;
+        const float cz = win ? cz_win : cz_sel;
         const float m_new = fmaxf(m_run, m * cz);         // cz > 0: the scaled maximum
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         float lsum = 0.0f;
-        f16x8 pb[2];                                     // P^T slot 8g + j of step u: entry 32u + 4g + j (j < 4), 32u + 12 + 4g + j
+        // P^T slot 8g + j of step u: entry 32u + 4g + j (j < 4), 32u + 12 + 4g + j.
+        // Each probability enters P.V as an fp16 pair, p = hi + lo + O(2^-24 p)
+        // (hi = fp16(p); p - hi is exact in fp32): one fp16 P would carry a
+        // relative error of 2^-12 into every term of the output, which for
+        // entries near the FP4 maximum (2,688) is far above the tolerance.
+        f16x8 pb[2], pl[2];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(z[t][i], cz, -m_new));
                 lsum += p;
-                pb[t >> 1][4 * (t & 1) + i] = (_Float16)p;
+                const _Float16 hi = (_Float16)p;
+                pb[t >> 1][4 * (t & 1) + i] = hi;
+                pl[t >> 1][4 * (t & 1) + i] = (_Float16)(p - (float)hi);
             }
         lsum = add_xor32(add_xor16(lsum));
         l_run = l_run * alpha + lsum;
         m_run = m_new;
         const _Float16* vb = sm.v[buf];
+        // the first window chunk re-expresses the running output in the
+        // window's factor (exact; 1 elsewhere)
+        const float rs = (win && c == csp) ? cross : 1.0f;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            f32x4 o = oacc[ct] * alpha;
+            f32x4 o = (oacc[ct] * rs) * alpha;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                o = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand(vb, 64 * wave + 16 * ct, u, n, g), pb[u], o, 0, 0, 0);
+            for (int u = 0; u < 2; ++u) {
+                const f16x8 vo = v_operand(vb, 64 * wave + 16 * ct, u, n, g);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, pb[u], o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, pl[u], o, 0, 0, 0);
+            }
             oacc[ct] = o;
         }
     };
@@ -460,16 +489,19 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         __syncthreads();
     };
 
-    // The end of unit u: with several splits its partial (output without the
-    // 2^tw, unnormalised, and its max and sum) goes to the workspace, else it
-    // is folded into (Mf, Lf, Of); the next unit starts afresh.
+    // The end of unit u, whose last chunk is c_last: with several splits its
+    // partial (output without the factor of its last chunk's kind,
+    // unnormalised, and its max and sum) goes to the workspace, else it is
+    // folded into (Mf, Lf, Of); the next unit starts afresh.
     const int h = h0 + n;
-    const float pw = __uint_as_float((uint32_t)(127 - tw) << 23);   // 2^-tw (exact)
+    const float pw_sel = 1.0f / (float)(1 << AT_TW_SEL);                  // 2^-AT_TW_SEL (exact)
+    const float pw_win = __uint_as_float((uint32_t)(127 - tw) << 23);    // 2^-tw (exact)
     float Mf = -INFINITY, Lf = 0.0f;
     f32x4 Of[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) Of[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    auto end_unit = [&](const int u) __attribute__((always_inline)) {
+    auto end_unit = [&](const int u, const int c_last) __attribute__((always_inline)) {
+        const float pw = c_last >= csp ? pw_win : pw_sel;
         if constexpr (SPLIT) {
             const size_t ps = ((size_t)row * a.n_heads + h) * AT_MAX_UNITS + u;
             float* wsO = a.ws;
@@ -499,7 +531,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         else stage_a(WIN, cb, raw0);
         __syncthreads();
         for (int c = cb;; c += 3) {
-            if (c > cb) end_unit(c / AT_UNIT - 1);    // c starts a unit
+            if (c > cb) end_unit(c / AT_UNIT - 1, c - 1);   // c starts a unit
             if (c + 1 >= ce) { stage_b(c); break; }
             step(c, raw1);
             if (c + 2 >= ce) { stage_b(c + 1); break; }
@@ -507,7 +539,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
             if (c + 3 >= ce) { stage_b(c + 2); break; }
             step(c + 2, raw0);
         }
-        end_unit((ce - 1) / AT_UNIT);
+        end_unit((ce - 1) / AT_UNIT, ce - 1);
     }
     if constexpr (SPLIT) return;
     // ---- epilogue: the folded units, an external partial (o_in, lse_in) and

@@ -36,6 +36,8 @@ hipError_t launch_index_score_shared(const KvView& kv, const IndexScoreArgs& a, 
 struct TopkArgs {
     const float* keys;
     int64_t key_stride;
+    const int32_t* ids;           // id per column (NULL: column index or pool position)
+    int64_t ids_stride;
     const int32_t* n_cols;
     int cols_mul, cols_div;
     const int32_t* pool;

@@ -388,7 +388,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     const uint32_t n = ncols <= TK_SWEEP ? select_row<1>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val)
                                          : select_row<0>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val);
     __syncthreads();
-    for (int j = threadIdx.x; j < a.k; j += TK_THREADS) orow[j] = j < (int)n ? col_id(pool, (int)sh.hist[j]) : -1;
+    const int32_t* irow = a.ids ? a.ids + (int64_t)row * a.ids_stride : nullptr;
+    for (int j = threadIdx.x; j < a.k; j += TK_THREADS)
+        orow[j] = j < (int)n ? (irow ? irow[sh.hist[j]] : col_id(pool, (int)sh.hist[j])) : -1;
     if (threadIdx.x == 0) a.out_count[row] = (int32_t)n;
 }
 

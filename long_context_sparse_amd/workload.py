@@ -10,10 +10,16 @@ together as one step of the hot path:
                 -> csa2_sparse_swa_attn (or csa2_sparse_attn -> csa2_swa_merge)
   Reindex layer csa2_index_score (pool) -> csa2_select_topk (512)
                 -> csa2_sparse_swa_attn (or csa2_sparse_attn -> csa2_swa_merge)
+  Reuse layer   csa2_sparse_swa_attn with the layer's own query and window over
+                the positions the last Full or Reindex layer selected
+
+A whole step (every layer) can also be captured once per KV copy as a HIP
+graph and replayed (``capture_graphs`` / ``replay``).
 
 ('DeepSeek V4.1 Flash architecture analysis' page, hierarchical sparse
 indexer: the first Full layer scores every position and builds the pool that
-later Reindex layers re-score; 'KV cache diet' page, figure 2: layer roles.)
+later Reindex layers re-score, and a Reuse layer still attends with its own
+query over the shared positions; 'KV cache diet' page, figure 2: layer roles.)
 """
 from __future__ import annotations
 
@@ -57,26 +63,36 @@ def _fill_packed(kind, seed, tensor, width, logical_first, n, codes, scales, slo
 
 
 class Layer:
-    """Per-layer query-side inputs and outputs of one step."""
+    """Per-layer query-side inputs and outputs of one step.  A Reuse layer
+    (``source`` given) has no indexer inputs and reads the selection of its
+    source layer."""
 
-    def __init__(self, cfg: Config, n_rows: int, layer: int, swa_first_tok, dev):
+    def __init__(self, cfg: Config, n_rows: int, layer: int, swa_first_tok, dev, role: str = "full",
+                 source: "Layer | None" = None):
+        self.role = role
+        self.index = layer
         H, Hi = cfg.heads, cfg.idx_heads
         off = 16 * layer
         s = cfg.seed
         self.q = torch.empty((n_rows, H, 512), dtype=torch.bfloat16, device=dev)
         csa2_synth_normal(s, synth.T_Q + off, 0, self.q)
-        self.q_idx = torch.empty((n_rows, Hi, 128), dtype=torch.bfloat16, device=dev)
-        csa2_synth_normal(s, synth.T_QIDX + off, 0, self.q_idx)
-        self.w = torch.empty((n_rows, Hi), dtype=torch.float32, device=dev)
-        csa2_synth_uniform(s, synth.T_W + off, 0, self.w)
+        if role != "reuse":
+            self.q_idx = torch.empty((n_rows, Hi, 128), dtype=torch.bfloat16, device=dev)
+            csa2_synth_normal(s, synth.T_QIDX + off, 0, self.q_idx)
+            self.w = torch.empty((n_rows, Hi), dtype=torch.float32, device=dev)
+            csa2_synth_uniform(s, synth.T_W + off, 0, self.w)
         # sliding window: the row's own 128 8-bit entries
         n_swa = int(swa_first_tok[-1] + cfg.window) if n_rows else 0
         self.swa_codes, self.swa_scales = _planes(max(n_swa, 1), SWA_FP8, dev)
         _fill_packed(SWA_FP8, s, synth.T_SWA + off, 512, 0, n_swa, self.swa_codes, self.swa_scales, dev=dev)
         self.swa_first = torch.as_tensor(np.asarray(swa_first_tok, np.int64), device=dev)
         self.swa_count = torch.full((n_rows,), cfg.window, dtype=torch.int32, device=dev)
-        self.idx = torch.empty((n_rows, 512), dtype=torch.int32, device=dev)
-        self.idx_count = torch.empty((n_rows,), dtype=torch.int32, device=dev)
+        if source is not None:
+            # the positions (and counts) of the last Full or Reindex layer
+            self.idx, self.idx_count = source.idx, source.idx_count
+        else:
+            self.idx = torch.empty((n_rows, 512), dtype=torch.int32, device=dev)
+            self.idx_count = torch.empty((n_rows,), dtype=torch.int32, device=dev)
         self.o_partial = torch.empty((n_rows, H, 512), dtype=torch.float32, device=dev)
         self.lse = torch.empty((n_rows, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((n_rows, H, 512), dtype=torch.float32, device=dev)
@@ -144,8 +160,19 @@ class Workload:
         if cfg.page_entries == 0 and len(set(L.tolist())) != 1:
             raise ValueError("contiguous layout needs equal contexts")
         # ---- layers
-        n_layers = 1 + cfg.reindex_layers
-        self.layers = [Layer(cfg, self.n_rows, li, swa_first, dev) for li in range(n_layers)]
+        self.layers = []
+        source = None
+        for li, role in enumerate(cfg.roles):
+            if role == "reuse" and source is None:
+                raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
+            layer = Layer(cfg, self.n_rows, li, swa_first, dev, role=role,
+                          source=source if role == "reuse" else None)
+            if role != "reuse":
+                source = layer
+            self.layers.append(layer)
+        if cfg.roles[0] not in ("full", "reindex", "prefill"):
+            raise ValueError("the first layer of a step must select its own positions")
+        self.graphs = None
         # ---- intermediates
         self.nv8 = (self.max_vis + 7) // 8 * 8
         mode = cfg.mode
@@ -265,15 +292,39 @@ class Workload:
             m(marks, "attention", 1)
 
     def step(self, copy: int = 0, stream=None, marks=None):
-        """One pass of the hot path.  `marks` maps step names to (start, end)
-        events recorded around that call (first layer only)."""
+        """One pass of the hot path over every layer.  `marks` maps step names
+        to (start, end) events recorded around that call (first layer only)."""
         kv = self.kvs[copy % len(self.kvs)]
-        if self.cfg.mode == "reindex":
-            self.run_reindex(self.layers[0], kv, stream, marks)
-            return
-        self.run_full(self.layers[0], kv, stream, marks)
-        for layer in self.layers[1:]:
-            self.run_reindex(layer, kv, stream)
+        for i, layer in enumerate(self.layers):
+            mk = marks if i == 0 else None
+            if layer.role in ("full", "prefill"):
+                self.run_full(layer, kv, stream, mk)
+            elif layer.role == "reindex":
+                self.run_reindex(layer, kv, stream, mk)
+            else:
+                self._attend(layer, kv, stream, mk)
+
+    # --------------------------------------------------------------- graphs
+    def capture_graphs(self):
+        """Capture one whole step per KV copy as a HIP graph (torch's graph
+        capture of the current stream; every call of the step is a kernel
+        launch of libcsa2 on that stream, nothing else: no memset, no
+        allocation).  Each copy's step runs eagerly once before capture."""
+        for c in range(len(self.kvs)):
+            self.step(copy=c)
+        torch.cuda.synchronize()
+        graphs = []
+        for c in range(len(self.kvs)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(copy=c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        self.graphs = graphs
+
+    def replay(self, copy: int = 0):
+        """Replay the captured step of KV copy `copy` on the current stream."""
+        self.graphs[copy % len(self.graphs)].replay()
 
     # --------------------------------------------------------------- bytes
     def algorithmic_bytes(self) -> dict:
@@ -281,24 +332,28 @@ class Workload:
         main entries gathered, window entries, queries in, outputs out.  Data
         that several rows share is counted once: the rows of a chunked
         prefill read one request's keys (its largest visible prefix) and
-        overlapping windows (rows + window - 1 entries)."""
+        overlapping windows (rows + window - 1 entries).  A Reuse layer moves
+        its gathered entries, window, query and output, no indexer bytes."""
         cfg = self.cfg
         H = cfg.heads
-        n_layers = len(self.layers)
         rows = self.n_rows
         prefill = cfg.mode == "prefill"
+        roles = [layer.role for layer in self.layers]
+        n_layers = len(roles)
+        n_index = sum(r != "reuse" for r in roles)
         d = {}
-        if self.full:
+        n_full = sum(r in ("full", "prefill") for r in roles)
+        if n_full:
             keys = int(self.n_vis_host.max()) if prefill else int(self.n_vis_host.sum())
-            d["index_keys_full"] = keys * 68
-        reindex_layers = n_layers - 1 if cfg.mode != "reindex" else 1
-        if reindex_layers:
+            d["index_keys_full"] = n_full * keys * 68
+        n_reindex = sum(r == "reindex" for r in roles)
+        if n_reindex:
             pool_pos = int(np.minimum(self.n_vis_host, 16384).sum()) if cfg.mode != "reindex" else rows * 16384
-            d["index_keys_pool"] = reindex_layers * pool_pos * 68
+            d["index_keys_pool"] = n_reindex * pool_pos * 68
         sel = int(np.minimum(self.n_vis_host, 512).sum())
         d["gathered_main"] = n_layers * sel * 288
         d["swa"] = n_layers * (rows + cfg.window - 1 if prefill else rows * cfg.window) * 544
-        d["q"] = n_layers * rows * (H * 512 * 2 + cfg.idx_heads * 128 * 2 + cfg.idx_heads * 4)
+        d["q"] = n_layers * rows * H * 512 * 2 + n_index * rows * (cfg.idx_heads * 128 * 2 + cfg.idx_heads * 4)
         d["out"] = n_layers * rows * H * 512 * 4
         d["total"] = sum(d.values())
         return d

@@ -33,6 +33,21 @@ class Config:
     window: int = 128
     description: str = ""
     extra: dict = field(default_factory=dict)
+    layer_roles: tuple | None = None   # per layer: "full" | "reindex" | "reuse" (None: from mode)
+
+    @property
+    def roles(self) -> tuple:
+        """The role of each layer of a step: a Full layer scores every
+        position and builds the pool, a Reindex layer re-scores the pool with
+        its own indexer query, a Reuse layer attends with its own query over
+        the positions the last Full or Reindex layer chose."""
+        if self.layer_roles is not None:
+            return tuple(self.layer_roles)
+        if self.mode == "reindex":
+            return ("reindex",)
+        if self.mode == "prefill":
+            return ("prefill",)
+        return ("full",) + ("reindex",) * self.reindex_layers
 
     @property
     def lens(self) -> np.ndarray:
@@ -81,10 +96,22 @@ def mixed_serving(**kw) -> Config:
                   "in a random page order, 1 Full + 4 Reindex layers, 64 heads", **kw)
 
 
+def decoder_stack_128k(**kw) -> Config:
+    # the decoder's 20 CSA2 layers: one Full or Reindex layer, then three
+    # Reuse layers, four times over ('KV cache diet' page, figure 2 and the
+    # layer roles; V4.1 Flash architecture page, "Global KV is built in four
+    # places")
+    roles = tuple("full" if i == 0 else "reindex" if i % 4 == 0 else "reuse" for i in range(20))
+    return Config("decoder_stack_16x128k", seed=5, n_req=16, heads=64, ctx=131072, mode="full",
+                  layer_roles=roles, description="16 requests x 131,072 entries, 64 heads, the decoder's 20 "
+                  "layers: 1 Full, 4 Reindex, 15 Reuse", **kw)
+
+
 ALL = {
     "c0": tiny_full_decode,
     "c1": full_decode_128k,
     "c2": reindex_decode_1m,
     "c3": chunked_prefill_256k,
     "c4": mixed_serving,
+    "stack": decoder_stack_128k,
 }

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lib.EXPORTS)
-    assert L.csa2_abi_version() == 4
+    assert L.csa2_abi_version() == 5
 
 
 def _kv(**over):
@@ -45,22 +45,41 @@ def test_status_strings():
         assert L.csa2_status_str(s)
 
 
+def _topk(L, keys=256, key_stride=100, ids=None, ids_stride=0, n_cols=None, mul=1, div=1, pool=None,
+          pool_stride=0, by_id=0, n_rows=4, max_cols=100, k=10, out=256, out_stride=16, cnt=256, ws=None,
+          ws_bytes=0):
+    return L.csa2_select_topk(keys, key_stride, ids, ids_stride, n_cols, mul, div, pool, pool_stride, by_id,
+                              n_rows, max_cols, k, out, out_stride, cnt, ws, ws_bytes, None)
+
+
 @pytest.mark.parametrize("k,expect", [(0, 3), (2049, 3)])
 def test_topk_rejects_k(k, expect):
     L = lib.lib()
-    assert L.csa2_select_topk(256, 100, None, 1, 1, None, 0, 0, 4, 100, k, 256, 2048, 256, None) == expect
+    assert _topk(L, k=k, out_stride=2048) == expect
     assert b"k must be" in L.csa2_last_error()
 
 
 def test_topk_rejects_shapes():
+    """Every call here is invalid (nothing is launched), except the one with
+    no rows."""
     L = lib.lib()
-    assert L.csa2_select_topk(None, 100, None, 1, 1, None, 0, 0, 4, 100, 10, 256, 16, 256, None) == 1
-    assert L.csa2_select_topk(256, 100, None, 1, 1, None, 0, 0, 4, 100, 10, 256, 5, 256, None) == 2
-    assert L.csa2_select_topk(256, 100, None, 1, 1, None, 0, 1, 4, 100, 10, 256, 16, 256, None) == 2
-    assert L.csa2_select_topk(256, 50, None, 1, 1, None, 0, 0, 4, 100, 10, 256, 16, 256, None) == 2
-    assert L.csa2_select_topk(256, 100, None, 9, 1, None, 0, 0, 4, 100, 10, 256, 16, 256, None) == 3
+    assert _topk(L, keys=None) == 1
+    assert _topk(L, out_stride=5) == 2                              # out_stride < k
+    assert _topk(L, by_id=1) == 2                                   # keys_by_id without a pool
+    assert _topk(L, key_stride=50) == 2                             # key_stride < max_cols
+    assert _topk(L, mul=9) == 3
+    assert _topk(L, ids=512, ids_stride=100, pool=768, pool_stride=16) == 2   # ids and pool exclusive
+    assert _topk(L, ids=512, ids_stride=99) == 2                    # ids_stride < max_cols
+    assert _topk(L, ws=None, ws_bytes=64) == 1                      # size without a workspace
+    assert _topk(L, ws=264, ws_bytes=64) == 4                       # workspace alignment
     # zero rows: nothing to do
-    assert L.csa2_select_topk(None, 0, None, 1, 1, None, 0, 0, 0, 0, 10, None, 0, None, None) == 0
+    assert _topk(L, keys=None, key_stride=0, n_rows=0, max_cols=0, out=None, out_stride=0, cnt=None) == 0
+
+
+def test_topk_workspace_size():
+    L = lib.lib()
+    for n_rows, max_cols, k in ((1, 1, 1), (64, 16384, 512), (4096, 131072, 2048)):
+        assert L.csa2_select_topk_workspace(n_rows, max_cols, k) == 0
 
 
 def test_select_full_rejects():

@@ -29,8 +29,10 @@ def bf16(x):
     return torch.as_tensor(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
 
 
-def tolerance_ok(got, ref):
-    return np.all(np.abs(got - ref) <= 2e-3 + 1e-2 * np.abs(ref))
+def tolerance_ok(got, ref, scale=1.0):
+    """|got - ref| <= 2e-3 + 1e-2 |ref| elementwise; for inputs drawn at a
+    scale s the absolute term is 2e-3 s (the same problem multiplied by s)."""
+    return np.all(np.abs(got - ref) <= 2e-3 * scale + 1e-2 * np.abs(ref))
 
 
 def planes(n, kind):
@@ -359,6 +361,33 @@ def test_topk_exact(n, k):
         assert np.all(O[r, C[r]:] == -1)
 
 
+@pytest.mark.parametrize("n,k", [(1, 1), (700, 512), (16384, 512), (40000, 2048)])
+def test_topk_ids_exact(n, k):
+    """A caller-supplied id per key (ascending within a row): the ids of the
+    top-k by (key descending, id ascending), ascending; ties are frequent so
+    the id decides ('DeepSeek-V4' page, section 2.3.1, top-k selector)."""
+    n_rows = 3
+    keys = (RNG.integers(0, 40, (n_rows, n)) * 0.25).astype(np.float32)
+    keys[1, ::3] = -np.inf
+    ids = np.stack([np.sort(RNG.choice(1 << 30, n, replace=False)) for _ in range(n_rows)]).astype(np.int32)
+    ids_pad = np.full((n_rows, n + 5), -9, np.int32)        # ids_stride > max_cols
+    ids_pad[:, :n] = ids
+    n_cols = np.array([n, max(n - 1, 0), n // 3], np.int32)
+    out = torch.full((n_rows, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
+    assert lib.csa2_select_topk_workspace(n_rows, n, k) == 0
+    lib.csa2_select_topk(T(keys), k, out, cnt, n_cols=T(n_cols), max_cols=n, ids=T(ids_pad))
+    torch.cuda.synchronize()
+    O, C = out.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(n_rows):
+        kk, ii = keys[r, :n_cols[r]], ids[r, :n_cols[r]]
+        present = ~np.isneginf(kk)
+        ref = oracle.topk(kk[present], k, ids=ii[present]) if present.any() else np.zeros(0, np.int32)
+        assert C[r] == len(ref)
+        assert np.array_equal(O[r, :C[r]], ref)
+        assert np.all(O[r, C[r]:] == -1)
+
+
 def test_topk_block_counts_and_pool_ids():
     n_rows, nb = 2, 3000
     bm = RNG.standard_normal((n_rows, nb)).astype(np.float32)
@@ -502,14 +531,26 @@ def test_full_path_empty_and_short_rows():
 
 
 # ---------------------------------------------------------------- K4 / K5 attention
-def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=torch.bfloat16, check_rows=None):
-    lat = bf16(RNG.standard_normal((n_rows * n_entries, 512)).astype(np.float32)).float().numpy()
+def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=torch.bfloat16, check_rows=None,
+               lat=None, swa=None, q=None, win_scale=1.0):
+    """Every call form against the oracle.  lat [n_rows * n_entries, 512],
+    swa [n_rows * 128, 512] and q [n_rows, H, 512] may be given (fp32 values,
+    rounded to bf16 here); by default they are N(0,1) (q times 2).  Outputs
+    that include the window are compared at the window's scale `win_scale`."""
+    if lat is None:
+        lat = RNG.standard_normal((n_rows * n_entries, 512)).astype(np.float32)
+    lat = bf16(lat).float().numpy()
     mc, ms = oracle.pack_main(lat)
     K = oracle.dequant_main(mc, ms)
-    swa = bf16(RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
+    if swa is None:
+        swa = RNG.standard_normal((n_rows * 128, 512)).astype(np.float32)
+    swa = bf16(swa).float().numpy()
     wc, wsc = oracle.pack_swa(swa)
     W = oracle.dequant_swa(wc, wsc)
-    q = bf16(RNG.standard_normal((n_rows, H, 512)).astype(np.float32) * 2).float().numpy()
+    if q is None:
+        q = RNG.standard_normal((n_rows, H, 512)).astype(np.float32) * 2
+    q = bf16(q).float().numpy()
+    assert np.all(np.isfinite(K)) and np.all(np.isfinite(W))
     idx = np.full((n_rows, 512), -1, np.int32)
     for r in range(n_rows):
         idx[r, :counts[r]] = np.sort(RNG.permutation(n_entries)[:counts[r]])
@@ -551,13 +592,82 @@ def _attn_case(n_rows, H, counts, swa_counts, n_entries=700, sink=False, qdt=tor
         else:
             assert np.all(np.isneginf(L_p[r])) and not O_p[r].any()
         fo, fl = oracle.attention(q[r], Kr, Wr, sink=sk, sigma=SIG)
-        assert tolerance_ok(Out[r], fo), (r, np.abs(Out[r] - fo).max())
+        assert tolerance_ok(Out[r], fo, win_scale), (r, np.abs(Out[r] - fo).max())
         for Oo, Ll in ((Out2, L2), (Out3, L3)):
-            assert tolerance_ok(Oo[r], fo), (r, np.abs(Oo[r] - fo).max())
+            assert tolerance_ok(Oo[r], fo, win_scale), (r, np.abs(Oo[r] - fo).max())
             if counts[r] or swa_counts[r] or sink:
                 assert np.allclose(Ll[r], fl, rtol=1e-5, atol=1e-5)
             else:
                 assert np.all(np.isneginf(Ll[r])) and not Oo[r].any()
+
+
+def _group_scale(rng, n, lo, hi, frac=1.0):
+    """Per (entry, 16-channel group) power-of-two multipliers 2^k, k uniform
+    in [lo, hi] on a fraction `frac` of the groups (1 elsewhere)."""
+    k = rng.integers(lo, hi + 1, (n, 32)).astype(np.float32)
+    k[rng.random((n, 32)) >= frac] = 0
+    return np.repeat(np.exp2(k), 16, axis=1).astype(np.float32)
+
+
+def _edge_data(case, n_rows, H, n_entries):
+    """Latent, window and query data at the edges of the exact fp16 domain of
+    the attention ('KV cache diet' page, FP4 maximum 2,688 = 448 x 6; the
+    window's 8-bit codes with a power-of-two scale per 16 channels).  The
+    query is scaled so every logit stays moderate (the fp32 score sums then
+    carry no rounding that the softmax would magnify).  Returns (latent,
+    window, query, the window's scale); the draws depend on (case, H) only."""
+    import zlib
+    rng = np.random.default_rng(zlib.crc32(f"{case}/{H}".encode()))
+    lat = rng.standard_normal((n_rows * n_entries, 512)).astype(np.float32)
+    swa = rng.standard_normal((n_rows * 128, 512)).astype(np.float32)
+    q = rng.standard_normal((n_rows, H, 512)).astype(np.float32)
+    if case == "main_fp4_max":
+        # a third of the latent groups have amax exactly 2,688: E4M3 scale
+        # 448 and codes up to 6, the largest value the MAIN format holds
+        g = rng.random((n_rows * n_entries, 32)) < 0.33
+        blk = lat.reshape(-1, 32, 16)
+        amax = np.abs(blk).max(axis=2, keepdims=True)
+        blk = np.where(g[:, :, None], blk / amax * np.float32(2688), blk)
+        lat = blk.reshape(-1, 512).astype(np.float32)
+        q *= np.float32(2.0 ** -9)
+    elif case == "main_subnormal_scales":
+        # groups with amax below 6 * 2^-6 (subnormal E4M3 scales), some below
+        # 6 * 2^-10 (a scale of zero: all-zero groups), beside normal ones
+        lat *= _group_scale(rng, n_rows * n_entries, -14, -5, frac=0.7)
+        q *= np.float32(4.0)
+    elif case == "window_spread":
+        # window groups spread over 30 octaves within an entry: groups more
+        # than 22 octaves below a row's largest one are rounded in fp16
+        swa *= _group_scale(rng, n_rows * 128, -20, 10)
+        q *= np.float32(2.0 ** -8)
+    elif case == "window_huge":
+        # half of the window groups with amax at 2^29 .. 2^32 (E8M0 exponents
+        # 21 .. 23, across the point where a factor shared with the selected
+        # entries would overflow fp16), the others N(0,1)
+        swa *= _group_scale(rng, n_rows * 128, 29, 31, frac=0.5)
+        q *= np.float32(2.0 ** -33)
+        # outputs of magnitude ~2^27 carry an fp32 ulp of 16: the absolute
+        # term of the tolerance scales with the window (2^31)
+        return lat, swa, q, 2.0 ** 31
+    elif case == "window_tiny":
+        # a window at 2^-100: the factor that lifts it is capped
+        swa *= np.float32(2.0 ** -100)
+    else:
+        raise ValueError(case)
+    return lat, swa, q, 1.0
+
+
+@pytest.mark.parametrize("case", ["main_fp4_max", "main_subnormal_scales", "window_spread", "window_huge",
+                                  "window_tiny"])
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_edge_scales(case, H):
+    """Edge scales of the dequantised operands, every call form, split (with
+    a workspace, few rows) and one-workgroup: selected counts that put a
+    selected-to-window crossing inside a unit (65 + 128, 512 + 128)."""
+    n_rows, n_entries = 4, 700
+    lat, swa, q, win_scale = _edge_data(case, n_rows, H, n_entries)
+    _attn_case(n_rows, H, [512, 65, 300, 0], [128, 128, 37, 128], n_entries=n_entries, lat=lat, swa=swa, q=q,
+               sink=case == "window_spread", win_scale=win_scale)
 
 
 @pytest.mark.parametrize("H", [16, 48, 64, 128])
