@@ -277,6 +277,29 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
                                  float softmax_scale, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as csa2_sparse_swa_attn without a workspace argument.  Where the call
+ * would spread rows over several workgroups, its partial results go to a
+ * device array the library owns instead: CSA2_ATTN_SCRATCH_BYTES per GPU,
+ * held from the library's load on that GPU until the process ends, its
+ * address looked up on the first call on each device.  The call itself
+ * allocates and frees nothing.  Outputs are the bits csa2_sparse_swa_attn
+ * gives with a workspace (and without one).  The scratch needs no clearing
+ * (every partial a call folds is written earlier in that call), but it is
+ * one array per GPU: calls that overlap on the same GPU (other streams, other
+ * host threads) race on it and must be serialised by the caller.  A call
+ * whose split pass would need more than CSA2_ATTN_SCRATCH_BYTES returns
+ * CSA2_ERR_RANGE before any launch (no supported shape does: the split pass
+ * is used up to 2,048 (row, head) pairs). */
+#define CSA2_ATTN_SCRATCH_BYTES ((size_t)2048 * 4 * 514 * 4)
+csa2_status csa2_sparse_swa_attn_noalloc(const csa2_kv* kv, const csa2_rows* rows,
+                                         const void* q, csa2_dtype q_dtype, int32_t n_heads,
+                                         const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
+                                         const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                                         const int64_t* swa_first, const int32_t* swa_count, const float* sink,
+                                         float softmax_scale, float* out, float* lse, void* stream);
+
 /* ---------------------------------------------------------------- streaming-read reference
  * Not a step of the method: the plain streaming read that the indexer scan's
  * HBM rate is measured against.  Reads the n_bytes of buf once (16-B

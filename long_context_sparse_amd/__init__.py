@@ -48,7 +48,7 @@ EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
     "csa2_index_score_shared",
     "csa2_select_topk_workspace", "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
-    "csa2_sparse_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost", "csa2_stream_xor",
+    "csa2_sparse_swa_attn", "csa2_sparse_swa_attn_noalloc", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost", "csa2_stream_xor",
 )
 
 
@@ -82,6 +82,8 @@ def lib():
     L.csa2_swa_merge.argtypes = [P, P, i64, P, P, i32, P, ctypes.c_int, i32, f32, P, P, P, P, P, ctypes.c_size_t, P]
     L.csa2_sparse_swa_attn.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P, i64, P,
                                        P, P, i64, P, P, P, f32, P, P, P, ctypes.c_size_t, P]
+    L.csa2_sparse_swa_attn_noalloc.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P,
+                                               i64, P, P, P, i64, P, P, P, f32, P, P, P]
     L.csa2_synth_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, ctypes.c_int, P, P]
     L.csa2_synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, P, P]
     L.csa2_synth_boost.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, i32, P, P]
@@ -241,6 +243,17 @@ def csa2_sparse_swa_attn(kv, rows, q, idx, idx_count, swa_codes, swa_scales, swa
         _ptr(idx_count), _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first),
         _ptr(swa_count), _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse),
         *_ws(workspace), _stream(stream)))
+
+
+def csa2_sparse_swa_attn_noalloc(kv, rows, q, idx, idx_count, swa_codes, swa_scales, swa_first, swa_count,
+                                 softmax_scale, out, sink=None, lse=None, stream=None):
+    """csa2_sparse_swa_attn without a workspace: the split pass uses the
+    library's own per-GPU scratch (calls overlapping on one GPU race)."""
+    H = int(q.shape[1])
+    _check("csa2_sparse_swa_attn_noalloc", lib().csa2_sparse_swa_attn_noalloc(
+        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), _rstride(idx),
+        _ptr(idx_count), _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first),
+        _ptr(swa_count), _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def csa2_synth_normal(seed, tensor_id, first, out, stream=None):

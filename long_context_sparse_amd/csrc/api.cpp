@@ -383,14 +383,13 @@ csa2_status csa2_swa_merge(const uint8_t* swa_codes, const uint8_t* swa_scales, 
     return hip_status(csa2::launch_attn(none, a, workspace_bytes, (hipStream_t)stream), "csa2_swa_merge launch");
 }
 
-csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
-                                 int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
-                                 const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
-                                 const int64_t* swa_first, const int32_t* swa_count, const float* sink,
-                                 float softmax_scale, float* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    csa2::KvView v;
-    csa2_status s = make_view(kv, true, false, &v);
+static csa2_status sparse_swa_args(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
+                                   int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
+                                   const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                                   const int64_t* swa_first, const int32_t* swa_count, const float* sink,
+                                   float softmax_scale, float* out, float* lse, void* workspace, csa2::KvView* v,
+                                   csa2::AttnArgs* a) {
+    csa2_status s = make_view(kv, true, false, v);
     if (s != CSA2_OK) return s;
     if ((s = check_rows(rows)) != CSA2_OK) return s;
     if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale, workspace)) != CSA2_OK) return s;
@@ -399,20 +398,58 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const
     if (!idx || !idx_count || !out) return fail(CSA2_ERR_NULL, "idx / idx_count / out is NULL");
     if (!aligned(out, 16)) return fail(CSA2_ERR_ALIGN, "out must be 16-byte aligned");
     if (idx_stride < 1) return fail(CSA2_ERR_SHAPE, "idx_stride must be >= 1");
+    fill_q(*a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
+    a->req = rows->req;
+    a->idx = idx;
+    a->idx_stride = idx_stride;
+    a->idx_count = idx_count;
+    a->swa_codes = swa_codes;
+    a->swa_scales = swa_scales;
+    a->swa_first = swa_first;
+    a->swa_count = swa_count;
+    a->sink = sink;
+    a->out = out;
+    a->lse_out = lse;
+    return CSA2_OK;
+}
+
+csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
+                                 int32_t n_heads, const int32_t* idx, int64_t idx_stride, const int32_t* idx_count,
+                                 const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                                 const int64_t* swa_first, const int32_t* swa_count, const float* sink,
+                                 float softmax_scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    csa2::KvView v;
     csa2::AttnArgs a;
-    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
-    a.req = rows->req;
-    a.idx = idx;
-    a.idx_stride = idx_stride;
-    a.idx_count = idx_count;
-    a.swa_codes = swa_codes;
-    a.swa_scales = swa_scales;
-    a.swa_first = swa_first;
-    a.swa_count = swa_count;
-    a.sink = sink;
-    a.out = out;
-    a.lse_out = lse;
+    csa2_status s = sparse_swa_args(kv, rows, q, q_dtype, n_heads, idx, idx_stride, idx_count, swa_codes, swa_scales,
+                                    swa_slots, swa_first, swa_count, sink, softmax_scale, out, lse, workspace, &v, &a);
+    if (s != CSA2_OK || rows->n_rows == 0) return s;
     return hip_status(csa2::launch_attn(v, a, workspace_bytes, (hipStream_t)stream), "csa2_sparse_swa_attn launch");
+}
+
+csa2_status csa2_sparse_swa_attn_noalloc(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
+                                         int32_t n_heads, const int32_t* idx, int64_t idx_stride,
+                                         const int32_t* idx_count, const uint8_t* swa_codes,
+                                         const uint8_t* swa_scales, int64_t swa_slots, const int64_t* swa_first,
+                                         const int32_t* swa_count, const float* sink, float softmax_scale,
+                                         float* out, float* lse, void* stream) {
+    csa2::KvView v;
+    csa2::AttnArgs a;
+    csa2_status s = sparse_swa_args(kv, rows, q, q_dtype, n_heads, idx, idx_stride, idx_count, swa_codes, swa_scales,
+                                    swa_slots, swa_first, swa_count, sink, softmax_scale, out, lse, nullptr, &v, &a);
+    if (s != CSA2_OK || rows->n_rows == 0) return s;
+    const size_t need = csa2_attn_workspace_size(rows->n_rows, n_heads);
+    if (need > CSA2_ATTN_SCRATCH_BYTES)
+        return fail(CSA2_ERR_RANGE, "csa2_sparse_swa_attn_noalloc: the split pass of %d rows x %d heads needs %zu "
+                                    "bytes of scratch, more than the %zu the library holds",
+                    rows->n_rows, n_heads, need, (size_t)CSA2_ATTN_SCRATCH_BYTES);
+    if (need == 0) return hip_status(csa2::launch_attn(v, a, 0, (hipStream_t)stream), "csa2_sparse_swa_attn_noalloc launch");
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    hipError_t e = csa2::noalloc_scratch(&ptr, &bytes);
+    if (e != hipSuccess) return hip_status(e, "csa2_sparse_swa_attn_noalloc: scratch address");
+    a.ws = (float*)ptr;
+    return hip_status(csa2::launch_attn(v, a, need, (hipStream_t)stream), "csa2_sparse_swa_attn_noalloc launch");
 }
 
 csa2_status csa2_synth_normal(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n, csa2_dtype out_dtype,

@@ -96,6 +96,10 @@ int attn_splits(int n_rows, int n_heads);
 size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits);
 hipError_t launch_attn(const KvView& kv, const AttnArgs& a, size_t ws_bytes, hipStream_t st);
 
+// Address (on the current device) and size of the library's own scratch
+// array for the allocation-free attention; looked up once per device.
+hipError_t noalloc_scratch(void** out, size_t* bytes);
+
 hipError_t launch_stream_xor(const void* buf, int64_t n_bytes, uint32_t* out, hipStream_t st);
 
 hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,
