@@ -277,6 +277,29 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
                                  float softmax_scale, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Dense form for the heavily compressed branch ('DeepSeek-V4' page, section
+ * 2.3.2: every m' = 128 tokens are compressed into one entry and the query
+ * attends to ALL of them, no sparse selection; the same shared-KV MQA, and,
+ * as section 2.3.3 adds, the same sliding-window branch and sink): the
+ * entries of row r are the MAIN entries of its positions 0 .. n_vis[r]-1
+ * (every visible compressed entry; rows->max_vis bounds them, at most
+ * CSA2_MAX_DENSE), joined in one softmax with the window entries (swa_codes
+ * NULL: no window) and the sink.  Same output conventions, numerics and
+ * bitwise batch invariance as csa2_sparse_swa_attn (the entry list is the
+ * row's entries padded to a multiple of 64, then the window, cut into units
+ * of 192 entries folded left to right).  workspace: NULL or
+ * csa2_dense_attn_workspace_size(n_rows, n_heads, rows->max_vis) bytes,
+ * 256-B aligned, not kept between calls; with it a launch with few rows
+ * spreads each row's units over several workgroups. */
+#define CSA2_MAX_DENSE (1 << 22)
+size_t csa2_dense_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t max_vis);
+csa2_status csa2_dense_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
+                                const void* q, csa2_dtype q_dtype, int32_t n_heads,
+                                const uint8_t* swa_codes, const uint8_t* swa_scales, int64_t swa_slots,
+                                const int64_t* swa_first, const int32_t* swa_count, const float* sink,
+                                float softmax_scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same
  * call as csa2_sparse_swa_attn without a workspace argument.  Where the call

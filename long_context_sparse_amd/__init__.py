@@ -48,7 +48,8 @@ EXPORTS = (
     "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
     "csa2_index_score_shared",
     "csa2_select_topk_workspace", "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
-    "csa2_sparse_swa_attn", "csa2_sparse_swa_attn_noalloc", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost", "csa2_stream_xor",
+    "csa2_sparse_swa_attn", "csa2_sparse_swa_attn_noalloc", "csa2_dense_attn_workspace_size",
+    "csa2_dense_swa_attn", "csa2_synth_normal", "csa2_synth_uniform", "csa2_synth_boost", "csa2_stream_xor",
 )
 
 
@@ -84,13 +85,17 @@ def lib():
                                        P, P, i64, P, P, P, f32, P, P, P, ctypes.c_size_t, P]
     L.csa2_sparse_swa_attn_noalloc.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P,
                                                i64, P, P, P, i64, P, P, P, f32, P, P, P]
+    L.csa2_dense_attn_workspace_size.restype = ctypes.c_size_t
+    L.csa2_dense_attn_workspace_size.argtypes = [i32, i32, i32]
+    L.csa2_dense_swa_attn.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P, P, i64, P, P,
+                                      P, f32, P, P, P, ctypes.c_size_t, P]
     L.csa2_synth_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, ctypes.c_int, P, P]
     L.csa2_synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, P, P]
     L.csa2_synth_boost.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i64, i64, i32, P, P]
     L.csa2_stream_xor.argtypes = [P, i64, P, P]
     for name in EXPORTS:
         if name not in ("csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_attn_workspace_size",
-                        "csa2_select_topk_workspace"):
+                        "csa2_select_topk_workspace", "csa2_dense_attn_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -254,6 +259,21 @@ def csa2_sparse_swa_attn_noalloc(kv, rows, q, idx, idx_count, swa_codes, swa_sca
         ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(idx), _rstride(idx),
         _ptr(idx_count), _ptr(swa_codes), _ptr(swa_scales), int(swa_codes.shape[0]), _ptr(swa_first),
         _ptr(swa_count), _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def csa2_dense_attn_workspace_size(n_rows, n_heads, max_vis) -> int:
+    return int(lib().csa2_dense_attn_workspace_size(int(n_rows), int(n_heads), int(max_vis)))
+
+
+def csa2_dense_swa_attn(kv, rows, q, softmax_scale, out, swa_codes=None, swa_scales=None, swa_first=None,
+                        swa_count=None, sink=None, lse=None, workspace=None, stream=None):
+    """Attention over every visible entry of each row (the heavily
+    compressed branch), jointly with the window (optional) and the sink."""
+    H = int(q.shape[1])
+    _check("csa2_dense_swa_attn", lib().csa2_dense_swa_attn(
+        ctypes.byref(kv), ctypes.byref(rows), _ptr(q), _dtype(q), H, _ptr(swa_codes), _ptr(swa_scales),
+        0 if swa_codes is None else int(swa_codes.shape[0]), _ptr(swa_first), _ptr(swa_count), _ptr(sink),
+        float(softmax_scale), _ptr(out), _ptr(lse), *_ws(workspace), _stream(stream)))
 
 
 def csa2_synth_normal(seed, tensor_id, first, out, stream=None):

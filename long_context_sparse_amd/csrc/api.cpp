@@ -452,6 +452,44 @@ csa2_status csa2_sparse_swa_attn_noalloc(const csa2_kv* kv, const csa2_rows* row
     return hip_status(csa2::launch_attn(v, a, need, (hipStream_t)stream), "csa2_sparse_swa_attn_noalloc launch");
 }
 
+size_t csa2_dense_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t max_vis) {
+    if (n_rows <= 0 || n_heads < 16 || n_heads > 128 || max_vis < 0 || max_vis > CSA2_MAX_DENSE) return 0;
+    return csa2::dense_workspace_bytes(n_rows, n_heads, max_vis);
+}
+
+csa2_status csa2_dense_swa_attn(const csa2_kv* kv, const csa2_rows* rows, const void* q, csa2_dtype q_dtype,
+                                int32_t n_heads, const uint8_t* swa_codes, const uint8_t* swa_scales,
+                                int64_t swa_slots, const int64_t* swa_first, const int32_t* swa_count,
+                                const float* sink, float softmax_scale, float* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    csa2::KvView v;
+    csa2_status s = make_view(kv, true, false, &v);
+    if (s != CSA2_OK) return s;
+    if ((s = check_rows(rows)) != CSA2_OK) return s;
+    if ((s = check_common(rows->n_rows, q, q_dtype, n_heads, softmax_scale, workspace)) != CSA2_OK) return s;
+    if (rows->max_vis > CSA2_MAX_DENSE)
+        return fail(CSA2_ERR_RANGE, "max_vis %d above %d entries", rows->max_vis, CSA2_MAX_DENSE);
+    if (rows->n_rows == 0) return CSA2_OK;
+    if (swa_codes && (s = check_swa(swa_codes, swa_scales, swa_slots, swa_first, swa_count)) != CSA2_OK) return s;
+    if (!out) return fail(CSA2_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(CSA2_ERR_ALIGN, "out must be 16-byte aligned");
+    csa2::AttnArgs a;
+    fill_q(a, q, q_dtype, n_heads, rows->n_rows, softmax_scale, workspace);
+    a.req = rows->req;
+    a.dense_n = rows->n_vis;
+    a.max_dense = rows->max_vis;
+    if (swa_codes) {
+        a.swa_codes = swa_codes;
+        a.swa_scales = swa_scales;
+        a.swa_first = swa_first;
+        a.swa_count = swa_count;
+    }
+    a.sink = sink;
+    a.out = out;
+    a.lse_out = lse;
+    return hip_status(csa2::launch_attn_dense(v, a, workspace_bytes, (hipStream_t)stream), "csa2_dense_swa_attn launch");
+}
+
 csa2_status csa2_synth_normal(uint64_t seed, uint32_t tensor_id, int64_t first, int64_t n, csa2_dtype out_dtype,
                               void* out, void* stream) {
     if (n < 0 || first < 0) return fail(CSA2_ERR_RANGE, "first / n must be >= 0");

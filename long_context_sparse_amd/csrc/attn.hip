@@ -92,17 +92,20 @@ struct RawChunk {
     uint32_t s;
 };
 
+template <bool DENSE>
 __device__ __forceinline__ void load_raw(const KvView& kv, const AttnArgs& a, const AttnSmem& sm, int c, int csp,
-                                         int nsp, int nsw, int64_t swa0, int et, int kh, int n, int g, RawChunk& r) {
+                                         int nsp, int nsw, int64_t swa0, int req, int et, int kh, int n, int g,
+                                         RawChunk& r) {
     // Addresses are selected, the loads are issued unconditionally (the
     // selected-entry case re-reads its 32 code bytes for c[2..3], unused).
+    // DENSE: the row's entry e is its position e (every visible entry).
     const bool sel = c < csp;
     int e = 16 * et + n + 64 * (sel ? c : c - csp);
     e = e < (sel ? nsp : nsw) ? e : 0;                // padding lanes re-read entry 0 (masked later)
     const uint8_t* cp;
     const uint8_t* sp;
     if (sel) {
-        const int64_t slot = sm.ent[e];
+        const int64_t slot = DENSE ? entry_of(kv, req, e) : sm.ent[e];
         cp = kv.main_codes + slot * 256 + 128 * kh + 32 * g;
         sp = kv.main_scales + slot * 32 + 16 * kh + 4 * g;
     } else {
@@ -256,7 +259,7 @@ __device__ __forceinline__ int xcd_order(int b, int total) {
 // Units of a row's entry list: ceil(chunks / 3), chunks = ceil(selected / 64)
 // + ceil(window / 64).
 __device__ __forceinline__ int row_units(const AttnArgs& a, int nsp_raw, int nsw_raw) {
-    const int nsp = a.idx ? min(max(nsp_raw, 0), AT_MAX_SEL) : 0;
+    const int nsp = a.dense_n ? min(max(nsp_raw, 0), a.max_dense) : (a.idx ? min(max(nsp_raw, 0), AT_MAX_SEL) : 0);
     const int nsw = a.swa_codes ? min(max(nsw_raw, 0), 128) : 0;
     const int ctot = (nsp + AT_ENT - 1) / AT_ENT + (nsw + AT_ENT - 1) / AT_ENT;
     return (ctot + AT_UNIT - 1) / AT_UNIT;
@@ -304,7 +307,7 @@ __device__ __forceinline__ f32x4 final_out(const FinalW& f, f32x4 O, float4 pin)
 // SPLIT: the launch has several splits per (row, group) (their partials go to
 // the workspace); without it the workgroup folds its units itself, and only
 // that form holds the folded output in registers.
-template <bool QBF16, bool SPLIT>
+template <bool QBF16, bool SPLIT, bool DENSE>
 __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a) {
     extern __shared__ __align__(16) uint8_t at_smem[];
     AttnSmem& sm = *(AttnSmem*)at_smem;
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int n = l & 15, g = l >> 4;
     const int et = wave & 3, kh = wave >> 2;
-    const int nsp = a.idx ? min(max(a.idx_count[row], 0), AT_MAX_SEL) : 0;
+    const int nsp = DENSE ? min(max(a.dense_n[row], 0), a.max_dense)
+                          : (a.idx ? min(max(a.idx_count[row], 0), AT_MAX_SEL) : 0);
     const int nsw = a.swa_codes ? min(max(a.swa_count[row], 0), 128) : 0;
     const int csp = (nsp + AT_ENT - 1) / AT_ENT;
     const int ctot = csp + (nsw + AT_ENT - 1) / AT_ENT;
@@ -332,15 +336,16 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // issued before any is used, from a valid address (a dummy one where it is
     // not needed): a load under a branch makes the compiler wait for it where
     // the branch joins, which would put three memory round trips in a row.
-    const int32_t* idx_p = a.idx ? a.idx + (int64_t)row * a.idx_stride + min((int64_t)threadIdx.x, a.idx_stride - 1)
-                                 : (const int32_t*)a.q;
+    const int32_t* idx_p = (!DENSE && a.idx) ? a.idx + (int64_t)row * a.idx_stride +
+                                                   min((int64_t)threadIdx.x, a.idx_stride - 1)
+                                             : (const int32_t*)a.q;
     const int32_t idx_raw = *idx_p;
     const int req_r = *(a.req ? a.req + row : (const int32_t*)a.q);
     const bool has_sc = (int)threadIdx.x * 8 < nsw * 32;
     const uint2 scv = *(const uint2*)(has_sc ? a.swa_scales + swa0 * 32 + 8 * threadIdx.x : (const uint8_t*)a.q);
     bf16x8 qb[8];
     float qa = load_q_operand<QBF16>(a.q, (int64_t)row * a.n_heads + h0 + n, kh, g, qb);
-    if ((int)threadIdx.x < nsp) sm.ent[threadIdx.x] = entry_of(kv, req_r, idx_raw);   // paged: one more load
+    if (!DENSE && (int)threadIdx.x < nsp) sm.ent[threadIdx.x] = entry_of(kv, req_r, idx_raw);   // paged: one more load
     int wmax = 0, wmin = 255;                       // over nonzero scale codes (all-zero groups have code 0)
     if (has_sc) {
 #pragma unroll
@@ -391,9 +396,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // microseconds to arrive when every CU is gathering).
     RawChunk raw0, raw1, raw2;
     if (ce > cb) {
-        load_raw(kv, a, sm, cb, csp, nsp, nsw, swa0, et, kh, n, g, raw0);
-        load_raw(kv, a, sm, min(cb + 1, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw1);
-        load_raw(kv, a, sm, min(cb + 2, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw2);
+        load_raw<DENSE>(kv, a, sm, cb, csp, nsp, nsw, swa0, req_r, et, kh, n, g, raw0);
+        load_raw<DENSE>(kv, a, sm, min(cb + 1, ce - 1), csp, nsp, nsw, swa0, req_r, et, kh, n, g, raw1);
+        load_raw<DENSE>(kv, a, sm, min(cb + 2, ce - 1), csp, nsp, nsw, swa0, req_r, et, kh, n, g, raw2);
     }
     f32x4 oacc[4];
 #pragma unroll
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         else dequant_main(raw, cvt_sel, vb + v_lane, kop);
         // always issued (near the end they re-read the final chunk, unused): a
         // load under a branch makes the compiler wait for it at the join
-        load_raw(kv, a, sm, min(c + 3, ce - 1), csp, nsp, nsw, swa0, et, kh, n, g, raw);
+        load_raw<DENSE>(kv, a, sm, min(c + 3, ce - 1), csp, nsp, nsw, swa0, req_r, et, kh, n, g, raw);
         f32x4 sc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], qh[ks], sc, 0, 0, 0);
@@ -503,10 +508,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     auto end_unit = [&](const int u, const int c_last) __attribute__((always_inline)) {
         const float pw = c_last >= csp ? pw_win : pw_sel;
         if constexpr (SPLIT) {
-            const size_t ps = ((size_t)row * a.n_heads + h) * AT_MAX_UNITS + u;
+            const size_t ps = ((size_t)row * a.n_heads + h) * a.max_units + u;
             float* wsO = a.ws;
-            float* wsM = wsO + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS * 512;
-            float* wsL = wsM + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS;
+            float* wsM = wsO + (size_t)a.n_rows * a.n_heads * a.max_units * 512;
+            float* wsL = wsM + (size_t)a.n_rows * a.n_heads * a.max_units;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
                 // partials are written once and read by another kernel:
@@ -561,9 +566,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
 
 // Folds the unit partials of every (row, head) in unit order, then joins the
 // external partial and the sink: the same operations as the epilogue of a
-// single-split attn_kernel.  One thread per (row, head, 4 channels); every
-// load is issued before any is used (slots past the row's unit count are
-// read but not folded).
+// single-split attn_kernel.  One thread per (row, head, 4 channels).  Sparse
+// rows have at most AT_MAX_UNITS units, whose loads are all issued before
+// any is used (slots past the row's unit count are read but not folded);
+// dense rows walk their units with the next unit's loads in flight.
+template <bool DENSE>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -571,30 +578,52 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int64_t rh = t >> 7;                        // row * n_heads + head
     const int c4 = (int)(t & 127) * 4;
     const int row = (int)(rh / a.n_heads), h = (int)(rh - (int64_t)row * a.n_heads);
+    const int MU = DENSE ? a.max_units : AT_MAX_UNITS;
     const float* wsO = a.ws;
-    const float* wsM = wsO + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS * 512;
-    const float* wsL = wsM + (size_t)a.n_rows * a.n_heads * AT_MAX_UNITS;
-    const int nsp_raw = a.idx ? a.idx_count[row] : 0;
+    const float* wsM = wsO + (size_t)a.n_rows * a.n_heads * MU * 512;
+    const float* wsL = wsM + (size_t)a.n_rows * a.n_heads * MU;
+    const int nsp_raw = DENSE ? a.dense_n[row] : (a.idx ? a.idx_count[row] : 0);
     const int nsw_raw = a.swa_codes ? a.swa_count[row] : 0;
-    float m[AT_MAX_UNITS], lw[AT_MAX_UNITS];
-    f32x4 o[AT_MAX_UNITS];
-#pragma unroll
-    for (int u = 0; u < AT_MAX_UNITS; ++u) {
-        m[u] = wsM[rh * AT_MAX_UNITS + u];
-        lw[u] = wsL[rh * AT_MAX_UNITS + u];
-        o[u] = *(const f32x4*)(wsO + (rh * AT_MAX_UNITS + u) * 512 + c4);
-    }
     const float lse_p = a.lse_in ? a.lse_in[rh] * LOG2E : -INFINITY;
     const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
     const float4 pin = a.o_in ? *(const float4*)(a.o_in + rh * 512 + c4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     const int U = row_units(a, nsp_raw, nsw_raw);
     float M = -INFINITY, L = 0.0f;
     f32x4 O = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!DENSE) {
+        float m[AT_MAX_UNITS], lw[AT_MAX_UNITS];
+        f32x4 o[AT_MAX_UNITS];
 #pragma unroll
-    for (int u = 0; u < AT_MAX_UNITS; ++u) {
-        if (u < U) {
-            const FoldW f = fold_unit(M, L, m[u], lw[u]);
-            O = fold_out(f, O, o[u]);
+        for (int u = 0; u < AT_MAX_UNITS; ++u) {
+            m[u] = wsM[rh * AT_MAX_UNITS + u];
+            lw[u] = wsL[rh * AT_MAX_UNITS + u];
+            o[u] = *(const f32x4*)(wsO + (rh * AT_MAX_UNITS + u) * 512 + c4);
+        }
+#pragma unroll
+        for (int u = 0; u < AT_MAX_UNITS; ++u) {
+            if (u < U) {
+                const FoldW f = fold_unit(M, L, m[u], lw[u]);
+                O = fold_out(f, O, o[u]);
+            }
+        }
+    } else {
+        const int Uc = min(U, MU);
+        float mn = 0.0f, ln = 0.0f;
+        f32x4 on = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        if (Uc > 0) {
+            mn = wsM[rh * MU];
+            ln = wsL[rh * MU];
+            on = *(const f32x4*)(wsO + (rh * MU) * 512 + c4);
+        }
+        for (int u = 0; u < Uc; ++u) {
+            const float mu = mn, lu = ln;
+            const f32x4 ou = on;
+            const int un = min(u + 1, Uc - 1);        // the next unit's loads (the last one re-reads itself)
+            mn = wsM[rh * MU + un];
+            ln = wsL[rh * MU + un];
+            on = *(const f32x4*)(wsO + (rh * MU + un) * 512 + c4);
+            const FoldW f = fold_unit(M, L, mu, lu);
+            O = fold_out(f, O, ou);
         }
     }
     const FinalW fw = final_weights(M, L, lse_p, sk);
@@ -615,8 +644,27 @@ size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits) {
     return (size_t)n_rows * n_heads * AT_MAX_UNITS * (512 + 2) * sizeof(float);
 }
 
+// Dense rows of up to max_dense entries: units of the longest row, and the
+// splits that fill the 256 CUs once (at most one per unit).
+int dense_units(int max_dense) {
+    const int chunks = (max_dense + AT_ENT - 1) / AT_ENT + 128 / AT_ENT;
+    return (chunks + AT_UNIT - 1) / AT_UNIT;
+}
+
+int dense_splits(int n_rows, int n_heads, int max_dense) {
+    const int groups = n_rows * (n_heads >> 4);
+    if (groups <= 0) return 1;
+    const int s = 256 / groups, u = dense_units(max_dense);
+    return s < 2 ? 1 : (s > u ? u : s);
+}
+
+size_t dense_workspace_bytes(int n_rows, int n_heads, int max_dense) {
+    if (dense_splits(n_rows, n_heads, max_dense) <= 1) return 0;
+    return (size_t)n_rows * n_heads * dense_units(max_dense) * (512 + 2) * sizeof(float);
+}
+
 // The kernels' dynamic LDS above 64 KB is allowed once per device (the flag
-// per device is set only after both attributes succeeded; a race between two
+// per device is set only after every attribute succeeded; a race between two
 // host threads on a new device repeats the same idempotent calls).
 constexpr int AT_MAX_DEVICES = 64;
 static std::atomic<bool> g_attr_set[AT_MAX_DEVICES];
@@ -627,30 +675,52 @@ static hipError_t set_lds_attrs() {
     if (e != hipSuccess) return e;
     const bool cached = dev >= 0 && dev < AT_MAX_DEVICES;
     if (cached && g_attr_set[dev].load(std::memory_order_acquire)) return hipSuccess;
-    const void* kernels[4] = {(const void*)attn_kernel<true, false>, (const void*)attn_kernel<false, false>,
-                              (const void*)attn_kernel<true, true>, (const void*)attn_kernel<false, true>};
+    const void* kernels[8] = {
+        (const void*)attn_kernel<true, false, false>, (const void*)attn_kernel<false, false, false>,
+        (const void*)attn_kernel<true, true, false>,  (const void*)attn_kernel<false, true, false>,
+        (const void*)attn_kernel<true, false, true>,  (const void*)attn_kernel<false, false, true>,
+        (const void*)attn_kernel<true, true, true>,   (const void*)attn_kernel<false, true, true>};
     for (const void* k : kernels)
         if ((e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)AT_LDS)) != hipSuccess) return e;
     if (cached) g_attr_set[dev].store(true, std::memory_order_release);
     return hipSuccess;
 }
 
+template <bool DENSE>
+static hipError_t launch_attn_kind(const KvView& kv, const AttnArgs& a, hipStream_t st) {
+    const unsigned blocks = (unsigned)a.n_rows * (unsigned)(a.n_heads >> 4) * (unsigned)a.n_splits;
+    const bool split = a.n_splits > 1;
+    if (a.q_bf16 && split) hipLaunchKernelGGL((attn_kernel<true, true, DENSE>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else if (a.q_bf16) hipLaunchKernelGGL((attn_kernel<true, false, DENSE>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else if (split) hipLaunchKernelGGL((attn_kernel<false, true, DENSE>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    else hipLaunchKernelGGL((attn_kernel<false, false, DENSE>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !split) return e;
+    const int64_t threads = (int64_t)a.n_rows * a.n_heads * 128;
+    hipLaunchKernelGGL((attn_merge_kernel<DENSE>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(const KvView& kv, const AttnArgs& a_in, size_t ws_bytes, hipStream_t st) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
     AttnArgs a = a_in;
+    a.dense_n = nullptr;
+    a.max_units = AT_MAX_UNITS;
     a.n_splits = attn_splits(a.n_rows, a.n_heads);
     if (!a.ws || ws_bytes < attn_workspace_bytes(a.n_rows, a.n_heads, a.n_splits)) a.n_splits = 1;
-    const unsigned blocks = (unsigned)a.n_rows * (unsigned)(a.n_heads >> 4) * (unsigned)a.n_splits;
-    const bool split = a.n_splits > 1;
-    if (a.q_bf16 && split) hipLaunchKernelGGL((attn_kernel<true, true>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
-    else if (a.q_bf16) hipLaunchKernelGGL((attn_kernel<true, false>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
-    else if (split) hipLaunchKernelGGL((attn_kernel<false, true>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
-    else hipLaunchKernelGGL((attn_kernel<false, false>), dim3(blocks), dim3(AT_THREADS), AT_LDS, st, kv, a);
-    if ((e = hipGetLastError()) != hipSuccess || a.n_splits == 1) return e;
-    const int64_t threads = (int64_t)a.n_rows * a.n_heads * 128;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
-    return hipGetLastError();
+    return launch_attn_kind<false>(kv, a, st);
+}
+
+hipError_t launch_attn_dense(const KvView& kv, const AttnArgs& a_in, size_t ws_bytes, hipStream_t st) {
+    hipError_t e = set_lds_attrs();
+    if (e != hipSuccess) return e;
+    AttnArgs a = a_in;
+    a.idx = nullptr;
+    a.max_units = dense_units(a.max_dense);
+    a.n_splits = dense_splits(a.n_rows, a.n_heads, a.max_dense);
+    if (!a.ws || ws_bytes < dense_workspace_bytes(a.n_rows, a.n_heads, a.max_dense)) a.n_splits = 1;
+    return launch_attn_kind<true>(kv, a, st);
 }
 
 }  // namespace csa2

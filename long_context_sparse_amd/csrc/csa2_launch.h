@@ -90,11 +90,19 @@ struct AttnArgs {
     float* out;
     float* lse_out;
     float* ws;                   // split partials (NULL: one workgroup per row and head group)
-    int n_splits;                // set by launch_attn
+    int n_splits;                // set by the launchers
+    int max_units;               // unit slots per (row, head) in ws; set by the launchers
+    const int32_t* dense_n;      // dense rows: entries [0, dense_n[row]) of the row (launch_attn_dense)
+    int max_dense;               // bound on dense_n
 };
 int attn_splits(int n_rows, int n_heads);
 size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits);
 hipError_t launch_attn(const KvView& kv, const AttnArgs& a, size_t ws_bytes, hipStream_t st);
+// Every visible entry of each row instead of a selection (the heavily
+// compressed branch): a.dense_n / a.max_dense give the rows' entry counts.
+int dense_units(int max_dense);
+size_t dense_workspace_bytes(int n_rows, int n_heads, int max_dense);
+hipError_t launch_attn_dense(const KvView& kv, const AttnArgs& a, size_t ws_bytes, hipStream_t st);
 
 // Address (on the current device) and size of the library's own scratch
 // array for the allocation-free attention; looked up once per device.

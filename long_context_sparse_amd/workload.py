@@ -12,6 +12,8 @@ together as one step of the hot path:
                 -> csa2_sparse_swa_attn (or csa2_sparse_attn -> csa2_swa_merge)
   Reuse layer   csa2_sparse_swa_attn with the layer's own query and window over
                 the positions the last Full or Reindex layer selected
+  Dense layer   csa2_dense_swa_attn over every compressed entry (the heavily
+                compressed branch of the V4 hybrid attention), window, sink
 
 A whole step (every layer) can also be captured once per KV copy as a HIP
 graph and replayed (``capture_graphs`` / ``replay``).
@@ -31,10 +33,10 @@ import torch
 import synth
 from synth.configs import Config
 
-from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_attn_workspace_size, csa2_index_score,
-               csa2_index_score_shared, csa2_pack_kv, csa2_select_full, csa2_select_topk, csa2_sparse_attn,
-               csa2_sparse_swa_attn, csa2_swa_merge, csa2_synth_boost, csa2_synth_normal, csa2_synth_uniform,
-               make_kv, make_rows)
+from . import (BF16, F32, INDEX_MXFP4, MAIN_FP4, SWA_FP8, csa2_attn_workspace_size, csa2_dense_attn_workspace_size,
+               csa2_dense_swa_attn, csa2_index_score, csa2_index_score_shared, csa2_pack_kv, csa2_select_full,
+               csa2_select_topk, csa2_sparse_attn, csa2_sparse_swa_attn, csa2_swa_merge, csa2_synth_boost,
+               csa2_synth_normal, csa2_synth_uniform, make_kv, make_rows)
 
 GEN_CHUNK = 1 << 20   # entries generated per chunk
 
@@ -76,7 +78,12 @@ class Layer:
         s = cfg.seed
         self.q = torch.empty((n_rows, H, 512), dtype=torch.bfloat16, device=dev)
         csa2_synth_normal(s, synth.T_Q + off, 0, self.q)
-        if role != "reuse":
+        self.sink = None
+        if cfg.extra.get("sink"):
+            # per-head sink logits, N(0,1) rounded to bf16, kept in fp32
+            self.sink = torch.empty((H,), dtype=torch.float32, device=dev)
+            csa2_synth_normal(s, synth.T_SINK + off, 0, self.sink)
+        if role not in ("reuse", "dense"):
             self.q_idx = torch.empty((n_rows, Hi, 128), dtype=torch.bfloat16, device=dev)
             csa2_synth_normal(s, synth.T_QIDX + off, 0, self.q_idx)
             self.w = torch.empty((n_rows, Hi), dtype=torch.float32, device=dev)
@@ -90,6 +97,8 @@ class Layer:
         if source is not None:
             # the positions (and counts) of the last Full or Reindex layer
             self.idx, self.idx_count = source.idx, source.idx_count
+        elif role == "dense":
+            self.idx = self.idx_count = None
         else:
             self.idx = torch.empty((n_rows, 512), dtype=torch.int32, device=dev)
             self.idx_count = torch.empty((n_rows,), dtype=torch.int32, device=dev)
@@ -170,7 +179,7 @@ class Workload:
             if role != "reuse":
                 source = layer
             self.layers.append(layer)
-        if cfg.roles[0] not in ("full", "reindex", "prefill"):
+        if cfg.roles[0] not in ("full", "reindex", "prefill", "dense"):
             raise ValueError("the first layer of a step must select its own positions")
         self.graphs = None
         # ---- intermediates
@@ -188,7 +197,8 @@ class Workload:
             # the selection's 512-block pool (an intermediate of the prefill step)
             self.pool = torch.empty((self.n_rows, 512), dtype=torch.int32, device=dev)
             self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
-        ws = csa2_attn_workspace_size(self.n_rows, cfg.heads)
+        ws = (csa2_dense_attn_workspace_size(self.n_rows, cfg.heads, self.max_vis) if mode == "dense"
+              else csa2_attn_workspace_size(self.n_rows, cfg.heads))
         self.workspace = torch.empty(max(ws, 256) // 4, dtype=torch.float32, device=dev) if ws else None
         if mode == "reindex":
             pools = np.stack([synth.given_pool(cfg.seed, r, int(L[r]) // 8, 2048) for r in range(self.n_rows)])
@@ -286,9 +296,15 @@ class Workload:
             m(marks, "swa_merge", 1)
         else:
             m(marks, "attention", 0)
-            csa2_sparse_swa_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, layer.swa_codes,
-                                 layer.swa_scales, layer.swa_first, layer.swa_count, self.sigma, layer.out,
-                                 workspace=self.workspace, stream=stream)
+            if layer.role == "dense":
+                csa2_dense_swa_attn(kv, self.rows, layer.q, self.sigma, layer.out, swa_codes=layer.swa_codes,
+                                    swa_scales=layer.swa_scales, swa_first=layer.swa_first,
+                                    swa_count=layer.swa_count, sink=layer.sink, lse=layer.lse,
+                                    workspace=self.workspace, stream=stream)
+            else:
+                csa2_sparse_swa_attn(kv, self.rows, layer.q, layer.idx, layer.idx_count, layer.swa_codes,
+                                     layer.swa_scales, layer.swa_first, layer.swa_count, self.sigma, layer.out,
+                                     sink=layer.sink, workspace=self.workspace, stream=stream)
             m(marks, "attention", 1)
 
     def step(self, copy: int = 0, stream=None, marks=None):
@@ -340,7 +356,7 @@ class Workload:
         prefill = cfg.mode == "prefill"
         roles = [layer.role for layer in self.layers]
         n_layers = len(roles)
-        n_index = sum(r != "reuse" for r in roles)
+        n_index = sum(r not in ("reuse", "dense") for r in roles)
         d = {}
         n_full = sum(r in ("full", "prefill") for r in roles)
         if n_full:
@@ -350,8 +366,11 @@ class Workload:
         if n_reindex:
             pool_pos = int(np.minimum(self.n_vis_host, 16384).sum()) if cfg.mode != "reindex" else rows * 16384
             d["index_keys_pool"] = n_reindex * pool_pos * 68
-        sel = int(np.minimum(self.n_vis_host, 512).sum())
-        d["gathered_main"] = n_layers * sel * 288
+        if cfg.mode == "dense":
+            d["dense_main"] = n_layers * int(self.n_vis_host.sum()) * 288
+        else:
+            sel = int(np.minimum(self.n_vis_host, 512).sum())
+            d["gathered_main"] = n_layers * sel * 288
         d["swa"] = n_layers * (rows + cfg.window - 1 if prefill else rows * cfg.window) * 544
         d["q"] = n_layers * rows * H * 512 * 2 + n_index * rows * (cfg.idx_heads * 128 * 2 + cfg.idx_heads * 4)
         d["out"] = n_layers * rows * H * 512 * 4

@@ -47,6 +47,8 @@ class Config:
             return ("reindex",)
         if self.mode == "prefill":
             return ("prefill",)
+        if self.mode == "dense":
+            return ("dense",)
         return ("full",) + ("reindex",) * self.reindex_layers
 
     @property
@@ -96,6 +98,16 @@ def mixed_serving(**kw) -> Config:
                   "in a random page order, 1 Full + 4 Reindex layers, 64 heads", **kw)
 
 
+def hca_decode_1m(**kw) -> Config:
+    # the heavily compressed branch of the V4 hybrid attention ('DeepSeek-V4'
+    # page, section 2.3.2): every 128 tokens of a 1,048,576-token context
+    # compressed into one entry (8,192 per request), attended densely with the
+    # sliding window and a per-head sink (section 2.3.3)
+    return Config("hca_decode_16x1m", seed=6, n_req=16, heads=64, ctx=8192, mode="dense", tokens_per_entry=128,
+                  extra={"sink": True}, description="16 requests x 1,048,576 tokens at 128 per entry (8,192 "
+                  "entries), 64 heads, dense attention over every entry + window 128 + sink", **kw)
+
+
 def decoder_stack_128k(**kw) -> Config:
     # the decoder's 20 CSA2 layers: one Full or Reindex layer, then three
     # Reuse layers, four times over ('KV cache diet' page, figure 2 and the
@@ -114,4 +126,5 @@ ALL = {
     "c3": chunked_prefill_256k,
     "c4": mixed_serving,
     "stack": decoder_stack_128k,
+    "hca": hca_decode_1m,
 }

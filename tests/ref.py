@@ -39,6 +39,8 @@ class RowRef:
         self.q_idx = f32(synth.normal_bf16(s, synth.T_QIDX + off, (Hi, 128), offset=row * Hi * 128))
         self.w = synth.uniform(s, synth.T_W + off, np.arange(row * Hi, row * Hi + Hi, dtype=np.uint64))
         self.qc, self.qs = oracle.quant_query(self.q_idx)
+        # per-head sink logits of the layer (workloads that use one)
+        self.sink = (f32(synth.normal_bf16(s, synth.T_SINK + off, (H,))) if cfg.extra.get("sink") else None)
 
     # ---------------------------------------------------------------- inputs
     def index_keys(self, pos):
@@ -87,6 +89,12 @@ class RowRef:
 
     def select_prefill(self, scores):
         return oracle.topk(scores, 512)
+
+    def attend_dense(self):
+        """Every visible entry of the row (the heavily compressed branch),
+        the window and the layer's sink."""
+        _, _, o = self.attend(np.arange(self.n_vis, dtype=np.int64), sink=self.sink)
+        return o
 
     def attend(self, idx, sink=None):
         kc, ks = oracle.pack_main(self.latent(idx))

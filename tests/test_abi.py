@@ -180,6 +180,33 @@ def test_attn_rejects():
              None) == 5
 
 
+def test_dense_attn_rejects():
+    """Host checks of the dense (heavily compressed) attention; every call
+    here is invalid, so nothing is launched."""
+    L = lib.lib()
+    kv = _kv()
+    B = ctypes.byref
+    F = ctypes.c_float(0.04)
+    f = L.csa2_dense_swa_attn
+    ok = dict(kv=B(kv), rows=B(_rows()), q=256, qd=0, H=64, swc=None, sws=None, slots=0, first=None, cnt=None,
+              sink=None, scale=F, out=256, lse=None, ws=None, wsb=0)
+
+    def call(**over):
+        a = dict(ok, **over)
+        return f(a["kv"], a["rows"], a["q"], a["qd"], a["H"], a["swc"], a["sws"], a["slots"], a["first"],
+                 a["cnt"], a["sink"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert call(H=40) == 5                                   # heads
+    assert call(out=None) == 1
+    assert call(out=260) == 4
+    assert call(rows=B(_rows(max_vis=(1 << 22) + 1))) == 3   # above CSA2_MAX_DENSE
+    assert call(swc=256, sws=256, slots=10, first=256, cnt=None) == 1   # window without counts
+    assert call(kv=B(_kv(main_codes=None))) == 1
+    assert L.csa2_dense_attn_workspace_size(2, 64, 8192) > 0
+    assert L.csa2_dense_attn_workspace_size(2, 64, (1 << 22) + 1) == 0
+    assert L.csa2_dense_attn_workspace_size(4096, 64, 8192) == 0   # enough rows: no split pass
+
+
 def test_stream_xor_rejects():
     """Host checks of the streaming-read reference (no launch on failure; a
     zero-byte call does nothing and succeeds)."""

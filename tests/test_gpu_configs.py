@@ -337,3 +337,23 @@ def test_graph_replay_matches_eager():
     _, _, o = RowRef(cfg, 2, 7).attend(RowRef(cfg, 2, 4).select_pool(
         wl.pool[2, :int(wl.pool_count[2])].cpu().numpy())[2])
     assert tol_ok(wl.layers[7].out[2].cpu().numpy(), o)
+
+
+def test_hca_decode_rows():
+    """The heavily compressed branch ('DeepSeek-V4' page, section 2.3.2): 16
+    requests of 1,048,576 tokens at 128 tokens per entry, every one of the
+    8,192 entries attended densely with the window and a per-head sink
+    (section 2.3.3).  Every row finite; three rows against the oracle."""
+    cfg = configs.hca_decode_1m()
+    wl = Workload(cfg)
+    wl.step()
+    torch.cuda.synchronize()
+    L = wl.layers[0]
+    out = L.out.cpu().numpy()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(L.lse.cpu().numpy()))
+    rows = [0, 6, 15]
+    refs = oracle.map_rows(lambda r: RowRef(cfg, r, 0).attend_dense(), rows)
+    for row, o in zip(rows, refs):
+        assert tol_ok(out[row], o), (row, float(np.abs(out[row] - o).max()))
+    del wl
+    torch.cuda.empty_cache()

@@ -670,6 +670,68 @@ def test_attention_edge_scales(case, H):
                sink=case == "window_spread", win_scale=win_scale)
 
 
+@pytest.mark.parametrize("H", [16, 64])
+def test_dense_attention(H):
+    """Every visible entry of each row attended (the heavily compressed
+    branch, 'DeepSeek-V4' page, section 2.3.2), with window and sink, paged
+    cache (64-entry pages in random order): rows of 8,192, 5,000, 65 and 1
+    entries and an empty one; the one-workgroup form and the split form
+    (workspace) give the same bits, a row alone gives the same bits as in the
+    batch, and every row is within the tolerance of the oracle."""
+    rng = np.random.default_rng(4242 + H)
+    lens = np.array([8192, 5000, 65, 1, 0], np.int64)
+    P = 64
+    pages = (lens + P - 1) // P
+    perm = rng.permutation(int(pages.sum()))
+    table = np.zeros((len(lens), int(pages.max())), np.int32)
+    k = 0
+    for r in range(len(lens)):
+        table[r, :pages[r]] = perm[k:k + pages[r]]
+        k += pages[r]
+    n_slots = int(pages.sum()) * P
+    lat = bf16(rng.standard_normal((n_slots, 512)).astype(np.float32)).float().numpy()
+    mc, ms = oracle.pack_main(lat)
+    K = oracle.dequant_main(mc, ms)
+    n_rows = len(lens)
+    swa = bf16(rng.standard_normal((n_rows * 128, 512)).astype(np.float32)).float().numpy()
+    wc, wsc = oracle.pack_swa(swa)
+    W = oracle.dequant_swa(wc, wsc)
+    q = bf16(rng.standard_normal((n_rows, H, 512)).astype(np.float32) * 0.5)
+    sk = (rng.standard_normal(H) * 2).astype(np.float32)
+    swa_counts = np.array([128, 100, 0, 128, 5], np.int32)
+    kv = lib.make_kv(main_codes=T(mc), main_scales=T(ms), n_slots=n_slots, page_entries=P, page_table=T(table))
+
+    def call(rows_sel, use_ws):
+        n = len(rows_sel)
+        rows = lib.make_rows(T(np.asarray(rows_sel, np.int32)), T(lens[rows_sel].astype(np.int32)),
+                             int(lens[rows_sel].max()))
+        wsb = lib.csa2_dense_attn_workspace_size(n, H, int(lens[rows_sel].max())) if use_ws else 0
+        ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV) if wsb else None
+        out = torch.empty((n, H, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((n, H), dtype=torch.float32, device=DEV)
+        lib.csa2_dense_swa_attn(kv, rows, q[rows_sel].contiguous().to(DEV), SIG, out, swa_codes=T(wc),
+                                swa_scales=T(wsc), swa_first=T(np.asarray(rows_sel, np.int64) * 128),
+                                swa_count=T(swa_counts[rows_sel]), sink=T(sk), lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu(), lse.cpu()
+
+    all_rows = list(range(n_rows))
+    o_ws, l_ws = call(all_rows, True)
+    assert lib.csa2_dense_attn_workspace_size(n_rows, H, 8192) > 0
+    o_1, l_1 = call(all_rows, False)
+    assert torch.equal(o_ws, o_1) and torch.equal(l_ws, l_1)
+    o_a, l_a = call([1], True)
+    assert torch.equal(o_a[0], o_ws[1]) and torch.equal(l_a[0], l_ws[1])
+    qn = q.float().numpy()
+    for r in all_rows:
+        pos = np.arange(lens[r])
+        slots = table[r, pos // P].astype(np.int64) * P + pos % P
+        fo, fl = oracle.attention(qn[r], K[slots] if lens[r] else None, W[r * 128:r * 128 + swa_counts[r]],
+                                  sink=sk, sigma=SIG)
+        assert tolerance_ok(o_ws[r].numpy(), fo), (r, np.abs(o_ws[r].numpy() - fo).max())
+        assert np.allclose(l_ws[r].numpy(), fl, rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("H", [16, 48, 64, 128])
 def test_attention_counts(H):
     _attn_case(4, H, [512, 1, 65, 0], [128, 128, 1, 100])
