@@ -124,6 +124,41 @@ csa2_status csa2_pack_kv(csa2_kind kind, const void* src, csa2_dtype src_dtype, 
                          int64_t src_row_stride, uint8_t* codes, uint8_t* scales,
                          const int64_t* slots, void* stream);
 
+/* ---------------------------------------------------------------- write path
+ * Compressed cache entries built from projected token streams, normalised,
+ * rotated and packed in one pass ('DeepSeek-V4' page, section 2.3.1,
+ * compressed key-value entries; 2.3.2 for the non-overlapping form; 2.3.3
+ * RMSNorm and partial RoPE; 'KV cache diet' page: quantisation after RoPE).
+ * The streams are the layer's projections of its hidden states (C = H W^KV,
+ * Z = H W^Z), computed by the caller: fp32, token rows of `row_stride`
+ * elements, `width` channels (512 for MAIN, 128 for INDEX).
+ *   Overlapping (cb, zb, bb given): entry i, per channel, is the softmax over
+ *   the 2m logits za[m i + k] + ba[k] and zb[m (i-1) + k] + bb[k] (k < m)
+ *   weighting ca[m i + k] and cb[m (i-1) + k]; entry 0 has no b part.
+ *   Non-overlapping (cb, zb, bb NULL): the softmax over za[m i + k] + ba[k]
+ *   weighting ca[m i + k].
+ * Then, if norm_weight [width] is given, y = x / sqrt(mean(x^2) + eps) *
+ * norm_weight; if rope, channel pairs (width - 64 + 2j, width - 63 + 2j)
+ * rotate by (pos0 + m i) * 10000^(-2j/64).  Entry i (i < n_tok / m) is
+ * written packed (kind MAIN_FP4 or INDEX_MXFP4, the csa2_pack_kv rules) to
+ * slots[i] (NULL: slot i); `values` [n_tok/m][width] (may be NULL) receives
+ * the fp32 values that were packed.  1 <= m <= 1,024. */
+typedef struct csa2_compress_streams {
+    const float* ca;
+    const float* za;
+    const float* cb;          /* NULL: non-overlapping compression */
+    const float* zb;
+    const float* ba;          /* [m][width] */
+    const float* bb;          /* [m][width], overlapping only */
+    int64_t n_tok;
+    int64_t row_stride;       /* elements between token rows (>= width, multiple of 4) */
+    int32_t m;
+} csa2_compress_streams;
+csa2_status csa2_compress_pack(csa2_kind kind, const csa2_compress_streams* streams,
+                               const float* norm_weight, float eps, int32_t rope, int64_t pos0,
+                               float* values, uint8_t* codes, uint8_t* scales, const int64_t* slots,
+                               void* stream);
+
 /* ---------------------------------------------------------------- indexer
  * Lightning-indexer scores ('DeepSeek-V4' page, section 2.3.1):
  *   q_idx [n_rows][n_idx_heads][128] (bf16 or fp32) is quantised to MXFP4 per

@@ -38,6 +38,12 @@ class KV(ctypes.Structure):
     ]
 
 
+class CompressStreams(ctypes.Structure):
+    _fields_ = [("ca", ctypes.c_void_p), ("za", ctypes.c_void_p), ("cb", ctypes.c_void_p), ("zb", ctypes.c_void_p),
+                ("ba", ctypes.c_void_p), ("bb", ctypes.c_void_p), ("n_tok", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64), ("m", ctypes.c_int32)]
+
+
 class Rows(ctypes.Structure):
     _fields_ = [("req", ctypes.c_void_p), ("n_vis", ctypes.c_void_p),
                 ("n_rows", ctypes.c_int32), ("max_vis", ctypes.c_int32)]
@@ -45,7 +51,8 @@ class Rows(ctypes.Structure):
 
 _lib = None
 EXPORTS = (
-    "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_index_score",
+    "csa2_abi_version", "csa2_status_str", "csa2_last_error", "csa2_pack_kv", "csa2_compress_pack",
+    "csa2_index_score",
     "csa2_index_score_shared",
     "csa2_select_topk_workspace", "csa2_select_topk", "csa2_select_full", "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_swa_merge",
     "csa2_sparse_swa_attn", "csa2_sparse_swa_attn_noalloc", "csa2_dense_attn_workspace_size",
@@ -67,6 +74,7 @@ def lib():
     L.csa2_status_str.argtypes = [ctypes.c_int]
     L.csa2_last_error.restype = ctypes.c_char_p
     L.csa2_pack_kv.argtypes = [ctypes.c_int, P, ctypes.c_int, i64, i64, P, P, P, P]
+    L.csa2_compress_pack.argtypes = [ctypes.c_int, ctypes.POINTER(CompressStreams), P, f32, i32, i64, P, P, P, P, P]
     L.csa2_index_score.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), P, ctypes.c_int, i32, P,
                                    P, i64, P, P, i64, P, i64, P]
     L.csa2_index_score_shared.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Rows), i32, P, ctypes.c_int, i32, P,
@@ -163,6 +171,19 @@ def csa2_pack_kv(kind, src, codes, scales, slots=None, stream=None):
     n = int(src.shape[0])
     _check("csa2_pack_kv", lib().csa2_pack_kv(kind, _ptr(src), _dtype(src), n, _rstride(src),
                                              _ptr(codes), _ptr(scales), _ptr(slots), _stream(stream)))
+
+
+def csa2_compress_pack(kind, m, ca, za, ba, codes, scales, cb=None, zb=None, bb=None, norm_weight=None,
+                       eps=1e-6, rope=True, pos0=0, values=None, slots=None, stream=None):
+    """Compressed entries of the fp32 token streams (ca, za [n_tok, width];
+    overlapping if cb, zb, bb are given), RMSNorm (if norm_weight), RoPE on
+    the last 64 channels (if rope), packed to kind (MAIN_FP4 width 512 or
+    INDEX_MXFP4 width 128) at slots; `values` receives the packed fp32 values."""
+    st = CompressStreams(_ptr(ca), _ptr(za), _ptr(cb), _ptr(zb), _ptr(ba), _ptr(bb), int(ca.shape[0]),
+                         _rstride(ca), int(m))
+    _check("csa2_compress_pack", lib().csa2_compress_pack(
+        int(kind), ctypes.byref(st), _ptr(norm_weight), float(eps), int(bool(rope)), int(pos0), _ptr(values),
+        _ptr(codes), _ptr(scales), _ptr(slots), _stream(stream)))
 
 
 def csa2_index_score(kv, rows, q_idx, w, scores=None, block_max=None, pool_blocks=None, pool_count=None,

@@ -115,6 +115,47 @@ csa2_status csa2_pack_kv(csa2_kind kind, const void* src, csa2_dtype src_dtype, 
                                         slots, (hipStream_t)stream), "csa2_pack_kv launch");
 }
 
+csa2_status csa2_compress_pack(csa2_kind kind, const csa2_compress_streams* st, const float* norm_weight, float eps,
+                               int32_t rope, int64_t pos0, float* values, uint8_t* codes, uint8_t* scales,
+                               const int64_t* slots, void* stream) {
+    if (kind != CSA2_MAIN_FP4 && kind != CSA2_INDEX_MXFP4)
+        return fail(CSA2_ERR_UNSUPPORTED, "csa2_compress_pack packs MAIN or INDEX entries (kind %d)", (int)kind);
+    if (!st) return fail(CSA2_ERR_NULL, "streams descriptor is NULL");
+    if (st->m < 1 || st->m > 1024) return fail(CSA2_ERR_RANGE, "m must be in 1..1024 (got %d)", st->m);
+    if (st->n_tok < 0 || st->n_tok > ((int64_t)1 << 40)) return fail(CSA2_ERR_RANGE, "n_tok out of range");
+    const int width = kind == CSA2_MAIN_FP4 ? 512 : 128;
+    const int64_t n_ent = st->n_tok / st->m;
+    if (n_ent == 0) return CSA2_OK;
+    if (!st->ca || !st->za || !st->ba || !codes || !scales) return fail(CSA2_ERR_NULL, "ca / za / ba / codes / scales is NULL");
+    const bool overlap = st->cb || st->zb || st->bb;
+    if (overlap && (!st->cb || !st->zb || !st->bb)) return fail(CSA2_ERR_NULL, "cb, zb and bb go together");
+    if (st->row_stride < width || st->row_stride % 4) return fail(CSA2_ERR_SHAPE, "row_stride must be >= %d and a multiple of 4", width);
+    const void* ptrs[6] = {st->ca, st->za, st->cb, st->zb, st->ba, st->bb};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 16)) return fail(CSA2_ERR_ALIGN, "stream and bias pointers must be 16-byte aligned");
+    if ((norm_weight && !aligned(norm_weight, 16)) || (values && !aligned(values, 16)))
+        return fail(CSA2_ERR_ALIGN, "norm_weight and values must be 16-byte aligned");
+    if (!aligned(codes, 256) || !aligned(scales, 256)) return fail(CSA2_ERR_ALIGN, "code and scale planes must be 256-byte aligned");
+    if (!(eps >= 0.0f) || eps > 1.0f) return fail(CSA2_ERR_RANGE, "eps must be in [0, 1]");
+    if (pos0 < 0) return fail(CSA2_ERR_RANGE, "pos0 must be >= 0");
+    csa2::CompressArgs a;
+    a.m = st->m;
+    a.ca = st->ca;
+    a.za = st->za;
+    a.cb = overlap ? st->cb : nullptr;
+    a.zb = overlap ? st->zb : nullptr;
+    a.ba = st->ba;
+    a.bb = overlap ? st->bb : nullptr;
+    a.stride = st->row_stride;
+    a.n_ent = n_ent;
+    a.norm_weight = norm_weight;
+    a.eps = eps;
+    a.rope = rope != 0;
+    a.pos0 = pos0;
+    return hip_status(csa2::launch_compress_pack(a, width, values, codes, scales, slots, (hipStream_t)stream),
+                      "csa2_compress_pack launch");
+}
+
 csa2_status csa2_index_score(const csa2_kv* kv, const csa2_rows* rows, const void* q_idx, csa2_dtype q_dtype,
                              int32_t n_idx_heads, const float* w, const int32_t* pool_blocks, int64_t pool_stride,
                              const int32_t* pool_count, float* scores, int64_t scores_stride, float* block_max,

@@ -108,6 +108,26 @@ hipError_t launch_attn_dense(const KvView& kv, const AttnArgs& a, size_t ws_byte
 // array for the allocation-free attention; looked up once per device.
 hipError_t noalloc_scratch(void** out, size_t* bytes);
 
+// The write path: compressed entries from projected token streams, then
+// RMSNorm, RoPE and packing (MAIN width 512 or INDEX width 128).
+struct CompressArgs {
+    int m;                       // tokens per block
+    const float* ca;             // value / logit streams of the entry's own block, token rows of `stride`
+    const float* za;
+    const float* cb;             // of the block before (NULL: no overlap)
+    const float* zb;
+    const float* ba;             // positional biases [m][width]
+    const float* bb;
+    int64_t stride;
+    int64_t n_ent;               // entries = complete blocks
+    const float* norm_weight;    // [width] or NULL: no RMSNorm
+    float eps;
+    int rope;                    // rotate the last 64 channels
+    int64_t pos0;                // token position of entry 0
+};
+hipError_t launch_compress_pack(const CompressArgs& a, int width, float* values, uint8_t* codes, uint8_t* scales,
+                                const int64_t* slots, hipStream_t st);
+
 hipError_t launch_stream_xor(const void* buf, int64_t n_bytes, uint32_t* out, hipStream_t st);
 
 hipError_t launch_synth_normal(uint64_t seed, uint32_t tensor, int64_t first, int64_t n, bool bf16,

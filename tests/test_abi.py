@@ -207,6 +207,35 @@ def test_dense_attn_rejects():
     assert L.csa2_dense_attn_workspace_size(4096, 64, 8192) == 0   # enough rows: no split pass
 
 
+def test_compress_pack_rejects():
+    """Host checks of the write path (every call here is invalid: nothing is
+    launched), and an empty call (no complete block) that does nothing."""
+    L = lib.lib()
+    f = L.csa2_compress_pack
+    B = ctypes.byref
+
+    def st(**over):
+        d = dict(ca=256, za=256, cb=None, zb=None, ba=256, bb=None, n_tok=8, row_stride=512, m=4)
+        d.update(over)
+        return lib.CompressStreams(d["ca"], d["za"], d["cb"], d["zb"], d["ba"], d["bb"], d["n_tok"],
+                                   d["row_stride"], d["m"])
+
+    F = ctypes.c_float(1e-6)
+    assert f(2, B(st()), None, F, 1, 0, None, 256, 256, None, None) == 5          # SWA: not compressed
+    assert f(0, None, None, F, 1, 0, None, 256, 256, None, None) == 1
+    assert f(0, B(st(m=0)), None, F, 1, 0, None, 256, 256, None, None) == 3
+    assert f(0, B(st(m=2000)), None, F, 1, 0, None, 256, 256, None, None) == 3
+    assert f(0, B(st(ca=None)), None, F, 1, 0, None, 256, 256, None, None) == 1
+    assert f(0, B(st(cb=256)), None, F, 1, 0, None, 256, 256, None, None) == 1     # cb without zb, bb
+    assert f(0, B(st(row_stride=500)), None, F, 1, 0, None, 256, 256, None, None) == 2
+    assert f(1, B(st(row_stride=130)), None, F, 1, 0, None, 256, 256, None, None) == 2
+    assert f(0, B(st(za=264)), None, F, 1, 0, None, 256, 256, None, None) == 4
+    assert f(0, B(st()), None, F, 1, 0, None, 272, 256, None, None) == 4            # codes alignment
+    assert f(0, B(st()), None, ctypes.c_float(-1.0), 1, 0, None, 256, 256, None, None) == 3
+    assert f(0, B(st()), None, F, 1, -5, None, 256, 256, None, None) == 3
+    assert f(0, B(st(n_tok=3, ca=None)), None, F, 1, 0, None, None, None, None, None) == 0   # no complete block
+
+
 def test_stream_xor_rejects():
     """Host checks of the streaming-read reference (no launch on failure; a
     zero-byte call does nothing and succeeds)."""

@@ -89,6 +89,62 @@ def test_pack_slots_and_stride():
     assert np.array_equal(scales.cpu().numpy()[slots], rs)
 
 
+# ---------------------------------------------------------------- write path
+@pytest.mark.parametrize("kind,m,overlap,norm_rope", [
+    (lib.MAIN_FP4, 4, True, True),      # overlapping compression of 4 tokens ('DeepSeek-V4' page, 2.3.1)
+    (lib.MAIN_FP4, 2, True, True),      # 2 tokens per entry (the V4.1 encoder caches)
+    (lib.MAIN_FP4, 1, True, True),      # one token per entry, still overlapping with the one before
+    (lib.MAIN_FP4, 128, False, True),   # the heavily compressed branch, m' = 128, no overlap (2.3.2)
+    (lib.INDEX_MXFP4, 4, True, False),  # indexer keys: the same compression, no norm or rotation
+    (lib.INDEX_MXFP4, 2, False, False),
+])
+def test_compress_pack(kind, m, overlap, norm_rope):
+    """Compressed entries, RMSNorm and RoPE (2.3.3) and packing in one pass:
+    the fp32 values the kernel packed are within 1e-5 (relative and absolute)
+    of the fp64 oracle, and the packed bytes are the oracle packer's bytes for
+    those values.  37 entries plus an incomplete block (ignored), written to
+    scattered slots; positions near 2^20 so the rotation angles are large."""
+    from oracle import compress as oc
+    rng = np.random.default_rng(m * 10 + int(kind) + 3 * overlap)
+    width = 512 if kind == lib.MAIN_FP4 else 128
+    n_ent = 37
+    n_tok = n_ent * m + (m - 1)
+    stride = width + 4                    # token rows with a gap
+    def stream(scale):
+        x = np.zeros((n_tok, stride), np.float32)
+        x[:, :width] = bf16(rng.standard_normal((n_tok, width)) * scale).float().numpy()
+        return x
+    ca, za, cb, zb = stream(1.0), stream(2.0), stream(1.0), stream(2.0)
+    ba = bf16(rng.standard_normal((m, width)) * 0.5).float().numpy()
+    bb = bf16(rng.standard_normal((m, width)) * 0.5).float().numpy()
+    w = bf16(1 + 0.1 * rng.standard_normal(width)).float().numpy() if norm_rope else None
+    pos0 = (1 << 20) - 7
+    n_slots = 3 * n_ent
+    slots = rng.permutation(n_slots)[:n_ent].astype(np.int64)
+    codes, scales = planes(n_slots, kind)
+    vals = torch.full((n_ent, width), float("nan"), dtype=torch.float32, device=DEV)
+    Td = lambda a: T(np.ascontiguousarray(a))   # noqa: E731
+    ca_d, za_d = Td(ca), Td(za)
+    lib.csa2_compress_pack(kind, m, ca_d[:, :width], za_d[:, :width], Td(ba), codes, scales,
+                           cb=Td(cb)[:, :width] if overlap else None, zb=Td(zb)[:, :width] if overlap else None,
+                           bb=Td(bb) if overlap else None, norm_weight=None if w is None else Td(w), eps=1e-6,
+                           rope=norm_rope, pos0=pos0, values=vals, slots=T(slots))
+    torch.cuda.synchronize()
+    got = vals.cpu().numpy()
+    ref = oc.write_entries(m, ca[:, :width], za[:, :width], ba,
+                           cb[:, :width] if overlap else None, zb[:, :width] if overlap else None,
+                           bb if overlap else None, norm_weight=w, eps=1e-6, rope=norm_rope, pos0=pos0)
+    assert ref.shape == got.shape
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-5 + 1e-5 * np.abs(ref)), float(err.max())
+    pk = oracle.pack_main if kind == lib.MAIN_FP4 else oracle.pack_index
+    rc, rs = pk(got)
+    C, S = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(C[slots], rc) and np.array_equal(S[slots], rs)
+    untouched = np.setdiff1d(np.arange(n_slots), slots)
+    assert not C[untouched].any() and not S[untouched].any()
+
+
 # ---------------------------------------------------------------- generator
 def test_synth_matches_host():
     out = torch.empty(50000, dtype=torch.bfloat16, device=DEV)
