@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0          # MI355X dense fp16/bf16 matrix peak
 LLC_BYTES = 256 << 20             # MI355X Infinity Cache
 METRIC = "CSA2 decode steps/s (batch×heads) at 128K ctx; achieved HBM GB/s vs peak"
 DOMINANT = "index_score"          # the kernel the roofline object describes
@@ -43,7 +44,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c1", help="c0..c4 (the JSON line is for c1 by default)")
+    ap.add_argument("--workload", default="c1",
+                    help="c0..c4, stack (20 decoder layers), hca (dense 8,192-entry attention), write (the write "
+                         "path); the JSON line is for c1 by default")
     ap.add_argument("--copies", type=int, default=4, help="rotated KV-cache copies")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-rows", type=int, default=16, help="requests in the oracle sample")
@@ -52,6 +55,8 @@ def parse():
     ap.add_argument("--breakdown-steps", type=int, default=50,
                     help="steps of the separate per-kernel pass (at least 25): HIP events around every call of "
                          "every step, the stream kept busy; the roofline averages its indexer launches")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the second timed pass (two independent batches on two streams)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -175,12 +180,76 @@ def cpu_baseline(cfg, rows, thread_counts, min_seconds):
     return res
 
 
+def bench_write(args):
+    """The write path alone (csa2_compress_pack): the prefill of a
+    262,144-token context at 2 tokens per entry (131,072 entries, overlapping
+    compression), latent entries with RMSNorm and RoPE packed to the 288-B
+    format and indexer keys to the 68-B one.  HBM-bound: each launch reads its
+    four fp32 token streams once and writes the packed entries."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_amd as lib
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_tok, m = 262144, 2
+    n_ent = n_tok // m
+    res = {}
+    for kind, width, norm in ((lib.MAIN_FP4, 512, True), (lib.INDEX_MXFP4, 128, False)):
+        st = [torch.empty((n_tok, width), dtype=torch.float32, device=dev) for _ in range(4)]
+        for k, t in enumerate(st):
+            lib.csa2_synth_normal(7, 40 + k, 0, t)
+        b = [torch.empty((m, width), dtype=torch.float32, device=dev) for _ in range(2)]
+        for k, t in enumerate(b):
+            lib.csa2_synth_normal(7, 50 + k, 0, t)
+        w = torch.ones(width, dtype=torch.float32, device=dev) if norm else None
+        codes = torch.empty((n_ent, 256 if width == 512 else 64), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n_ent, 32 if width == 512 else 4), dtype=torch.uint8, device=dev)
+
+        def call():
+            lib.csa2_compress_pack(kind, m, st[0], st[1], b[0], codes, scales, cb=st[2], zb=st[3], bb=b[1],
+                                   norm_weight=w, rope=norm, pos0=0)
+        for _ in range(args.warmup):
+            call()
+        n = max(25, args.steps)
+        evs = [(HipEvent(), HipEvent()) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, e in evs:
+            a.record()
+            call()
+            e.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_ms(e) for a, e in evs])) * 1e3
+        nbytes = 4 * n_tok * width * 4 + n_ent * (288 if width == 512 else 68) + 2 * m * width * 4
+        res["latent_512" if width == 512 else "index_128"] = {
+            "entries": n_ent, "avg_launch_us": round(us, 2), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        del st, b, codes, scales
+        torch.cuda.empty_cache()
+    lat = res["latent_512"]
+    out = {
+        "metric": "write path: compressed entries written/s (compression + RMSNorm + RoPE + FP4 packing)",
+        "value": round(n_ent / (lat["avg_launch_us"] * 1e-6), 1),
+        "unit": "entries/s",
+        "n_gpus": 1, "steps": max(25, args.steps), "warmup": args.warmup, "higher_is_better": True,
+        "dtype": "fp32 in, FP4/MXFP4 out", "data": "synthetic (seeded N(0,1) streams)",
+        "config": {"workload": "write_prefill_262144_tokens_m2", "tokens": n_tok, "tokens_per_entry": m},
+        "kernels": res,
+        "roofline": {"kernel": "compress_pack_kernel<512>", "bound": "hbm", "achieved": lat["gbs"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": lat["frac_of_hbm_peak"], "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); requests are independent, so "
               f"N GPUs would each run this same step on their own requests.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "write":
+        bench_write(args)
+        return
     import numpy as np
     import torch
 
@@ -208,6 +277,40 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
+    # ---- second timed pass: two independent batches of the same workload in
+    # flight on two streams of equal (default) priority, steps alternating
+    # between them; each stream runs its batch's steps in order.  The
+    # latency-bound selection and attention of one batch then run beside the
+    # bandwidth-bound indexer scan of the other.  Reported beside the value,
+    # which is the single-batch figure above.
+    overlap = None
+    if not args.no_overlap:
+        mbs = [wl, wl.micro_batch()]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        main = torch.cuda.current_stream()
+        for s_ in streams:
+            s_.wait_stream(main)
+        for i in range(2 * args.warmup):
+            with torch.cuda.stream(streams[i % 2]):
+                mbs[i % 2].step(copy=i)
+        torch.cuda.synchronize()
+        n2 = 2 * args.steps
+        t0 = time.perf_counter()
+        for i in range(n2):
+            with torch.cuda.stream(streams[i % 2]):
+                mbs[i % 2].step(copy=args.warmup + i)
+        torch.cuda.synchronize()
+        dt2 = time.perf_counter() - t0
+        overlap = {
+            "what": "two independent batches of this workload in flight on two streams (default priority), "
+                    "their steps alternating; each batch's steps in order on its own stream",
+            "steps": n2,
+            "us_per_step": round(dt2 * 1e6 / n2, 2),
+            "value": round(n2 / dt2 * B * H, 1),
+            "step_frac_of_hbm_peak": round(algo["total"] / (dt2 / n2) / 1e9 / PEAK_HBM_GBS, 4),
+        }
+        del mbs
+
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -222,6 +325,9 @@ def main():
     names = ["index_score", "select", "attention"]
     if cfg.mode == "reindex":
         names = ["index_score", "select_positions", "attention"]
+    elif cfg.mode == "dense":
+        names = ["attention"]
+    dominant = "attention" if cfg.mode == "dense" else DOMINANT
     nb = max(25, args.breakdown_steps)
     marks_all = [{n: (HipEvent(), HipEvent()) for n in names} for _ in range(nb)]
     torch.cuda.synchronize()
@@ -232,7 +338,7 @@ def main():
     breakdown_step_us = (time.perf_counter() - tb0) * 1e6 / nb
     per = {n: np.array([m[n][0].elapsed_ms(m[n][1]) * 1e3 for m in marks_all]) for n in names}
     kernels_us = {n: round(float(np.mean(v)), 2) for n, v in per.items()}
-    k2_ms = float(np.mean(per[DOMINANT])) * 1e-3
+    k2_ms = float(np.mean(per[dominant])) * 1e-3
 
     # ---- streaming-read ceiling (separate, untimed): the plain non-temporal
     # read of the indexer's key-code plane, the same rotated buffers, one
@@ -262,6 +368,37 @@ def main():
     k2_gbs = k2_bytes / (k2_ms * 1e-3) / 1e9
     step_gbs = algo["total"] / (ms * 1e-3) / 1e9
     traffic = measured_traffic(cfg.name)
+    if cfg.mode == "dense":
+        # every entry of every row against every head: two products of 2 x 512
+        # flops per (head, entry) pair; the matrix cores' fp16 dense peak
+        entries = int(wl.n_vis_host.sum()) + B * cfg.window
+        flops = 4 * H * 512 * entries
+        roofline = {
+            "kernel": "attention (dense: attn_kernel + attn_merge_kernel)",
+            "bound": "mfma",
+            "achieved": round(flops / k2_ms / 1e9, 2),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / k2_ms / 1e9 / PEAK_F16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(k2_ms * 1e3, 2),
+            "launches_timed": nb,
+        }
+    else:
+        roofline = {
+            "kernel": DOMINANT,
+            "bound": "hbm",
+            "achieved": round(k2_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(k2_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": k2_bytes,
+            "avg_launch_us": round(k2_ms * 1e3, 2),
+            "launches_timed": nb,
+            "frac_of_read_ceiling": round(k2_gbs / rd_gbs, 4) if rd_hbm else None,
+        }
 
     out = {
         "metric": METRIC,
@@ -283,22 +420,11 @@ def main():
         "step_algorithmic_bytes": algo["total"],
         "step_gbs": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / PEAK_HBM_GBS, 4),
+        "two_batches_in_flight": overlap,
         "kernels_us": kernels_us,
         "kernels_us_note": f"means over the {nb}-step per-kernel pass (events around each call, stream kept busy; "
                            f"that pass ran at {breakdown_step_us:.1f} us per step)",
-        "roofline": {
-            "kernel": DOMINANT,
-            "bound": "hbm",
-            "achieved": round(k2_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(k2_gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": k2_bytes,
-            "avg_launch_us": round(k2_ms * 1e3, 2),
-            "launches_timed": nb,
-            "frac_of_read_ceiling": round(k2_gbs / rd_gbs, 4) if rd_hbm else None,
-        },
+        "roofline": roofline,
         "read_ceiling": None if not rd_hbm else {
             "kernel": "stream_xor_kernel",
             "what": "plain streaming read (16-B non-temporal loads) of the indexer's key-code plane, same rotated buffers",

@@ -206,6 +206,34 @@ class Workload:
             self.pool_count.fill_(2048)
         torch.cuda.synchronize()
 
+    def micro_batch(self) -> "Workload":
+        """Another batch over the same cache and query-side inputs, with its
+        own per-step buffers (scores, block maxima, pool, positions, outputs,
+        workspace), so that its step can run on another stream while this
+        one's runs."""
+        import copy
+        mb = copy.copy(self)
+        for name in ("scores", "block_max", "pool", "pool_count", "pool_scores", "workspace"):
+            t = getattr(self, name, None)
+            if t is not None:
+                setattr(mb, name, t.clone())
+        mb.layers = []
+        new_sel = {}
+        for layer in self.layers:
+            nl = copy.copy(layer)
+            if layer.role == "reuse":
+                src = new_sel[id(layer.idx)]
+                nl.idx, nl.idx_count = src.idx, src.idx_count
+            elif layer.idx is not None:
+                nl.idx, nl.idx_count = torch.empty_like(layer.idx), torch.empty_like(layer.idx_count)
+                new_sel[id(layer.idx)] = nl
+            nl.o_partial, nl.lse, nl.out = (torch.empty_like(layer.o_partial), torch.empty_like(layer.lse),
+                                            torch.empty_like(layer.out))
+            mb.layers.append(nl)
+        mb.graphs = None
+        torch.cuda.synchronize()
+        return mb
+
     # --------------------------------------------------------------- setup
     def _fill_kv(self, main, idx):
         cfg = self.cfg
