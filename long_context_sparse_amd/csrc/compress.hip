@@ -72,7 +72,10 @@ __device__ __forceinline__ void accumulate(const float* v, const float* z, const
     }
 }
 
-template <int WIDTH>
+// Blocks of M <= 4 tokens (M > 0): every row of the entry (M of stream a, M
+// of stream b) is requested before any is used, then a two-pass softmax in
+// registers.  M == 0: any block size, rows walked with an online softmax.
+template <int WIDTH, int M>
 __global__ __launch_bounds__(64 * CP_WAVES) void compress_pack_kernel(CompressArgs a, float* __restrict__ values,
                                                                      uint8_t* __restrict__ codes,
                                                                      uint8_t* __restrict__ scales,
@@ -82,15 +85,51 @@ __global__ __launch_bounds__(64 * CP_WAVES) void compress_pack_kernel(CompressAr
     if (i >= a.n_ent) return;                           // whole waves leave together
     const int l = threadIdx.x & 63;
     const int c0 = CH * l;
-    float mx[CH], s[CH], acc[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) { mx[j] = -INFINITY; s[j] = 0.0f; acc[j] = 0.0f; }
-    // the entry's own block (stream a), then the block before it (stream b)
-    accumulate<CH>(a.ca, a.za, a.ba, i * a.m, a.m, a.stride, c0, mx, s, acc);
-    if (a.cb && i > 0) accumulate<CH>(a.cb, a.zb, a.bb, (i - 1) * a.m, a.m, a.stride, c0, mx, s, acc);
     float y[CH];
+    if constexpr (M > 0) {
+        const bool has_b = a.cb && i > 0;
+        // rows 0..M-1: stream a of block i; rows M..2M-1: stream b of block i-1
+        // (re-reading block i's a rows where there is no b part; masked below)
+        float vv[2 * M][CH], zz[2 * M][CH], bs[2 * M][CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) y[j] = acc[j] / s[j];
+        for (int k = 0; k < M; ++k) {
+            const int64_t ta = (i * M + k) * a.stride + c0;
+            load_ch<CH>(a.ca + ta, vv[k]);
+            load_ch<CH>(a.za + ta, zz[k]);
+            load_ch<CH>(a.ba + k * WIDTH + c0, bs[k]);
+            const int64_t tb = has_b ? ((i - 1) * M + k) * a.stride + c0 : ta;
+            load_ch<CH>(has_b ? a.cb + tb : a.ca + tb, vv[M + k]);
+            load_ch<CH>(has_b ? a.zb + tb : a.za + tb, zz[M + k]);
+            load_ch<CH>((has_b ? a.bb : a.ba) + k * WIDTH + c0, bs[M + k]);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            float lg[2 * M];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 2 * M; ++r) {
+                lg[r] = (r < M || has_b) ? zz[r][j] + bs[r][j] : -INFINITY;
+                mx = fmaxf(mx, lg[r]);
+            }
+            float sum = 0.0f, acc = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 2 * M; ++r) {
+                const float p = (r < M || has_b) ? expf(lg[r] - mx) : 0.0f;
+                sum += p;
+                acc = fmaf(p, vv[r][j], acc);
+            }
+            y[j] = acc / sum;
+        }
+    } else {
+        float mx[CH], s[CH], acc[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) { mx[j] = -INFINITY; s[j] = 0.0f; acc[j] = 0.0f; }
+        // the entry's own block (stream a), then the block before it (stream b)
+        accumulate<CH>(a.ca, a.za, a.ba, i * a.m, a.m, a.stride, c0, mx, s, acc);
+        if (a.cb && i > 0) accumulate<CH>(a.cb, a.zb, a.bb, (i - 1) * a.m, a.m, a.stride, c0, mx, s, acc);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) y[j] = acc[j] / s[j];
+    }
     if (a.norm_weight) {
         float ss = 0.0f;
 #pragma unroll
@@ -155,8 +194,21 @@ __global__ __launch_bounds__(64 * CP_WAVES) void compress_pack_kernel(CompressAr
 hipError_t launch_compress_pack(const CompressArgs& a, int width, float* values, uint8_t* codes, uint8_t* scales,
                                 const int64_t* slots, hipStream_t st) {
     const dim3 grid((unsigned)((a.n_ent + CP_WAVES - 1) / CP_WAVES)), block(64 * CP_WAVES);
-    if (width == 512) hipLaunchKernelGGL(compress_pack_kernel<512>, grid, block, 0, st, a, values, codes, scales, slots);
-    else hipLaunchKernelGGL(compress_pack_kernel<128>, grid, block, 0, st, a, values, codes, scales, slots);
+#define CP_LAUNCH(W, M) hipLaunchKernelGGL((compress_pack_kernel<W, M>), grid, block, 0, st, a, values, codes, scales, slots)
+    const int m = a.m;   // the unrolled forms serve the overlapping compression of 1, 2 or 4 tokens
+    const int mk = (a.cb && (m == 1 || m == 2 || m == 4)) ? m : 0;
+    if (width == 512) {
+        if (mk == 1) CP_LAUNCH(512, 1);
+        else if (mk == 2) CP_LAUNCH(512, 2);
+        else if (mk == 4) CP_LAUNCH(512, 4);
+        else CP_LAUNCH(512, 0);
+    } else {
+        if (mk == 1) CP_LAUNCH(128, 1);
+        else if (mk == 2) CP_LAUNCH(128, 2);
+        else if (mk == 4) CP_LAUNCH(128, 4);
+        else CP_LAUNCH(128, 0);
+    }
+#undef CP_LAUNCH
     return hipGetLastError();
 }
 
