@@ -58,7 +58,16 @@ extern "C" {
 
 #define CSA2_ABI_VERSION 5
 
-typedef enum {
+/* The enums are int-sized in C; in C++ they are given int as their fixed
+ * underlying type, so that every int a C caller passes (an invalid one is
+ * rejected with a status) is a valid value of the parameter's type. */
+#ifdef __cplusplus
+#define CSA2_INT_ENUM : int
+#else
+#define CSA2_INT_ENUM
+#endif
+
+typedef enum CSA2_INT_ENUM {
     CSA2_OK = 0,
     CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
     CSA2_ERR_SHAPE = 2,       /* inconsistent sizes or strides */
@@ -69,8 +78,8 @@ typedef enum {
     CSA2_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
 } csa2_status;
 
-typedef enum { CSA2_BF16 = 0, CSA2_F32 = 1 } csa2_dtype;
-typedef enum { CSA2_MAIN_FP4 = 0, CSA2_INDEX_MXFP4 = 1, CSA2_SWA_FP8 = 2 } csa2_kind;
+typedef enum CSA2_INT_ENUM { CSA2_BF16 = 0, CSA2_F32 = 1 } csa2_dtype;
+typedef enum CSA2_INT_ENUM { CSA2_MAIN_FP4 = 0, CSA2_INDEX_MXFP4 = 1, CSA2_SWA_FP8 = 2 } csa2_kind;
 
 /* Fixed constants of the method: 'candidate_topk_blocks' 2,048,
  * 'candidate_block_size' 8, 'index_topk' 512, sliding window 128. */
@@ -111,7 +120,9 @@ typedef struct csa2_rows {
 } csa2_rows;
 
 int csa2_abi_version(void);
-const char* csa2_status_str(csa2_status s);
+/* Text of a status code; any int is accepted (codes outside csa2_status give
+ * "unknown status"). */
+const char* csa2_status_str(int status);
 const char* csa2_last_error(void);
 
 /* ---------------------------------------------------------------- packing

@@ -80,8 +80,8 @@ extern "C" {
 
 int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
 
-const char* csa2_status_str(csa2_status s) {
-    switch (s) {
+const char* csa2_status_str(int status) {
+    switch (status) {
         case CSA2_OK: return "ok";
         case CSA2_ERR_NULL: return "null pointer";
         case CSA2_ERR_SHAPE: return "inconsistent shape";
