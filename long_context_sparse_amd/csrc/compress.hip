@@ -26,6 +26,8 @@
 // codecs, so the packed bytes are those csa2_pack_kv gives for the same
 // values.  Memory-bound: 4m (or 2m') rows of `width` fp32 values read per
 // entry, 288 or 68 bytes written.
+#include <cmath>
+
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -143,16 +145,22 @@ __global__ __launch_bounds__(64 * CP_WAVES) void compress_pack_kernel(CompressAr
         for (int j = 0; j < CH; ++j) y[j] = y[j] * r * w[j];
     }
     if (a.rope && c0 >= WIDTH - 64) {
+        // angle = pos * 10000^(-2j/64) in turns, formed in fp64 (exact to far
+        // below an fp32 ulp of the reduced angle at any position < 2^40); its
+        // integer turns removed there, the remaining fraction of a turn is an
+        // fp32 angle in [-pi, pi] whose sine and cosine carry fp32 accuracy
+        constexpr double INV_2PI = 0.15915494309189533577;
         const double pos = (double)(a.pos0 + i * a.m);
 #pragma unroll
         for (int j = 0; j < CH; j += 2) {
             const int pair = (c0 + j - (WIDTH - 64)) >> 1;
-            const double ang = pos * pow(10000.0, -2.0 * pair / 64.0);
-            double sn, cs;
-            sincos(ang, &sn, &cs);
-            const double x0 = y[j], x1 = y[j + 1];
-            y[j] = (float)(x0 * cs - x1 * sn);
-            y[j + 1] = (float)(x0 * sn + x1 * cs);
+            const double turns = pos * (a.inv_freq[pair] * INV_2PI);
+            const float fr = (float)(turns - rint(turns));
+            float sn, cs;
+            sincosf(fr * 6.28318530717958647692f, &sn, &cs);
+            const float x0 = y[j], x1 = y[j + 1];
+            y[j] = fmaf(x0, cs, -x1 * sn);
+            y[j + 1] = fmaf(x0, sn, x1 * cs);
         }
     }
     if (values) {
@@ -191,8 +199,10 @@ __global__ __launch_bounds__(64 * CP_WAVES) void compress_pack_kernel(CompressAr
     }
 }
 
-hipError_t launch_compress_pack(const CompressArgs& a, int width, float* values, uint8_t* codes, uint8_t* scales,
+hipError_t launch_compress_pack(const CompressArgs& a_in, int width, float* values, uint8_t* codes, uint8_t* scales,
                                 const int64_t* slots, hipStream_t st) {
+    CompressArgs a = a_in;
+    for (int j = 0; j < 32; ++j) a.inv_freq[j] = std::pow(10000.0, -2.0 * j / 64.0);
     const dim3 grid((unsigned)((a.n_ent + CP_WAVES - 1) / CP_WAVES)), block(64 * CP_WAVES);
 #define CP_LAUNCH(W, M) hipLaunchKernelGGL((compress_pack_kernel<W, M>), grid, block, 0, st, a, values, codes, scales, slots)
     const int m = a.m;   // the unrolled forms serve the overlapping compression of 1, 2 or 4 tokens

@@ -124,6 +124,7 @@ struct CompressArgs {
     float eps;
     int rope;                    // rotate the last 64 channels
     int64_t pos0;                // token position of entry 0
+    double inv_freq[32];         // 10000^(-2j/64), j = 0 .. 31 (set by the launcher)
 };
 hipError_t launch_compress_pack(const CompressArgs& a, int width, float* values, uint8_t* codes, uint8_t* scales,
                                 const int64_t* slots, hipStream_t st);
