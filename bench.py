@@ -414,7 +414,8 @@ def main():
         "dtype": "mxfp4 (indexer MFMA, exact) + bf16/fp16 (attention MFMA), fp32 accumulate",
         "data": "synthetic (seeded counter-based N(0,1)/U(0,1), packed on the GPU)",
         "config": {"workload": cfg.name, "requests": B, "context_entries": int(wl.max_vis), "heads": H,
-                   "idx_heads": cfg.idx_heads, "pool_blocks": 2048, "topk": 512, "window": cfg.window,
+                   "idx_heads": cfg.idx_heads,
+                   "pool_blocks": {"dense": None, "prefill": 512, "csa": 512}.get(cfg.mode, 2048), "topk": 512, "window": cfg.window,
                    "kv_copies_rotated": args.copies},
         "steps_per_s": round(steps_s, 2),
         "step_algorithmic_bytes": algo["total"],

@@ -349,7 +349,7 @@ template <bool QBF16, bool POOL, int NM, bool MULTI, bool PTE>
 __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, IndexScoreArgs a) {
     constexpr bool GROUPED = NM == 0;
     constexpr int NMR = GROUPED ? 4 : NM;             // MFMAs per head group
-    __shared__ QShared<GROUPED ? IS_MAX_HEADS : 16> qs;
+    __shared__ __align__(16) QShared<GROUPED ? IS_MAX_HEADS : 16> qs;
     const int row = blockIdx.y;
     const int nv = min(a.n_vis[row], a.max_vis);
     const int64_t pool_cap = a.pool_stride < 2048 ? a.pool_stride : 2048;
@@ -393,22 +393,24 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     if (threadIdx.x == 0) qs.n_fix = 0;
     __syncthreads();
 
-    // MFMA k takes heads 4k .. 4k+3 on every row group: row n carries head 4k + (n & 3)
-    i32x8 Aq[NMR];
-    int sa[NMR];
-    float wl[4 * NMR];
-    auto group_operands = [&](int g) __attribute__((always_inline)) {
+    // Up to 16 heads: MFMA k takes heads 4k .. 4k+3 on every row group (row n
+    // carries head 4k + (n & 3)).  More than 16 heads: MFMA g takes the 16
+    // heads of group g, one per row (row n carries head 16g + n).
+    constexpr int NA = GROUPED ? IS_MAX_HEADS / 16 : NMR;
+    i32x8 Aq[NA];
+    int sa[NA];
+    float wl[GROUPED ? 1 : 4 * NMR];
 #pragma unroll
-        for (int k = 0; k < NMR; ++k) {
-            const int h = 16 * g + 4 * k + (n & 3);
-            const uint4 v = *(const uint4*)&qs.q.codes[h][16 * lg];
-            Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            sa[k] = qs.q.scales[h][lg];
+    for (int k = 0; k < NA; ++k) {
+        const int h = GROUPED ? 16 * k + n : 4 * k + (n & 3);
+        const uint4 v = *(const uint4*)&qs.q.codes[h][16 * lg];   // group rows above ng: unused
+        Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sa[k] = qs.q.scales[h][lg];
+        if (!GROUPED) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.q.w[16 * g + 4 * k + i];   // 0 above n_heads
+            for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.q.w[4 * k + i];   // 0 above n_heads
         }
-    };
-    if (!GROUPED) group_operands(0);
+    }
     int qspread, qmin, qmax;
     if (GROUPED) {
         qspread = 0; qmin = 1 << 20; qmax = -(1 << 20);
@@ -421,13 +423,81 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     float* srow = a.scores ? a.scores + (int64_t)row * a.scores_stride : nullptr;
     float* brow = (!POOL && a.block_max) ? a.block_max + (int64_t)row * a.block_max_stride : nullptr;
     const int nv8 = (nv + 7) & ~7;
-    const bool writer = lg == 0;                       // the 4 row groups hold identical results
+    const bool writer = lg == 0;                       // up to 16 heads: the 4 row groups hold identical results
 
     // One batch: tile t's MFMAs leave key 16t + n's score in every lane n of
     // each row group; lane l keeps the one of tile l / 16, so the batch's 64
     // scores leave in one coalesced 256-B store, and its 8 block maxima in one
     // 32-B store.
-    auto compute = [&](const KeyBatch& kb, int col_base, int lbase) {
+    //
+    // More than 16 heads: MFMA (g, t) leaves heads 16g + 4 lg + i (i = 0..3)
+    // of key 16t + n in lane (n, lg).  A 4 x 4 transpose of (tile, row group)
+    // over the lanes -- V_PERMLANE32_SWAP_B32 between tiles t and t + 2, then
+    // V_PERMLANE16_SWAP_B32 between tiles t and t + 1 -- hands lane (n, lg)
+    // all 16 heads of group g for key 16 lg + n, the key whose score it stores,
+    // so each lane folds its own key's heads in head order and no MFMA or fma
+    // is repeated.
+    auto compute_grouped = [&](const KeyBatch& kb, int col_base, int lbase) __attribute__((always_inline)) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NA; ++g) {
+            if (g >= ng) break;                        // uniform
+            f32x4 d[IS_TILES];
+#pragma unroll
+            for (int t = 0; t < IS_TILES; ++t) {
+                const i32x8 Bk = {(int)kb.code[t].x, (int)kb.code[t].y, (int)kb.code[t].z, (int)kb.code[t].w, 0, 0, 0, 0};
+                const int sb = (int)((kb.scl[t] >> (8 * lg)) & 0xFFu);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[g], Bk, z, 4, 4, 0, sa[g], 0, sb);
+            }
+            // pinned in wave-uniform control flow, as below
+#pragma unroll
+            for (int t = 0; t < IS_TILES; ++t) asm volatile("" : "+v"(d[t]));
+            float hv[4][4];                            // [source row group s][i]: head 16g + 4s + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d[0][i]), __float_as_uint(d[2][i]), false, false);
+                const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d[1][i]), __float_as_uint(d[3][i]), false, false);
+                const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+                const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+                hv[0][i] = __uint_as_float(q01[0]);
+                hv[1][i] = __uint_as_float(q01[1]);
+                hv[2][i] = __uint_as_float(q23[0]);
+                hv[3][i] = __uint_as_float(q23[1]);
+            }
+            const float4* wg = (const float4*)&qs.q.w[16 * g];   // 0 above n_heads
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const float4 w4 = wg[s4];
+                acc = fmaf(w4.x, relu_bits(hv[s4][0]), acc);
+                acc = fmaf(w4.y, relu_bits(hv[s4][1]), acc);
+                acc = fmaf(w4.z, relu_bits(hv[s4][2]), acc);
+                acc = fmaf(w4.w, relu_bits(hv[s4][3]), acc);
+            }
+        }
+        const uint32_t sd = lg == 0 ? kb.scl[0] : (lg == 1 ? kb.scl[1] : (lg == 2 ? kb.scl[2] : kb.scl[3]));
+        const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
+        const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
+        const bool ok = (kmax - kmin + qspread <= 9) && (qmin + kmin >= 136) && (qmax + kmax <= 356);
+        acc = (acc == 0.0f) ? 0.0f : acc;
+        const int col = col_base + l;                  // = col_base + 16 lg + n
+        const bool in_cols = col < ncols;
+        const int pos = POOL ? (in_cols ? 8 * qs.pool_l[lbase + ((col >> 3) & 31)] + (col & 7) : 0x7FFFFFFF) : col;
+        if (__builtin_expect(__any(!ok), 0)) {
+            int bad = (!ok && in_cols && pos < nv) ? 1 : 0;
+            bad |= __builtin_amdgcn_update_dpp(0, bad, 0x111, 0xF, 0xF, false);   // row_shr:1
+            bad |= __builtin_amdgcn_update_dpp(0, bad, 0x112, 0xF, 0xF, false);   // row_shr:2
+            bad |= __builtin_amdgcn_update_dpp(0, bad, 0x114, 0xF, 0xF, false);   // row_shr:4
+            if ((n & 7) == 7 && bad) qs.fix[atomicAdd(&qs.n_fix, 1)] = col & ~7;
+        }
+        return (in_cols && pos < nv) ? acc : -INFINITY;
+    };
+
+    auto compute = [&](const KeyBatch& kb, int col_base, int lbase) __attribute__((always_inline)) {
+        float val;
+        if constexpr (GROUPED) {
+            val = compute_grouped(kb, col_base, lbase);
+        } else {
         float vt[IS_TILES];
 #pragma unroll
         for (int t = 0; t < IS_TILES; ++t) {
@@ -438,9 +508,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             const uint32_t sd = kb.scl[t];
             const int sb = (int)((sd >> (8 * lg)) & 0xFFu);
             float acc = 0.0f;
-            // heads in groups of 16 (one group below 17 heads), folded in order
-            for (int g = 0; g < ng; ++g) {
-                if (GROUPED) group_operands(g);
+            {
                 f32x4 d[NMR];
 #pragma unroll
                 for (int k = 0; k < NMR; ++k) {
@@ -475,7 +543,8 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
             }
             vt[t] = (in_cols && pos < nv) ? acc : -INFINITY;
         }
-        const float val = lg == 0 ? vt[0] : (lg == 1 ? vt[1] : (lg == 2 ? vt[2] : vt[3]));
+        val = lg == 0 ? vt[0] : (lg == 1 ? vt[1] : (lg == 2 ? vt[2] : vt[3]));
+        }
         const int col = col_base + l;                  // = col_base + 16 lg + n
         const bool in_cols = col < ncols;
         if (srow) {

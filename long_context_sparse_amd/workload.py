@@ -185,7 +185,7 @@ class Workload:
         # ---- intermediates
         self.nv8 = (self.max_vis + 7) // 8 * 8
         mode = cfg.mode
-        self.full = mode in ("full", "prefill", "mixed")
+        self.full = mode in ("full", "prefill", "mixed", "csa")
         if self.full:
             self.scores = torch.empty((self.n_rows, self.nv8), dtype=torch.float32, device=dev)
             self.block_max = torch.empty((self.n_rows, self.nv8 // 8), dtype=torch.float32, device=dev)
@@ -193,8 +193,8 @@ class Workload:
             self.pool = torch.empty((self.n_rows, 2048), dtype=torch.int32, device=dev)
             self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
             self.pool_scores = torch.empty((self.n_rows, 16384), dtype=torch.float32, device=dev)
-        elif mode == "prefill":
-            # the selection's 512-block pool (an intermediate of the prefill step)
+        elif mode in ("prefill", "csa"):
+            # the selection's 512-block pool (an intermediate of the step)
             self.pool = torch.empty((self.n_rows, 512), dtype=torch.int32, device=dev)
             self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
         ws = (csa2_dense_attn_workspace_size(self.n_rows, cfg.heads, self.max_vis) if mode == "dense"
@@ -271,8 +271,9 @@ class Workload:
             csa2_index_score(kv, self.rows, layer.q_idx, layer.w, scores=self.scores, block_max=self.block_max,
                              stream=stream)
         m(marks, "index_score", 1)
-        if self.cfg.mode == "prefill":
-            # a row's top-512 positions lie in its 512 best blocks (a block ranked
+        if self.cfg.mode in ("prefill", "csa"):
+            # top-512 over every visible score (no 2,048-block pool): a row's
+            # top-512 positions lie in its 512 best blocks (a block ranked
             # above a top-512 position's block holds a distinct better position),
             # so the fused selection with a pool of 512 blocks returns exactly
             # the top-512 of all visible scores

@@ -1,4 +1,4 @@
-"""The five synthetic workloads (shapes, seeds, structure) -- data only.
+"""The synthetic workloads (shapes, seeds, structure) -- data only.
 
 Element numbering shared by every consumer (host generator, GPU generator,
 oracle): a cache entry has a *logical* id ``req_base[req] + pos`` (requests
@@ -21,7 +21,7 @@ class Config:
     n_req: int
     heads: int = 64
     idx_heads: int = 8
-    mode: str = "full"            # "full" | "reindex" | "prefill" | "mixed"
+    mode: str = "full"            # "full" | "reindex" | "prefill" | "mixed" | "dense" | "csa"
     ctx: int = 0                  # entries per request (uniform contexts)
     lengths: np.ndarray | None = None   # ragged contexts (entries)
     page_entries: int = 0         # 0 = contiguous
@@ -98,6 +98,17 @@ def mixed_serving(**kw) -> Config:
                   "in a random page order, 1 Full + 4 Reindex layers, 64 heads", **kw)
 
 
+def v4_csa_decode_1m(**kw) -> Config:
+    # the compressed sparse attention of the V4 hybrid ('DeepSeek-V4' page,
+    # section 2.3.1 and the model setup of section 4.2.1: 4 tokens per entry,
+    # 64 indexer heads of 128 channels, top-512 over every visible compressed
+    # entry, no block pool), with the window and a per-head sink (2.3.3)
+    return Config("v4_csa_decode_16x1m", seed=8, n_req=16, heads=64, idx_heads=64, ctx=262144, mode="csa",
+                  tokens_per_entry=4, extra={"sink": True},
+                  description="16 requests x 1,048,576 tokens at 4 per entry (262,144 entries), 64 indexer heads, "
+                  "top-512 over all entries, 64 heads, window 128 + sink", **kw)
+
+
 def hca_decode_1m(**kw) -> Config:
     # the heavily compressed branch of the V4 hybrid attention ('DeepSeek-V4'
     # page, section 2.3.2): every 128 tokens of a 1,048,576-token context
@@ -127,4 +138,5 @@ ALL = {
     "c4": mixed_serving,
     "stack": decoder_stack_128k,
     "hca": hca_decode_1m,
+    "v4csa": v4_csa_decode_1m,
 }

@@ -357,3 +357,35 @@ def test_hca_decode_rows():
         assert tol_ok(out[row], o), (row, float(np.abs(out[row] - o).max()))
     del wl
     torch.cuda.empty_cache()
+
+
+def test_v4_csa_decode_rows():
+    """The compressed sparse attention of the V4 hybrid ('DeepSeek-V4' page,
+    sections 2.3.1 and 4.2.1): 16 requests of 1,048,576 tokens at 4 tokens
+    per entry (262,144 entries), 64 indexer heads, the top-512 over every
+    visible entry, the window and a per-head sink.  Invariants on every row;
+    three rows' scores, block maxima, top-512 and output against the oracle."""
+    cfg = configs.v4_csa_decode_1m()
+    wl = Workload(cfg)
+    wl.step()
+    torch.cuda.synchronize()
+    check_invariants(wl, n_pool=512)
+    rows = [0, 9, 15]
+
+    def job(row):
+        ref = RowRef(cfg, row, 0)
+        scores = ref.scores_at(np.arange(ref.n_vis), chunk=1 << 15)
+        idx = ref.select_prefill(scores)      # the top-512 of every visible score
+        o_p, lse_p, o = ref.attend(idx, sink=ref.sink)
+        return dict(ref=ref, scores=scores, idx=idx, o_p=o_p, lse_p=lse_p, o=o)
+
+    for row in rows:
+        d = job(row)
+        n_vis = d["ref"].n_vis
+        got = wl.scores[row, :n_vis].cpu().numpy()
+        assert np.array_equal(got, d["scores"]), (row, np.nonzero(got != d["scores"])[0][:5])
+        nb = (n_vis + 7) // 8
+        assert np.array_equal(wl.block_max[row, :nb].cpu().numpy(), oracle.block_max(d["scores"]))
+        compare_attention(wl, 0, row, d)
+    del wl
+    torch.cuda.empty_cache()
