@@ -342,11 +342,12 @@ __device__ __forceinline__ int slice_pte(const KvView& kv, int req, int ncols, i
 
 // MULTI: a full scan whose workgroups take more than one slice of their row;
 // PTE: a full scan of a paged cache (page-table entries loaded ahead).
-// NM = ceil(heads / 4) MFMAs per tile with the query operands in registers,
-// for up to 16 heads; NM = 0: more than 16 heads, in groups of 16 whose
-// operands are read from LDS for each tile, folded in head order.
+// NM = ceil(heads / 4) MFMAs per tile for up to 16 heads, each giving all
+// lanes the same 4 heads; NM = 0: more than 16 heads, one MFMA per group of
+// 16 heads and tile, transposed over the lanes before the fold.  The query
+// operands stay in registers for the whole scan.
 template <bool QBF16, bool POOL, int NM, bool MULTI, bool PTE>
-__global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, IndexScoreArgs a) {
+__device__ __forceinline__ void index_score_body(const KvView& kv, const IndexScoreArgs& a) {
     constexpr bool GROUPED = NM == 0;
     constexpr int NMR = GROUPED ? 4 : NM;             // MFMAs per head group
     __shared__ __align__(16) QShared<GROUPED ? IS_MAX_HEADS : 16> qs;
@@ -396,17 +397,21 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
     // Up to 16 heads: MFMA k takes heads 4k .. 4k+3 on every row group (row n
     // carries head 4k + (n & 3)).  More than 16 heads: MFMA g takes the 16
     // heads of group g, one per row (row n carries head 16g + n).
+    // (the transposed layout measured slower than this one for 8 heads, where
+    // the scan is bound by HBM: it serves more than 16 heads only)
+    constexpr bool TRANS = GROUPED;
     constexpr int NA = GROUPED ? IS_MAX_HEADS / 16 : NMR;
+    constexpr int NS = 4;                              // row groups of 4 heads folded per head group
     i32x8 Aq[NA];
     int sa[NA];
-    float wl[GROUPED ? 1 : 4 * NMR];
+    float wl[TRANS ? 1 : 4 * NMR];
 #pragma unroll
     for (int k = 0; k < NA; ++k) {
-        const int h = GROUPED ? 16 * k + n : 4 * k + (n & 3);
+        const int h = TRANS ? 16 * k + n : 4 * k + (n & 3);
         const uint4 v = *(const uint4*)&qs.q.codes[h][16 * lg];   // group rows above ng: unused
         Aq[k] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         sa[k] = qs.q.scales[h][lg];
-        if (!GROUPED) {
+        if (!TRANS) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) wl[4 * k + i] = qs.q.w[4 * k + i];   // 0 above n_heads
         }
@@ -459,15 +464,17 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
                 const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d[0][i]), __float_as_uint(d[2][i]), false, false);
                 const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d[1][i]), __float_as_uint(d[3][i]), false, false);
                 const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
-                const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
                 hv[0][i] = __uint_as_float(q01[0]);
                 hv[1][i] = __uint_as_float(q01[1]);
-                hv[2][i] = __uint_as_float(q23[0]);
-                hv[3][i] = __uint_as_float(q23[1]);
+                if (NS > 2) {
+                    const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+                    hv[2][i] = __uint_as_float(q23[0]);
+                    hv[3][i] = __uint_as_float(q23[1]);
+                }
             }
             const float4* wg = (const float4*)&qs.q.w[16 * g];   // 0 above n_heads
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
+            for (int s4 = 0; s4 < NS; ++s4) {
                 const float4 w4 = wg[s4];
                 acc = fmaf(w4.x, relu_bits(hv[s4][0]), acc);
                 acc = fmaf(w4.y, relu_bits(hv[s4][1]), acc);
@@ -495,7 +502,7 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
 
     auto compute = [&](const KeyBatch& kb, int col_base, int lbase) __attribute__((always_inline)) {
         float val;
-        if constexpr (GROUPED) {
+        if constexpr (TRANS) {
             val = compute_grouped(kb, col_base, lbase);
         } else {
         float vt[IS_TILES];
@@ -611,6 +618,20 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, I
         }
         if (brow) brow[c8 >> 3] = bm;
     }
+}
+
+template <bool QBF16, bool POOL, int NM, bool MULTI, bool PTE>
+__global__ __launch_bounds__(IS_WAVES * 64) void index_score_kernel(KvView kv, IndexScoreArgs a) {
+    index_score_body<QBF16, POOL, NM, MULTI, PTE>(kv, a);
+}
+
+// More than 16 heads.  The declared floor of 2 waves per SIMD caps the
+// kernel at 256 registers, so the compiler gives the MFMAs VGPR results (the
+// transpose reads them right away) instead of AGPRs copied out one by one.
+template <bool QBF16, bool POOL, bool MULTI, bool PTE>
+__global__ __launch_bounds__(IS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void index_score_heads_kernel(
+    KvView kv, IndexScoreArgs a) {
+    index_score_body<QBF16, POOL, 0, MULTI, PTE>(kv, a);
 }
 
 // ---------------------------------------------------------------- rows of one request
@@ -796,7 +817,7 @@ static void launch_nm(int nm, dim3 grid, dim3 block, hipStream_t st, const KvVie
         case 2: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 2, MULTI, PTE>), grid, block, 0, st, kv, a); break;
         case 3: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 3, MULTI, PTE>), grid, block, 0, st, kv, a); break;
         case 4: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 4, MULTI, PTE>), grid, block, 0, st, kv, a); break;
-        default: hipLaunchKernelGGL((index_score_kernel<QBF16, POOL, 0, MULTI, PTE>), grid, block, 0, st, kv, a); break;
+        default: hipLaunchKernelGGL((index_score_heads_kernel<QBF16, POOL, MULTI, PTE>), grid, block, 0, st, kv, a); break;
     }
 }
 
