@@ -361,6 +361,20 @@ __device__ __forceinline__ void load_pool_keys(const float* krow, const int32_t*
     }
 }
 
+// Keys of the 8 blocks of super-block sb (blocks 8 sb .. 8 sb + 7; absent
+// past nb or for sb < 0): two 16-B loads where the run is whole and aligned.
+__device__ __forceinline__ void load_block8(const float* brow, int nb, int sb, uint32_t* u) {
+    const float* p = brow + 8 * (int64_t)(sb >= 0 ? sb : 0);
+    if (sb >= 0 && 8 * sb + 8 <= nb && ((uintptr_t)p & 15) == 0) {
+        const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
+        u[0] = order_key(v0.x); u[1] = order_key(v0.y); u[2] = order_key(v0.z); u[3] = order_key(v0.w);
+        u[4] = order_key(v1.x); u[5] = order_key(v1.y); u[6] = order_key(v1.z); u[7] = order_key(v1.w);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = (sb >= 0 && 8 * sb + i < nb) ? order_key(p[i]) : 0u;
+}
+
 __device__ __forceinline__ int col_id(const int32_t* pool, int c) {
     return pool ? 8 * pool[c >> 3] + (c & 7) : c;
 }
@@ -404,10 +418,23 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
 // among the blocks whose maximum reaches the histogram bin of the k-th largest
 // block maximum; y = 1 gathers the scores of those blocks only (if there are
 // more than the pool size, of the top k blocks) and selects among them.
+//
+// PATH (chosen by the launcher, one instantiation each so that the register
+// allocation of one form does not weigh on the others): SF_SPLIT, two
+// workgroups per row; SF_REG, one per row, every row of at most 16,384 x 8
+// blocks (held in registers); SF_ANY, one per row, any length.
+constexpr int SF_SPLIT = 0, SF_REG = 1, SF_ANY = 2;
+
+// the select kernel's LDS: the top-k state and the row's super-block maxima
+struct __align__(16) SfShared : TkShared {
+    uint32_t sbk[TK_SWEEP];            // order key of the maximum of each super-block of 8 blocks
+};
+
+template <int PATH>
 __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs a) {
-    __shared__ TkShared sh;
+    __shared__ SfShared sh;
     const int row = blockIdx.x;
-    const bool split = gridDim.y > 1;
+    constexpr bool split = PATH == SF_SPLIT;
     const int nv = max(0, min(a.n_vis[row], a.max_vis));
     const int nb = (nv + 7) >> 3;
     const float* brow = a.block_max + (int64_t)row * a.block_max_stride;
@@ -528,25 +555,44 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         np = select_row<1>(sh, nb, a.k, bkeys, temit, 0u, m, vv);
     } else if (nb <= TK_SWEEP) {
         np = select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
-    } else if (nb <= 8 * TK_SWEEP) {
+    } else if (PATH == SF_REG || nb <= 8 * TK_SWEEP) {
         // Longer rows, in registers: the top n_pool blocks lie in the top
         // n_pool super-blocks of 8 blocks ranked by their maximum (a super-
         // block ranked above the one of a top block holds a distinct block
         // ranked above it: its maximum, on equal values with a lower id).
-        // Thread t takes super-blocks 16t .. 16t+15 (blocks 128t .. 128t+127).
+        // The super-block maxima are formed once, into LDS, from loads in
+        // which consecutive threads read consecutive super-blocks (a wave's
+        // load covers 2 KB of the row), 4 super-blocks per thread in flight;
+        // the selection then reads thread t's super-blocks 16t .. 16t+15
+        // from LDS.
         const int nsb = (nb + 7) >> 3;
+#pragma unroll 1
+        for (int j0 = 0; j0 * TK_THREADS < nsb; j0 += 4) {
+            uint32_t b[4][8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sb = (j0 + j) * TK_THREADS + (int)threadIdx.x;
+                load_block8(brow, nb, sb < nsb ? sb : -1, b[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sb = (j0 + j) * TK_THREADS + (int)threadIdx.x;
+                uint32_t m = 0u;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = max(m, b[j][i]);
+                if (sb < nsb) sh.sbk[sb] = m;
+            }
+        }
+        __syncthreads();
         auto skeys = [&](int, uint32_t* u) {
+            const int c0 = TK_ITEMS * (int)threadIdx.x;
 #pragma unroll
-            for (int j = 0; j < TK_ITEMS / 2; ++j) {
-                uint32_t b[TK_ITEMS];
-                load_cols(brow, nb, 128 * (int)threadIdx.x + 16 * j, b);
-                uint32_t m0 = 0u, m1 = 0u;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { m0 = max(m0, b[i]); m1 = max(m1, b[8 + i]); }
-                u[2 * j] = m0;
-                u[2 * j + 1] = m1;
-                // at most 64 block maxima in flight per thread (all 128 would spill)
-                if (j == TK_ITEMS / 4 - 1) __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < TK_ITEMS; i += 4) {
+                const uint4 v = *(const uint4*)&sh.sbk[c0 + i];   // c0 + 15 < 16,384: in the array
+                u[i] = c0 + i < nsb ? v.x : 0u;
+                u[i + 1] = c0 + i + 1 < nsb ? v.y : 0u;
+                u[i + 2] = c0 + i + 2 < nsb ? v.z : 0u;
+                u[i + 3] = c0 + i + 3 < nsb ? v.w : 0u;
             }
         };
         auto semit = [&](int col, uint32_t slot, uint32_t) { sh.pool[slot] = col; };
@@ -559,15 +605,8 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         const int sb0 = 2 * (int)threadIdx.x < (int)nsp ? sh.pool[2 * threadIdx.x] : -1;
         const int sb1 = 2 * (int)threadIdx.x + 1 < (int)nsp ? sh.pool[2 * threadIdx.x + 1] : -1;
         auto ckeys = [&](int, uint32_t* u) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int sb = h ? sb1 : sb0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int blk = 8 * sb + i;
-                    u[8 * h + i] = (sb >= 0 && blk < nb) ? order_key(brow[blk]) : 0u;
-                }
-            }
+            load_block8(brow, nb, sb0, u);
+            load_block8(brow, nb, sb1, u + 8);
         };
         auto cemit = [&](int col, uint32_t slot, uint32_t key) {
             const int blk = 8 * ((col & 8) ? sb1 : sb0) + (col & 7);
@@ -620,7 +659,10 @@ hipError_t launch_select_full(const SelectFullArgs& a, hipStream_t st) {
     // shorter rows and larger k keep one workgroup per row
     const bool split = a.max_vis > 64 * a.k && a.max_vis <= 8 * TK_SWEEP && a.k <= a.n_pool && a.k <= 1024 &&
                        2 * a.n_rows <= 256;
-    hipLaunchKernelGGL(select_full_kernel, dim3((unsigned)a.n_rows, split ? 2u : 1u), dim3(TK_THREADS), 0, st, a);
+    const dim3 grid((unsigned)a.n_rows, split ? 2u : 1u), block(TK_THREADS);
+    if (split) hipLaunchKernelGGL(select_full_kernel<SF_SPLIT>, grid, block, 0, st, a);
+    else if ((a.max_vis + 7) / 8 <= 8 * TK_SWEEP) hipLaunchKernelGGL(select_full_kernel<SF_REG>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(select_full_kernel<SF_ANY>, grid, block, 0, st, a);
     return hipGetLastError();
 }
 
