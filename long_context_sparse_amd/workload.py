@@ -64,6 +64,12 @@ def _fill_packed(kind, seed, tensor, width, logical_first, n, codes, scales, slo
         del buf
 
 
+def _padded_rows(n_rows: int, n: int, dev) -> torch.Tensor:
+    """[n_rows][n] fp32 whose rows start on 64-B boundaries, so that the
+    selection reads whole runs of block maxima with 16-B loads."""
+    return torch.empty((n_rows, (n + 15) // 16 * 16), dtype=torch.float32, device=dev)[:, :n]
+
+
 class Layer:
     """Per-layer query-side inputs and outputs of one step.  A Reuse layer
     (``source`` given) has no indexer inputs and reads the selection of its
@@ -188,7 +194,7 @@ class Workload:
         self.full = mode in ("full", "prefill", "mixed", "csa")
         if self.full:
             self.scores = torch.empty((self.n_rows, self.nv8), dtype=torch.float32, device=dev)
-            self.block_max = torch.empty((self.n_rows, self.nv8 // 8), dtype=torch.float32, device=dev)
+            self.block_max = _padded_rows(self.n_rows, self.nv8 // 8, dev)
         if mode in ("full", "mixed", "reindex"):
             self.pool = torch.empty((self.n_rows, 2048), dtype=torch.int32, device=dev)
             self.pool_count = torch.empty((self.n_rows,), dtype=torch.int32, device=dev)
@@ -216,7 +222,7 @@ class Workload:
         for name in ("scores", "block_max", "pool", "pool_count", "pool_scores", "workspace"):
             t = getattr(self, name, None)
             if t is not None:
-                setattr(mb, name, t.clone())
+                setattr(mb, name, _padded_rows(t.shape[0], t.shape[1], self.dev) if name == "block_max" else t.clone())
         mb.layers = []
         new_sel = {}
         for layer in self.layers:
