@@ -333,7 +333,7 @@ csa2_status csa2_sparse_swa_attn(const csa2_kv* kv, const csa2_rows* rows,
  * NULL: no window) and the sink.  Same output conventions, numerics and
  * bitwise batch invariance as csa2_sparse_swa_attn (the entry list is the
  * row's entries padded to a multiple of 64, then the window, cut into units
- * of 192 entries folded left to right).  workspace: NULL or
+ * of 768 entries folded left to right).  workspace: NULL or
  * csa2_dense_attn_workspace_size(n_rows, n_heads, rows->max_vis) bytes,
  * 256-B aligned, not kept between calls; with it a launch with few rows
  * spreads each row's units over several workgroups. */

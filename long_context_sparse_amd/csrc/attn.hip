@@ -12,9 +12,10 @@
 // MI355X mapping
 //   * A row's entry list is its selected FP4 entries padded to a multiple of
 //     64, then its window entries; it is walked in chunks of 64 with an
-//     online softmax.  Every 3 chunks form a unit (at most 4 per row) whose
-//     max, sum and output start afresh; the units are joined left to right
-//     by one fold.  One workgroup takes (row, group of 16 heads, split):
+//     online softmax.  Every 3 chunks form a unit (at most 4 per row; 12
+//     chunks for the dense rows of the heavily compressed branch, so a long
+//     row leaves one partial per 768 entries) whose max, sum and output start
+//     afresh; the units are joined left to right by one fold.  One workgroup takes (row, group of 16 heads, split):
 //     without a workspace there is one split, which folds its units as it
 //     goes and writes the final output; with one, a launch with few rows
 //     gives each (row, group) up to 4 splits of consecutive units (so the
@@ -66,6 +67,7 @@ constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int V_LD = 512 + 16;          // fp16 elements per entry row of V in LDS (32 B pad spreads the banks)
 constexpr int AT_MAX_SEL = 512;
 constexpr int AT_UNIT = 3;              // chunks per unit of the fixed fold
+constexpr int AT_UNIT_DENSE = 12;       // chunks per unit of a dense row (one partial per 768 entries)
 constexpr int AT_MAX_UNITS = (AT_MAX_SEL / AT_ENT + 128 / AT_ENT + AT_UNIT - 1) / AT_UNIT;   // 4
 constexpr int AT_MAX_SPLITS = AT_MAX_UNITS;   // workgroups sharing one (row, head group)
 constexpr int AT_TW_SEL = 4;            // power of two on every dequantised selected entry
@@ -256,13 +258,14 @@ __device__ __forceinline__ int xcd_order(int b, int total) {
     return base + k;
 }
 
-// Units of a row's entry list: ceil(chunks / 3), chunks = ceil(selected / 64)
-// + ceil(window / 64).
+// Units of a row's entry list: ceil(chunks / 3) (dense rows: ceil(chunks /
+// 12)), chunks = ceil(selected / 64) + ceil(window / 64).
 __device__ __forceinline__ int row_units(const AttnArgs& a, int nsp_raw, int nsw_raw) {
     const int nsp = a.dense_n ? min(max(nsp_raw, 0), a.max_dense) : (a.idx ? min(max(nsp_raw, 0), AT_MAX_SEL) : 0);
     const int nsw = a.swa_codes ? min(max(nsw_raw, 0), 128) : 0;
     const int ctot = (nsp + AT_ENT - 1) / AT_ENT + (nsw + AT_ENT - 1) / AT_ENT;
-    return (ctot + AT_UNIT - 1) / AT_UNIT;
+    const int unit = a.dense_n ? AT_UNIT_DENSE : AT_UNIT;
+    return (ctot + unit - 1) / unit;
 }
 
 // The fold of one unit (base-2 max m, sum l, output o = sum of 2^(z - m) E,
@@ -322,11 +325,12 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     const int nsp = DENSE ? min(max(a.dense_n[row], 0), a.max_dense)
                           : (a.idx ? min(max(a.idx_count[row], 0), AT_MAX_SEL) : 0);
     const int nsw = a.swa_codes ? min(max(a.swa_count[row], 0), 128) : 0;
+    constexpr int UNIT = DENSE ? AT_UNIT_DENSE : AT_UNIT;           // chunks per unit
     const int csp = (nsp + AT_ENT - 1) / AT_ENT;
     const int ctot = csp + (nsw + AT_ENT - 1) / AT_ENT;
-    const int U = (ctot + AT_UNIT - 1) / AT_UNIT;
+    const int U = (ctot + UNIT - 1) / UNIT;
     const int ub = split * U / S, ue = (split + 1) * U / S;         // this split's units
-    const int cb = AT_UNIT * ub, ce = min(AT_UNIT * ue, ctot);      // and chunks
+    const int cb = UNIT * ub, ce = min(UNIT * ue, ctot);            // and chunks
     if (SPLIT && ue == ub) return;                                  // a short row: no unit here
     const int64_t swa0 = nsw ? a.swa_first[row] : 0;
 
@@ -341,6 +345,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
                                              : (const int32_t*)a.q;
     const int32_t idx_raw = *idx_p;
     const int req_r = *(a.req ? a.req + row : (const int32_t*)a.q);
+    // the external partial's log-sum-exp and the sink, used by the epilogue
+    const float lse_raw = *(a.lse_in ? a.lse_in + (int64_t)row * a.n_heads + h0 + n : (const float*)a.q);
+    const float sink_raw = *(a.sink ? a.sink + h0 + n : (const float*)a.q);
     const bool has_sc = (int)threadIdx.x * 8 < nsw * 32;
     const uint2 scv = *(const uint2*)(has_sc ? a.swa_scales + swa0 * 32 + 8 * threadIdx.x : (const uint8_t*)a.q);
     bf16x8 qb[8];
@@ -530,13 +537,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         for (int ct = 0; ct < 4; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     };
 
-    static_assert(AT_UNIT == 3, "a unit is one turn of the three-step loop");
+    static_assert(AT_UNIT % 3 == 0 && AT_UNIT_DENSE % 3 == 0, "a unit is whole turns of the three-step loop");
     if (ce > cb) {
         if (cb < csp) stage_a(SEL, cb, raw0);
         else stage_a(WIN, cb, raw0);
         __syncthreads();
         for (int c = cb;; c += 3) {
-            if (c > cb) end_unit(c / AT_UNIT - 1, c - 1);   // c starts a unit
+            if (c > cb && c % UNIT == 0) end_unit(c / UNIT - 1, c - 1);   // c starts a unit
             if (c + 1 >= ce) { stage_b(c); break; }
             step(c, raw1);
             if (c + 2 >= ce) { stage_b(c + 1); break; }
@@ -544,14 +551,14 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
             if (c + 3 >= ce) { stage_b(c + 2); break; }
             step(c + 2, raw0);
         }
-        end_unit((ce - 1) / AT_UNIT, ce - 1);
+        end_unit((ce - 1) / UNIT, ce - 1);
     }
     if constexpr (SPLIT) return;
     // ---- epilogue: the folded units, an external partial (o_in, lse_in) and
     // the sink in one denominator; write O^T[64*wave + 16ct + 4g + i][head
     // h0 + n].  Natural-log terms become base 2 with log2(e).
-    const float lse_p = a.lse_in ? a.lse_in[(int64_t)row * a.n_heads + h] * LOG2E : -INFINITY;
-    const float sk = a.sink ? a.sink[h] * LOG2E : -INFINITY;
+    const float lse_p = a.lse_in ? lse_raw * LOG2E : -INFINITY;
+    const float sk = a.sink ? sink_raw * LOG2E : -INFINITY;
     const FinalW fw = final_weights(Mf, Lf, lse_p, sk);
     const float* oin = a.o_in ? a.o_in + ((int64_t)row * a.n_heads + h) * 512 : nullptr;
     float* orow = a.out + ((int64_t)row * a.n_heads + h) * 512;
@@ -648,7 +655,7 @@ size_t attn_workspace_bytes(int n_rows, int n_heads, int n_splits) {
 // splits that fill the 256 CUs once (at most one per unit).
 int dense_units(int max_dense) {
     const int chunks = (max_dense + AT_ENT - 1) / AT_ENT + 128 / AT_ENT;
-    return (chunks + AT_UNIT - 1) / AT_UNIT;
+    return (chunks + AT_UNIT_DENSE - 1) / AT_UNIT_DENSE;
 }
 
 int dense_splits(int n_rows, int n_heads, int max_dense) {
