@@ -80,55 +80,6 @@ def measured_traffic(workload):
     return d.get("bytes_per_launch")
 
 
-class HipEvent:
-    """A HIP event recorded on torch's current stream (the stream every kernel
-    of the step is launched on).  Created with hipEventDisableSystemFence: the
-    default event ends with a system-scope release, a cache write-back that
-    costs about 2.5 us per event pair and lands inside the bracketed interval;
-    without it the event interval matches the kernel-trace duration of the
-    bracketed kernel and the step is not slowed by the measurement."""
-    FLAGS = 0x20000000          # hipEventDisableSystemFence
-    _hip = None
-
-    @classmethod
-    def _rt(cls):
-        if cls._hip is None:
-            import ctypes
-            import torch  # noqa: F401  (loads the HIP runtime the library and torch share)
-            h = ctypes.CDLL("libamdhip64.so.7")
-            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
-            cls._hip = h
-        return cls._hip
-
-    def __init__(self):
-        import ctypes
-        self._c = ctypes
-        self.h = ctypes.c_void_p()
-        rc = self._rt().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS)
-        if rc != 0:
-            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
-
-    def record(self):
-        import torch
-        rc = self._rt().hipEventRecord(self.h, self._c.c_void_p(torch.cuda.current_stream().cuda_stream))
-        if rc != 0:
-            raise RuntimeError(f"hipEventRecord failed ({rc})")
-
-    def elapsed_ms(self, end: "HipEvent") -> float:
-        f = self._c.c_float()
-        rc = self._rt().hipEventElapsedTime(self._c.byref(f), self.h, end.h)
-        if rc != 0:
-            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
-        return f.value
-
-    def __del__(self):
-        if self._hip is not None and self.h:
-            self._hip.hipEventDestroy(self.h)
-
-
 def cpu_model():
     """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
     try:
@@ -190,6 +141,7 @@ def bench_write(args):
     import torch
 
     import long_context_sparse_amd as lib
+    from long_context_sparse_amd.hip_events import HipEvent
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     n_tok, m = 262144, 2
@@ -254,6 +206,7 @@ def main():
     import torch
 
     import long_context_sparse_amd as lib
+    from long_context_sparse_amd.hip_events import HipEvent
     from long_context_sparse_amd.workload import Workload
     from synth import configs
 
@@ -321,7 +274,9 @@ def main():
     # every step bracketed by HIP events (no system fence), steps enqueued back
     # to back with no synchronisation in between, so each interval holds its
     # kernels' execution on a busy stream and not the host's launch latency.
-    # The dominant kernel's roofline averages this pass's launches.
+    # The dominant kernel's roofline averages this pass's launches.  (Events
+    # around one call only per pass measure worse: the bracketed interval
+    # then also holds the end-of-kernel write-back of the call before it.)
     names = ["index_score", "select", "attention"]
     if cfg.mode == "reindex":
         names = ["index_score", "select_positions", "attention"]
@@ -424,7 +379,9 @@ def main():
         "two_batches_in_flight": overlap,
         "kernels_us": kernels_us,
         "kernels_us_note": f"means over the {nb}-step per-kernel pass (events around each call, stream kept busy; "
-                           f"that pass ran at {breakdown_step_us:.1f} us per step)",
+                           f"that pass ran at {breakdown_step_us:.1f} us per step); consecutive kernels overlap at "
+                           f"their boundaries (the next one is dispatched during the previous one's end-of-kernel "
+                           f"write-back), so the durations of one step can add up to slightly more than the step",
         "roofline": roofline,
         "read_ceiling": None if not rd_hbm else {
             "kernel": "stream_xor_kernel",

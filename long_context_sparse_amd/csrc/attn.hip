@@ -80,7 +80,7 @@ struct AttnSmem {
     f32x4 sp[2][AT_WAVES][64];          // per-wave half-channel S^T tiles, double-buffered
     int64_t ent[AT_MAX_SEL];            // cache slot of each selected entry
     float qmax[2][16];                  // per channel half and head: largest |q|
-    int wrange[2][AT_WAVES];            // per wave: largest and smallest nonzero window scale code
+    int wrange[AT_WAVES];               // per wave: largest nonzero window scale code
 };
 constexpr size_t AT_LDS = sizeof(AttnSmem);
 static_assert(AT_LDS <= 160 * 1024, "attention LDS exceeds the 160 KB of a CU");
@@ -353,46 +353,58 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     bf16x8 qb[8];
     float qa = load_q_operand<QBF16>(a.q, (int64_t)row * a.n_heads + h0 + n, kh, g, qb);
     if (!DENSE && (int)threadIdx.x < nsp) sm.ent[threadIdx.x] = entry_of(kv, req_r, idx_raw);   // paged: one more load
-    int wmax = 0, wmin = 255;                       // over nonzero scale codes (all-zero groups have code 0)
-    if (has_sc) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = (int)(((i < 4 ? scv.x : scv.y) >> (8 * (i & 3))) & 0xFFu);
-            if (c) { wmax = max(wmax, c); wmin = min(wmin, c); }
-        }
-    }
     qa = max_xor32(max_xor16(qa));
     if (et == 0 && g == 0) sm.qmax[kh][n] = qa;
+    // The window's scale range needs the window's position first (two memory
+    // round trips, the selected slots one), and only chunks of the window use
+    // it: a split whose first chunk is a selected one publishes it at the
+    // barrier after that chunk's dequantisation, when the scales have long
+    // arrived; one that starts in the window publishes it here.
+    const bool early = cb >= csp;
+    auto publish_wmax = [&]() __attribute__((always_inline)) {
+        int wmax = 0;                               // over nonzero scale codes (all-zero groups have code 0)
+        if (has_sc) {
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        wmax = max(wmax, __shfl_xor(wmax, d, 64));
-        wmin = min(wmin, __shfl_xor(wmin, d, 64));
-    }
-    if (l == 0) { sm.wrange[0][wave] = wmax; sm.wrange[1][wave] = wmin; }
+            for (int i = 0; i < 8; ++i) {
+                const int c = (int)(((i < 4 ? scv.x : scv.y) >> (8 * (i & 3))) & 0xFFu);
+                if (c) wmax = max(wmax, c);
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) wmax = max(wmax, __shfl_xor(wmax, d, 64));
+        if (l == 0) sm.wrange[wave] = wmax;
+    };
+    if (early) publish_wmax();
     __syncthreads();
     const float qmax = fmaxf(sm.qmax[0][n], sm.qmax[1][n]);
     int kq = qmax > 0.0f ? 14 - ((int)((__float_as_uint(qmax) >> 23) & 0xFFu) - 127) : 0;
     kq = kq < -110 ? -110 : (kq > 110 ? 110 : kq);
     f16x8 qh[8];
     q_to_f16(qb, kq, qh);
-    wmax = 0;
-    wmin = 255;
-#pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) { wmax = max(wmax, sm.wrange[0][w]); wmin = min(wmin, sm.wrange[1][w]); }
+    // logits in base 2: z2 = S' * cz with S' = S * 2^(kq + factor), per entry kind
+    constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
+    const float cz_sel = ldexpf(a.scale * LOG2E, -kq - AT_TW_SEL);
+    constexpr float cvt_sel = (float)(1 << (AT_TW_SEL + 8));                    // 2^(AT_TW_SEL + 8)
     // The window's power of two 2^tw: its largest group (biased scale code
     // wmax, e = wmax - 127) lands at e + tw = 7, the top of the exact fp16
     // range; groups within 22 octaves of it are exact, smaller ones rounded
     // (an absolute change of at most 2^-40 of the window's largest value).
-    // Selected entries always carry 2^AT_TW_SEL.
-    int tw = wmax ? 134 - wmax : 0;
-    tw = tw < AT_TW_WIN_MIN ? AT_TW_WIN_MIN : (tw > AT_TW_WIN_MAX ? AT_TW_WIN_MAX : tw);
-    // logits in base 2: z2 = S' * cz with S' = S * 2^(kq + factor), per entry kind
-    constexpr float LOG2E = 1.44269504088896341f, LN2 = 0.693147180559945309f;
-    const float cz_sel = ldexpf(a.scale * LOG2E, -kq - AT_TW_SEL);
-    const float cz_win = ldexpf(a.scale * LOG2E, -kq - tw);
-    constexpr float cvt_sel = (float)(1 << (AT_TW_SEL + 8));                    // 2^(AT_TW_SEL + 8)
-    // a running output crossing from selected to window chunks: 2^(tw - AT_TW_SEL)
-    const float cross = __uint_as_float((uint32_t)(127 + tw - AT_TW_SEL) << 23);
+    // Selected entries always carry 2^AT_TW_SEL.  cz_win: the window's logit
+    // factor; cross: a running output crossing from selected to window chunks
+    // is re-expressed by 2^(tw - AT_TW_SEL); pw_win: 2^-tw.
+    int tw = 0;
+    float cz_win = 0.0f, cross = 1.0f, pw_win = 1.0f;
+    auto take_tw = [&]() __attribute__((always_inline)) {
+        int wmax = 0;
+#pragma unroll
+        for (int w = 0; w < AT_WAVES; ++w) wmax = max(wmax, sm.wrange[w]);
+        tw = wmax ? 134 - wmax : 0;
+        tw = tw < AT_TW_WIN_MIN ? AT_TW_WIN_MIN : (tw > AT_TW_WIN_MAX ? AT_TW_WIN_MAX : tw);
+        cz_win = ldexpf(a.scale * LOG2E, -kq - tw);
+        cross = __uint_as_float((uint32_t)(127 + tw - AT_TW_SEL) << 23);
+        pw_win = __uint_as_float((uint32_t)(127 - tw) << 23);
+    };
+    if (early) take_tw();
 
     // Software pipeline, one barrier per chunk: while a wave turns the scores of
     // chunk c into probabilities and accumulates P.V (LDS buffers c & 1), it
@@ -507,7 +519,6 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     // folded into (Mf, Lf, Of); the next unit starts afresh.
     const int h = h0 + n;
     const float pw_sel = 1.0f / (float)(1 << AT_TW_SEL);                  // 2^-AT_TW_SEL (exact)
-    const float pw_win = __uint_as_float((uint32_t)(127 - tw) << 23);    // 2^-tw (exact)
     float Mf = -INFINITY, Lf = 0.0f;
     f32x4 Of[4];
 #pragma unroll
@@ -541,7 +552,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
     if (ce > cb) {
         if (cb < csp) stage_a(SEL, cb, raw0);
         else stage_a(WIN, cb, raw0);
+        if (!early) publish_wmax();
         __syncthreads();
+        if (!early) take_tw();
         for (int c = cb;; c += 3) {
             if (c > cb && c % UNIT == 0) end_unit(c / UNIT - 1, c - 1);   // c starts a unit
             if (c + 1 >= ce) { stage_b(c); break; }
