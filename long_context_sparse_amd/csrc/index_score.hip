@@ -172,17 +172,22 @@ struct QRaw {
     uint32_t w[32];
 };
 
-// Lane (head hoff + l % 16, block l / 16).
+// Lane (head hoff + l % 16, block l / 16).  Up to 8 heads (`halves`): lane
+// (head l % 8, half (l / 8) % 2, block l / 16) holds the 16 channels of that
+// half of the block, so every lane of the wave has work.
 template <bool QBF16>
-__device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, int n_heads, int hoff = 0) {
+__device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, int n_heads, int hoff = 0,
+                                           bool halves = false) {
     const int l = threadIdx.x & 63;
-    const int m = hoff + (l & 15), g = l >> 4;
+    const int m = hoff + (halves ? (l & 7) : (l & 15)), g = l >> 4;
     if (m >= n_heads) return;
-    const int64_t off = ((int64_t)row * n_heads + m) * 128 + 32 * g;
+    const int64_t off = ((int64_t)row * n_heads + m) * 128 + 32 * g + (halves ? 16 * ((l >> 3) & 1) : 0);
+    const int nw = (QBF16 ? 4 : 8) >> (halves ? 1 : 0);     // 16-B loads
     if (QBF16) {
         const uint4* p = (const uint4*)((const uint16_t*)q_idx + off);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (i >= nw) break;
             const uint4 v = p[i];
             r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
         }
@@ -190,6 +195,7 @@ __device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, 
         const uint4* p = (const uint4*)((const float*)q_idx + off);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            if (i >= nw) break;
             const uint4 v = p[i];
             r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
         }
@@ -201,34 +207,64 @@ __device__ __forceinline__ void load_query(QRaw& r, const void* q_idx, int row, 
 // their exactness-guard bounds (spread, min, max; returned in every lane).
 template <bool QBF16, class QR>
 __device__ __forceinline__ void prep_query(QR& qs, const QRaw& r, const float* w, int row, int n_heads, int hoff,
-                                           int& spread_out, int& smin_out, int& smax_out) {
+                                           int& spread_out, int& smin_out, int& smax_out, bool halves = false) {
     const int l = threadIdx.x & 63;
-    const int m = hoff + (l & 15), g = l >> 4;
+    const int m = hoff + (halves ? (l & 7) : (l & 15)), g = l >> 4;
     uint32_t words[4] = {0, 0, 0, 0};
     int sc = 127;
     const bool real = m < n_heads;
-    if (real) {
-        float x[32];
+    if (halves) {
+        // 16 channels per lane; the block's scale needs the other half's
+        // largest magnitude (lane l ^ 8)
+        float x[16];
         if (QBF16) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
+            for (int j = 0; j < 8; ++j) {
                 x[2 * j] = __uint_as_float(r.w[j] << 16);
                 x[2 * j + 1] = __uint_as_float(r.w[j] & 0xFFFF0000u);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(r.w[i]);
+            for (int i = 0; i < 16; ++i) x[i] = __uint_as_float(r.w[i]);
         }
         float amax = 0.0f;
+        if (real) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-        const int ex = mx_exponent(amax, 2);
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+        if (real) {
+            const int ex = mx_exponent(amax, 2);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_encode(ldexpf(x[i], -ex)) << (4 * (i & 7));
-        sc = ex + 127;
+            for (int i = 0; i < 16; ++i) words[i >> 3] |= e2m1_encode(ldexpf(x[i], -ex)) << (4 * (i & 7));
+            sc = ex + 127;
+        }
+        *(uint2*)&qs.codes[m][16 * g + 8 * ((l >> 3) & 1)] = make_uint2(words[0], words[1]);
+        if (!(l & 8)) qs.scales[m][g] = (uint8_t)sc;
+    } else {
+        if (real) {
+            float x[32];
+            if (QBF16) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    x[2 * j] = __uint_as_float(r.w[j] << 16);
+                    x[2 * j + 1] = __uint_as_float(r.w[j] & 0xFFFF0000u);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(r.w[i]);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+            const int ex = mx_exponent(amax, 2);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_encode(ldexpf(x[i], -ex)) << (4 * (i & 7));
+            sc = ex + 127;
+        }
+        *(uint4*)&qs.codes[m][16 * g] = make_uint4(words[0], words[1], words[2], words[3]);
+        qs.scales[m][g] = (uint8_t)sc;
     }
-    *(uint4*)&qs.codes[m][16 * g] = make_uint4(words[0], words[1], words[2], words[3]);
-    qs.scales[m][g] = (uint8_t)sc;
     if (l < 16) qs.w[hoff + l] = (hoff + l < n_heads) ? w[(int64_t)row * n_heads + hoff + l] : 0.0f;
     // per-head spread over its 4 blocks (lanes m, m+16, m+32, m+48)
     int mn = real ? sc : 1 << 20, mx = real ? sc : -(1 << 20);
@@ -373,7 +409,10 @@ __device__ __forceinline__ void index_score_body(const KvView& kv, const IndexSc
 
     QRaw qraw;
     const int ng = GROUPED ? (a.n_heads + 15) >> 4 : 1;   // head groups of 16; wave w prepares group w
-    if (wave < ng) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads, 16 * wave);   // issued before the keys
+    // up to 8 heads: every lane of wave 0 quantises half a block (the other
+    // waves wait for it at the barrier below)
+    const bool halves = !GROUPED && a.n_heads <= 8;
+    if (wave < ng) load_query<QBF16>(qraw, a.q_idx, row, a.n_heads, 16 * wave, halves);   // issued before the keys
     KeyBatch A, B;
     int pte = PTE && !POOL ? slice_pte(kv, req, ncols, wbase, BSTRIDE, TSTRIDE, l) : 0;
     load_batch<POOL, PTE && !POOL>(kv, req, pool, nullptr, 0, nv, ncols, wbase, TSTRIDE, n, lg, A, pte);   // in flight during the query prep
@@ -385,7 +424,7 @@ __device__ __forceinline__ void index_score_body(const KvView& kv, const IndexSc
     }
     if (wave < ng) {
         int sp, mn, mx;
-        prep_query<QBF16>(qs.q, qraw, a.w, row, a.n_heads, 16 * wave, sp, mn, mx);
+        prep_query<QBF16>(qs.q, qraw, a.w, row, a.n_heads, 16 * wave, sp, mn, mx, halves);
         if (l == 0) {
             if (GROUPED) { qs.st[wave][0] = sp; qs.st[wave][1] = mn; qs.st[wave][2] = mx; }
             else { qs.q.spread = sp; qs.q.smin = mn; qs.q.smax = mx; }
