@@ -399,8 +399,31 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     // threshold is known) and leave in coalesced runs
     auto emit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)col; };
     uint32_t thr_mask, thr_val;
-    const uint32_t n = ncols <= TK_SWEEP ? select_row<1>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val)
-                                         : select_row<0>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val);
+    uint32_t n;
+    if (ncols <= TK_SWEEP) {
+        // Keys held in registers.  The k largest keys are at least the k-th
+        // largest maximum of any partition of the row into groups (those k
+        // maxima are k distinct keys), so one radix pass over the maxima of
+        // each thread's two groups of 8 columns bounds them from below: keys
+        // under that pass's bin of the k-th largest maximum are dropped, and
+        // the selection proper runs over the rest (the same result, ties
+        // included, with far fewer histogram atomics).
+        uint32_t u[TK_ITEMS];
+        keys(0, u);
+        uint32_t gm[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; ++i) gm[i >> 3] = max(gm[i >> 3], u[i]);
+        uint32_t fmask, fval, kmax;
+        kth_bin<2>(sh, gm, (uint32_t)a.k, fmask, fval, kmax);
+        auto cand = [&](int, uint32_t* v) {
+#pragma unroll
+            for (int i = 0; i < TK_ITEMS; ++i) v[i] = (u[i] & fmask) >= fval ? u[i] : 0u;
+        };
+        n = select_row<1, decltype(cand), decltype(emit), true>(sh, ncols, a.k, cand, emit, 0u, thr_mask,
+                                                                thr_val, fval, kmax);
+    } else {
+        n = select_row<0>(sh, ncols, a.k, keys, emit, 0u, thr_mask, thr_val);
+    }
     __syncthreads();
     const int32_t* irow = a.ids ? a.ids + (int64_t)row * a.ids_stride : nullptr;
     for (int j = threadIdx.x; j < a.k; j += TK_THREADS)
