@@ -234,6 +234,19 @@ __device__ __forceinline__ void q_to_f16(const bf16x8* qv, int kq, f16x8* qh) {
     }
 }
 
+// The low fp16 parts of two probabilities, fp16(p - hi) with hi = fp16(p):
+// p - hi is exact, and V_FMA_MIX{LO,HI}_F16 forms it from the fp16 hi and
+// the fp32 p with one rounding to fp16, writing each half in place (the
+// same bits as an fp32 subtraction and a conversion, in two instructions
+// instead of six).
+__device__ __forceinline__ f16x2 split_lo(f16x2 hi, float p0, float p1) {
+    uint32_t d;
+    const uint32_t h = __builtin_bit_cast(uint32_t, hi);
+    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(p0));
+    asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(d) : "v"(h), "v"(p1));
+    return __builtin_bit_cast(f16x2, d);
+}
+
 // V^T A operand of P.V for channels ch0 .. ch0+15, contraction step u, read
 // from V [entry][channel] with DS_READ_B64_TR_B16.  Within each 16-lane group
 // the transposing read hands lane 4a+b element b of the 4-element rows
@@ -477,12 +490,17 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(z[t][i], cz, -m_new));
-                lsum += p;
-                const _Float16 hi = (_Float16)p;
-                pb[t >> 1][4 * (t & 1) + i] = hi;
-                pl[t >> 1][4 * (t & 1) + i] = (_Float16)(p - (float)hi);
+            for (int i = 0; i < 4; i += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(z[t][i], cz, -m_new));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(z[t][i + 1], cz, -m_new));
+                lsum += p0;
+                lsum += p1;
+                const f16x2 hi = (f16x2){(_Float16)p0, (_Float16)p1};
+                const f16x2 lo = split_lo(hi, p0, p1);
+                pb[t >> 1][4 * (t & 1) + i] = hi[0];
+                pb[t >> 1][4 * (t & 1) + i + 1] = hi[1];
+                pl[t >> 1][4 * (t & 1) + i] = lo[0];
+                pl[t >> 1][4 * (t & 1) + i + 1] = lo[1];
             }
         lsum = add_xor32(add_xor16(lsum));
         l_run = l_run * alpha + lsum;
@@ -490,10 +508,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         const _Float16* vb = sm.v[buf];
         // the first window chunk re-expresses the running output in the
         // window's factor (exact; 1 elsewhere)
-        const float rs = (win && c == csp) ? cross : 1.0f;
+        // (rs is a power of two and alpha <= 1: one product, no rounding)
+        const float ra = (win && c == csp) ? cross * alpha : alpha;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            f32x4 o = (oacc[ct] * rs) * alpha;
+            f32x4 o = oacc[ct] * ra;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const f16x8 vo = v_operand(vb, 64 * wave + 16 * ct, u, n, g);
