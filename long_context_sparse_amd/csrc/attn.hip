@@ -234,19 +234,6 @@ __device__ __forceinline__ void q_to_f16(const bf16x8* qv, int kq, f16x8* qh) {
     }
 }
 
-// The low fp16 parts of two probabilities, fp16(p - hi) with hi = fp16(p):
-// p - hi is exact, and V_FMA_MIX{LO,HI}_F16 forms it from the fp16 hi and
-// the fp32 p with one rounding to fp16, writing each half in place (the
-// same bits as an fp32 subtraction and a conversion, in two instructions
-// instead of six).
-__device__ __forceinline__ f16x2 split_lo(f16x2 hi, float p0, float p1) {
-    uint32_t d;
-    const uint32_t h = __builtin_bit_cast(uint32_t, hi);
-    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(p0));
-    asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(d) : "v"(h), "v"(p1));
-    return __builtin_bit_cast(f16x2, d);
-}
-
 // V^T A operand of P.V for channels ch0 .. ch0+15, contraction step u, read
 // from V [entry][channel] with DS_READ_B64_TR_B16.  Within each 16-lane group
 // the transposing read hands lane 4a+b element b of the 4-element rows
@@ -439,6 +426,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) oacc[ct] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;            // base-2 running max and sum of the unit
+    float neg1 = -1.0f;
+    asm volatile("" : "+v"(neg1));                    // opaque to the optimiser (see stage_b)
     const int chb = 256 * kh + 64 * g;               // first of this lane's 64 dequant channels
     const int v_lane = (16 * et + n) * V_LD + chb;  // this lane's entry row and channels in LDS
 
@@ -471,11 +460,12 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
                 for (int i = 0; i < 4; ++i)
                     if (16 * t + 4 * g + i >= nent) z[t][i] = -INFINITY;
         }
-        float m = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
-                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
-        m = fmaxf(m, fmaxf(fmaxf(fmaxf(z[2][0], z[2][1]), fmaxf(z[2][2], z[2][3])),
-                           fmaxf(fmaxf(z[3][0], z[3][1]), fmaxf(z[3][2], z[3][3]))));
-        m = max_xor32(max_xor16(m));
+        // a tree of three-operand maxima (V_MAX3_F32)
+        auto mx3 = [](float x, float y, float w) { return fmaxf(fmaxf(x, y), w); };
+        const float m9 = mx3(mx3(z[0][0], z[0][1], z[0][2]), mx3(z[0][3], z[1][0], z[1][1]),
+                             mx3(z[1][2], z[1][3], z[2][0]));
+        const float m7 = mx3(mx3(z[2][1], z[2][2], z[2][3]), mx3(z[3][0], z[3][1], z[3][2]), z[3][3]);
+        float m = max_xor32(max_xor16(fmaxf(m9, m7)));
         const bool win = c >= csp;
         const float cz = win ? cz_win : cz_sel;
         const float m_new = fmaxf(m_run, m * cz);         // cz > 0: the scaled maximum
@@ -496,7 +486,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
                 lsum += p0;
                 lsum += p1;
                 const f16x2 hi = (f16x2){(_Float16)p0, (_Float16)p1};
-                const f16x2 lo = split_lo(hi, p0, p1);
+                // p - hi is exact; as an fma with an opaque -1 (not folded
+                // into a subtraction) the compiler forms it from the fp16 hi
+                // and the fp32 p with V_FMA_MIX{LO,HI}_F16, one rounding to
+                // fp16 written in place: the same bits as an fp32 difference
+                // and a conversion, in fewer instructions
+                const f16x2 lo = (f16x2){(_Float16)__builtin_fmaf((float)hi[0], neg1, p0),
+                                         (_Float16)__builtin_fmaf((float)hi[1], neg1, p1)};
                 pb[t >> 1][4 * (t & 1) + i] = hi[0];
                 pb[t >> 1][4 * (t & 1) + i + 1] = hi[1];
                 pl[t >> 1][4 * (t & 1) + i] = lo[0];
