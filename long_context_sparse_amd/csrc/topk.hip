@@ -476,6 +476,34 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     auto bemit = [&](int col, uint32_t slot, uint32_t key) {
         sh.pool[slot] = (key & thr_mask) >= thr_val ? col : (int32_t)((uint32_t)col | 0x80000000u);
     };
+    if (!split && nb <= a.n_pool && nv <= TK_SWEEP) {
+        // Every block is in the pool (blocks 0 .. nb-1, ascending; block
+        // maxima of visible blocks are finite), so the top k positions are
+        // the top k of the whole row: taken directly among its scores, held
+        // in registers, after the group-maximum bound of the k-th key (the
+        // groups of 8 columns are the blocks).  Same ids as the pool route.
+        for (int j = threadIdx.x; j < a.n_pool; j += TK_THREADS) prow[j] = j < nb ? j : -1;
+        if (threadIdx.x == 0) a.pool_count[row] = nb;
+        uint32_t u[TK_ITEMS];
+        load_cols(srow, nv, TK_ITEMS * (int)threadIdx.x, u);
+        uint32_t gm[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < TK_ITEMS; ++i) gm[i >> 3] = max(gm[i >> 3], u[i]);
+        uint32_t fmask, fval, kmax;
+        kth_bin<2>(sh, gm, (uint32_t)a.k, fmask, fval, kmax);
+        auto dkeys = [&](int, uint32_t* v) {
+#pragma unroll
+            for (int i = 0; i < TK_ITEMS; ++i) v[i] = (u[i] & fmask) >= fval ? u[i] : 0u;
+        };
+        auto demit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)col; };
+        uint32_t m3, v3;
+        const uint32_t nd = select_row<1, decltype(dkeys), decltype(demit), true>(sh, nv, a.k, dkeys, demit, 0u, m3,
+                                                                                  v3, fval, kmax);
+        __syncthreads();
+        for (int j = threadIdx.x; j < a.k; j += TK_THREADS) irow[j] = j < (int)nd ? (int32_t)sh.hist[j] : -1;
+        if (threadIdx.x == 0) a.idx_count[row] = (int32_t)nd;
+        return;
+    }
     uint32_t np;
     if (split && blockIdx.y == 0) {
         // the pool alone, emitted straight into the output row

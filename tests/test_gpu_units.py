@@ -483,7 +483,8 @@ def test_topk_block_counts_and_pool_ids():
 def test_select_full_exact(ties, k, rows):
     """The fused Full-layer selection equals the oracle's pool + top-k and
     the two-call form, on rows with no entry, a partial block, fewer than
-    2,048 blocks and more than 16,384 blocks (two sweeps).  With k below the
+    2,048 blocks, exactly 2,048 and just over, and more than 16,384 blocks
+    (two sweeps).  With k below the
     pool size only the pool blocks at or above the histogram bin of the k-th
     block are read again; heavy ties put many blocks into that bin.  Rows of
     at most 131,072 entries ("split") take two workgroups per row, the
@@ -493,7 +494,10 @@ def test_select_full_exact(ties, k, rows):
     if rows == "split":
         n_vis = np.array([0, 13, 5003, 131072, 100003, 40000], np.int32)
     else:
-        n_vis = np.array([0, 13, 5003, 16384 * 8 + 21], np.int32)
+        # rows of at most 2,048 blocks and 16,384 entries (every block in the
+        # pool: their top k is taken directly among all their scores), one
+        # just past that, one of more than 16,384 blocks
+        n_vis = np.array([0, 13, 5003, 16384, 16385, 16384 * 8 + 21], np.int32)
     n_rows, n = len(n_vis), int(n_vis.max())
     nv8 = (n + 7) // 8 * 8
     sc = np.full((n_rows, nv8), -np.inf, np.float32)
