@@ -693,8 +693,11 @@ struct SharedRowsLds {
     uint8_t fix_row[4 * RG * SR_CHUNK / 8];           // its row within the workgroup
 };
 
+// The declared floor of 2 waves per SIMD (the kernel's register count gives
+// 2 anyway) lets the compiler put the MFMA results in VGPRs.
 template <bool QBF16, int NM, int RG>
-__global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvView kv, IndexScoreArgs a, int req) {
+__global__ __launch_bounds__(IS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void index_score_shared_kernel(
+    KvView kv, IndexScoreArgs a, int req) {
     constexpr int R = 4 * RG;
     __shared__ SharedRowsLds<RG> sh;
     const int r0 = (int)blockIdx.y * R;
@@ -775,11 +778,12 @@ __global__ __launch_bounds__(IS_WAVES * 64) void index_score_shared_kernel(KvVie
                     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                     d[rg][k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq[rg][k], Bk, z, 4, 4, 0, sa[rg][k], 0, sb);
                 }
-            // pin every MFMA in wave-uniform control flow (see the single-row kernel)
+            // pin every MFMA in wave-uniform control flow (see the single-row
+            // kernel); the results stay in VGPRs (no AGPR reads per tile)
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-                for (int k = 0; k < NM; ++k) asm volatile("" : "+a"(d[rg][k]));
+                for (int k = 0; k < NM; ++k) asm volatile("" : "+v"(d[rg][k]));
             const int b0 = sd & 0xFF, b1 = (sd >> 8) & 0xFF, b2 = (sd >> 16) & 0xFF, b3 = sd >> 24;
             const int kmin = min(min(b0, b1), min(b2, b3)), kmax = max(max(b0, b1), max(b2, b3));
             const int col = col0 + n;
