@@ -503,8 +503,9 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kernel(KvView kv, AttnArgs a)
         m_run = m_new;
         const _Float16* vb = sm.v[buf];
         // the first window chunk re-expresses the running output in the
-        // window's factor (exact; 1 elsewhere)
-        // (rs is a power of two and alpha <= 1: one product, no rounding)
+        // window's factor: cross, a power of two, joins alpha in one factor
+        // (an exact product unless it falls below the normal range, where the
+        // running output no longer counts)
         const float ra = (win && c == csp) ? cross * alpha : alpha;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
