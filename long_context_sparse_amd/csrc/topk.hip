@@ -17,7 +17,10 @@
 // order writes the selected ids ascending.  Thread t owns columns
 // [16t, 16t+16) of each 16,384-column sweep, so column order is thread order,
 // then item order.  Rows of at most 16,384 columns stay in registers; longer
-// rows are re-read.
+// rows are re-read.  A row held in registers first bounds its k-th key from
+// below by one radix pass over the maxima of groups of 8 columns (the k
+// largest group maxima are k distinct keys) and drops the keys under that
+// bin before the selection proper.
 //
 // Wave-level scans and reductions use DPP row shifts and row broadcasts (no
 // LDS round trips); the 16 wave totals meet in LDS behind one barrier, and
@@ -29,7 +32,8 @@
 // with the pool kept in LDS between them, or, for launches of few long rows,
 // side by side in two workgroups per row: the top 512 positions lie in the
 // top 512 blocks, so they are selected from the blocks at or above a radix
-// bin of the block maxima without waiting for the pool.
+// bin of the block maxima without waiting for the pool.  A row whose blocks
+// all fit the pool takes its top k directly among its scores.
 #include "csa2.h"
 #include "csa2_device.h"
 #include "csa2_launch.h"
