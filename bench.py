@@ -262,6 +262,38 @@ def main():
             "value": round(n2 / dt2 * B * H, 1),
             "step_frac_of_hbm_peak": round(algo["total"] / (dt2 / n2) / 1e9 / PEAK_HBM_GBS, 4),
         }
+        # The same pass once more, each step bracketed by HIP events on its
+        # own stream (after the timed pass, so that its host calls do not
+        # touch the figure above): the share of a step's interval during which
+        # a step of the other batch is also in flight.  A kernel trace cannot
+        # show this: the profiler runs the two streams' dispatches one after
+        # another.
+        n_ev = 50
+        evs = [(HipEvent(), HipEvent()) for _ in range(n_ev)]
+        ref = HipEvent()
+        torch.cuda.synchronize()
+        ref.record(main)
+        for s_ in streams:
+            s_.wait_stream(main)
+        for i in range(n_ev):
+            st_ = streams[i % 2]
+            with torch.cuda.stream(st_):
+                evs[i][0].record(st_)
+                mbs[i % 2].step(copy=args.warmup + i)
+                evs[i][1].record(st_)
+        torch.cuda.synchronize()
+        iv = [(ref.elapsed_ms(a_) * 1e3, ref.elapsed_ms(b_) * 1e3) for a_, b_ in evs]
+        shares = []
+        for i, (lo, hi) in enumerate(iv):
+            other = [iv[j] for j in range(i % 2 ^ 1, n_ev, 2)]
+            beside = sum(max(0.0, min(hi, h2) - max(lo, l2)) for l2, h2 in other)
+            shares.append(beside / max(hi - lo, 1e-9))
+        overlap["event_pass"] = {
+            "steps": n_ev,
+            "mean_step_interval_us": round(sum(h - l for l, h in iv) / n_ev, 2),
+            "span_us_per_step": round((iv[-1][1] - iv[0][0]) / n_ev, 2),
+            "mean_share_beside_other_batch": round(sum(shares) / n_ev, 3),
+        }
         del mbs
 
     if args.calib_copy:
