@@ -13,7 +13,8 @@
 // pass with an LDS histogram of 4,096 bins (scores of one row share few
 // exponent values, so a digit that covers only exponent bits would send most
 // atomics to one bin; 12 bits reach into the mantissa), and stops as soon as
-// the bin holding the k-th key is taken whole.  A block-wide scan in column
+// the bin holding the k-th key is taken whole, or holds at most 64 keys:
+// those are listed and ranked directly.  A block-wide scan in column
 // order writes the selected ids ascending.  Thread t owns columns
 // [16t, 16t+16) of each 16,384-column sweep, so column order is thread order,
 // then item order.  Rows of at most 16,384 columns stay in registers; longer
@@ -55,6 +56,9 @@ struct __align__(16) TkShared {
     uint32_t red[3][TK_WAVES];
     uint32_t digit, above, count, digit2;
     uint32_t ovf[TK_WAVES];            // split selection: a wave had more candidate blocks than its list holds
+    uint32_t lcnt;                     // keys of the k-th key's bin, once it holds at most 64 (ranked directly)
+    uint32_t lkey[64];
+    int32_t lcol[64];
     int32_t pool[TK_POOL];             // fused selection: the row's pool, ascending
 };
 
@@ -138,6 +142,10 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
     uint32_t u[TK_ITEMS];
 #pragma unroll
     for (int i = 0; i < TK_ITEMS; ++i) u[i] = 0u;
+    // the bin list of a previous selection was last read before that
+    // selection's final scan; the first barrier below orders this clear
+    // before any append
+    if (threadIdx.x == 0) sh.lcnt = 0u;
 
     // ---- count, min and max of the present keys; clear the histogram
     uint32_t n_present = 0xFFFFFFFFu, umin = hint_min, umax = hint_max;
@@ -183,6 +191,43 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
         uint32_t in_bin = n_present;
         int pass = 0;
         while (hb >= 0 && in_bin != rem) {
+            if (in_bin <= 64u) {
+                // At most 64 keys remain in the bin of the k-th key: list them
+                // and let every wave rank them itself by (key descending,
+                // column ascending), one list entry per lane.  The rem-th of
+                // them is the threshold key T; the selection is then the keys
+                // above T and the first rem' keys equal to T in column order,
+                // which is what the final scan takes with mask = all bits.
+                for (int s = 0; s < nsweep; ++s) {
+                    if (nsweep > 1) keys(s, u);
+                    const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
+#pragma unroll
+                    for (int i = 0; i < TK_ITEMS; ++i)
+                        if (u[i] != 0u && (u[i] & mask) == prefix) {
+                            const uint32_t slot = atomicAdd(&sh.lcnt, 1u);
+                            sh.lkey[slot] = u[i];
+                            sh.lcol[slot] = c0 + i;
+                        }
+                }
+                __syncthreads();
+                const uint32_t nl = __builtin_amdgcn_readfirstlane(in_bin);
+                const bool has = (uint32_t)lane < nl;
+                const uint32_t kj = has ? sh.lkey[lane] : 0u;
+                const int cj = has ? sh.lcol[lane] : 0;
+                uint32_t rank = 0u;
+                for (uint32_t e = 0; e < nl; ++e) {
+                    const uint32_t ke = __builtin_amdgcn_readlane(kj, e);
+                    const int ce = __builtin_amdgcn_readlane(cj, e);
+                    rank += (ke > kj) || (ke == kj && ce < cj);
+                }
+                // exactly one listed key has rank rem - 1 (1 <= rem <= nl)
+                const uint64_t at = __ballot(has && rank == rem - 1u);
+                const uint32_t t = __builtin_amdgcn_readlane(kj, (int)__builtin_ctzll(at));
+                rem = (uint32_t)__popcll(__ballot(has && kj == t && rank < rem));
+                prefix = t;
+                mask = 0xFFFFFFFFu;
+                break;
+            }
             const int wbits = pass == 0 ? 12 : 10;
             const int shift = hb >= wbits - 1 ? hb - (wbits - 1) : 0;
             const int width = hb - shift + 1;
