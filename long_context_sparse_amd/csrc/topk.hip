@@ -119,8 +119,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
 
 // ---------------------------------------------------------------- one row's selection
 // KEYS(sweep, u) fills u[16] with the order keys of columns
-// sweep*16384 + 16*threadIdx.x + i (0 where absent); EMIT(col, slot, key)
-// records selected column `col` for output slot `slot`.  Returns the count.
+// sweep*16384 + 16*threadIdx.x + i (0 where absent); EMIT(col, slot, mark)
+// records selected column `col` for output slot `slot`; with MARK, `mark` is
+// 1 where the column's key passes (u & thr_mask) >= thr_val below (else it
+// is 0).  Returns the count.
 // NSW = 1 compiles the case of one sweep (ncols <= 16,384: the keys are read
 // once and stay in registers); NSW = 0 handles any ncols.
 //
@@ -132,7 +134,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
 // HINT (one sweep only): every present key lies in [hint_min, hint_max] and
 // the histogram is already clear, so the opening count / min / max round is
 // skipped; the count of present keys comes from the first pass's histogram.
-template <int NSW, class KEYS, class EMIT, bool HINT = false>
+template <int NSW, class KEYS, class EMIT, bool HINT = false, bool MARK = false>
 __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit,
                                                uint32_t k2, uint32_t& thr_mask, uint32_t& thr_val,
                                                uint32_t hint_min = 0u, uint32_t hint_max = 0u) {
@@ -284,31 +286,38 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
     }
 
     // ---- selection in column order: one scan of (greater, equal) counts; the
-    // equal items taken before a thread are min(equal before it, need)
+    // equal items taken before a thread are min(equal before it, need).  The
+    // thread's selected items are a 16-bit mask, emitted by walking its set
+    // bits (a few per thread), not by a pass over all 16 items.
     uint32_t gt_base = 0u, eq_base = 0u;
     for (int s = 0; s < nsweep; ++s) {
         if (nsweep > 1) keys(s, u);
-        uint32_t n_gt = 0u, n_eq = 0u;
+        uint32_t gtm = 0u, eqm = 0u, mkm = 0u;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
             const uint32_t hi = u[i] & mask;
-            n_gt += u[i] != 0u && hi > prefix;
-            n_eq += u[i] != 0u && hi == prefix;
+            gtm |= (uint32_t)(u[i] != 0u && hi > prefix) << i;
+            eqm |= (uint32_t)(u[i] != 0u && hi == prefix) << i;
+            if (MARK) mkm |= (uint32_t)((u[i] & thr_mask) >= thr_val) << i;
         }
         uint32_t tot;
-        const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, sh.part[pb], tot);
+        const uint32_t ex = block_excl_scan(((uint32_t)__builtin_popcount(gtm) << 16) | (uint32_t)__builtin_popcount(eqm),
+                                            sh.part[pb], tot);
         pb ^= 1;
-        uint32_t eq_rank = eq_base + (ex & 0xFFFFu);
-        uint32_t pos = gt_base + (ex >> 16) + min(eq_rank, need);
+        const uint32_t eq_before = eq_base + (ex & 0xFFFFu);
+        uint32_t pos = gt_base + (ex >> 16) + min(eq_before, need);
+        // equal items: the first need - eq_before of this thread's, in column order
+        uint32_t selm = gtm;
+        for (uint32_t take = need > eq_before ? need - eq_before : 0u; eqm != 0u && take != 0u; --take) {
+            selm |= eqm & (0u - eqm);
+            eqm &= eqm - 1u;
+        }
         const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
-#pragma unroll
-        for (int i = 0; i < TK_ITEMS; ++i) {
-            const uint32_t hi = u[i] & mask;
-            const bool eq = u[i] != 0u && hi == prefix;
-            const bool sel = (u[i] != 0u && hi > prefix) || (eq && eq_rank < need);
-            eq_rank += eq;
-            if (sel) emit(c0 + i, pos, u[i]);
-            pos += sel;
+        while (selm != 0u) {
+            const int i = __builtin_ctz(selm);
+            selm &= selm - 1u;
+            emit(c0 + i, pos, (mkm >> i) & 1u);
+            ++pos;
         }
         gt_base += tot >> 16;
         eq_base += tot & 0xFFFFu;
@@ -424,6 +433,14 @@ __device__ __forceinline__ void load_block8(const float* brow, int nb, int sb, u
     for (int i = 0; i < 8; ++i) u[i] = (sb >= 0 && 8 * sb + i < nb) ? order_key(p[i]) : 0u;
 }
 
+// x0 for columns 0..7 of a thread's 16, x1 for columns 8..15: a bitwise
+// select (a ternary on the column, inside the loop over selected items, is
+// turned into a two-entry table in scratch memory)
+__device__ __forceinline__ int pick8(int col, int x0, int x1) {
+    const int m = -((col >> 3) & 1);
+    return (x0 & ~m) | (x1 & m);
+}
+
 __device__ __forceinline__ int col_id(const int32_t* pool, int c) {
     return pool ? 8 * pool[c >> 3] + (c & 7) : c;
 }
@@ -522,8 +539,8 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     // kept in the pool but marked (negative in LDS) and not read again.
     uint32_t thr_mask = 0u, thr_val = 0u;
     auto bkeys = [&](int s, uint32_t* u) { load_cols(brow, nb, s * TK_SWEEP + threadIdx.x * TK_ITEMS, u); };
-    auto bemit = [&](int col, uint32_t slot, uint32_t key) {
-        sh.pool[slot] = (key & thr_mask) >= thr_val ? col : (int32_t)((uint32_t)col | 0x80000000u);
+    auto bemit = [&](int col, uint32_t slot, uint32_t mark) {
+        sh.pool[slot] = mark ? col : (int32_t)((uint32_t)col | 0x80000000u);
     };
     if (!split && nb <= a.n_pool && nv <= TK_SWEEP) {
         // Every block is in the pool (blocks 0 .. nb-1, ascending; block
@@ -633,7 +650,7 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         };
         // positions go straight to the output row (the fallback below rewrites
         // every slot of it)
-        auto remit = [&](int col, uint32_t s2, uint32_t) { irow[s2] = 8 * ((col & 8) ? cb1 : cb0) + (col & 7); };
+        auto remit = [&](int col, uint32_t s2, uint32_t) { irow[s2] = 8 * pick8(col, cb0, cb1) + (col & 7); };
         // every present key lies in [thr_val, key_max] (no score exceeds the
         // largest block maximum) and kth_bin left the histogram clear
         uint32_t m2, v2;
@@ -654,7 +671,8 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         uint32_t m, vv;
         np = select_row<1>(sh, nb, a.k, bkeys, temit, 0u, m, vv);
     } else if (nb <= TK_SWEEP) {
-        np = select_row<1>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
+        np = select_row<1, decltype(bkeys), decltype(bemit), false, true>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k,
+                                                                         thr_mask, thr_val);
     } else if (PATH == SF_REG || nb <= 8 * TK_SWEEP) {
         // Longer rows, in registers: the top n_pool blocks lie in the top
         // n_pool super-blocks of 8 blocks ranked by their maximum (a super-
@@ -708,13 +726,15 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
             load_block8(brow, nb, sb0, u);
             load_block8(brow, nb, sb1, u + 8);
         };
-        auto cemit = [&](int col, uint32_t slot, uint32_t key) {
-            const int blk = 8 * ((col & 8) ? sb1 : sb0) + (col & 7);
-            sh.pool[slot] = (key & thr_mask) >= thr_val ? blk : (int32_t)((uint32_t)blk | 0x80000000u);
+        auto cemit = [&](int col, uint32_t slot, uint32_t mark) {
+            const int blk = 8 * pick8(col, sb0, sb1) + (col & 7);
+            sh.pool[slot] = mark ? blk : (int32_t)((uint32_t)blk | 0x80000000u);
         };
-        np = select_row<1>(sh, 8 * (int)nsp, a.n_pool, ckeys, cemit, (uint32_t)a.k, thr_mask, thr_val);
+        np = select_row<1, decltype(ckeys), decltype(cemit), false, true>(sh, 8 * (int)nsp, a.n_pool, ckeys, cemit,
+                                                                         (uint32_t)a.k, thr_mask, thr_val);
     } else {
-        np = select_row<0>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k, thr_mask, thr_val);
+        np = select_row<0, decltype(bkeys), decltype(bemit), false, true>(sh, nb, a.n_pool, bkeys, bemit, (uint32_t)a.k,
+                                                                         thr_mask, thr_val);
     }
     __syncthreads();                                  // the pool is complete in LDS
 
@@ -732,7 +752,7 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
     // candidate blocks have present keys, so the entries used are >= 0.
     const int pb0 = 2 * (int)threadIdx.x < (int)np ? 8 * (sh.pool[2 * threadIdx.x] & 0x7FFFFFFF) : 0;
     const int pb1 = 2 * (int)threadIdx.x + 1 < (int)np ? 8 * (sh.pool[2 * threadIdx.x + 1] & 0x7FFFFFFF) : 0;
-    auto pemit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)(((col & 8) ? pb1 : pb0) + (col & 7)); };
+    auto pemit = [&](int col, uint32_t slot, uint32_t) { sh.hist[slot] = (uint32_t)(pick8(col, pb0, pb1) + (col & 7)); };
     uint32_t thr2_mask, thr2_val;
     const uint32_t ni = select_row<1>(sh, ncols, a.k, pkeys, pemit, 0u, thr2_mask, thr2_val);
     __syncthreads();
