@@ -134,10 +134,15 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* part, 
 // HINT (one sweep only): every present key lies in [hint_min, hint_max] and
 // the histogram is already clear, so the opening count / min / max round is
 // skipped; the count of present keys comes from the first pass's histogram.
+//
+// nit (wave-uniform, one sweep only): items nit .. 15 of every thread of the
+// wave are absent, so the passes over a thread's items stop there (each
+// instruction a thread runs costs the workgroup 16 cycles of VALU issue).
 template <int NSW, class KEYS, class EMIT, bool HINT = false, bool MARK = false>
 __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, KEYS keys, EMIT emit,
                                                uint32_t k2, uint32_t& thr_mask, uint32_t& thr_val,
-                                               uint32_t hint_min = 0u, uint32_t hint_max = 0u) {
+                                               uint32_t hint_min = 0u, uint32_t hint_max = 0u,
+                                               int nit = TK_ITEMS) {
     static_assert(!HINT || NSW == 1, "a range hint is for keys held in registers");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsweep = NSW ? NSW : (ncols + TK_SWEEP - 1) / TK_SWEEP;
@@ -160,8 +165,10 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
         for (int s = 0; s < nsweep; ++s) {
             keys(s, u);
 #pragma unroll
-            for (int i = 0; i < TK_ITEMS; ++i)
+            for (int i = 0; i < TK_ITEMS; ++i) {
+                if (i >= nit) break;
                 if (u[i]) { cnt++; umin = min(umin, u[i]); umax = max(umax, u[i]); }
+            }
         }
         for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0u;
         cnt = __builtin_amdgcn_readlane(wave_incl_sum(cnt), 63);
@@ -204,12 +211,14 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
                     if (nsweep > 1) keys(s, u);
                     const int c0 = s * TK_SWEEP + threadIdx.x * TK_ITEMS;
 #pragma unroll
-                    for (int i = 0; i < TK_ITEMS; ++i)
+                    for (int i = 0; i < TK_ITEMS; ++i) {
+                        if (i >= nit) break;
                         if (u[i] != 0u && (u[i] & mask) == prefix) {
                             const uint32_t slot = atomicAdd(&sh.lcnt, 1u);
                             sh.lkey[slot] = u[i];
                             sh.lcol[slot] = c0 + i;
                         }
+                    }
                 }
                 __syncthreads();
                 const uint32_t nl = __builtin_amdgcn_readfirstlane(in_bin);
@@ -237,8 +246,10 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
             for (int s = 0; s < nsweep; ++s) {
                 if (nsweep > 1) keys(s, u);
 #pragma unroll
-                for (int i = 0; i < TK_ITEMS; ++i)
+                for (int i = 0; i < TK_ITEMS; ++i) {
+                    if (i >= nit) break;
                     if (u[i] != 0u && (u[i] & mask) == prefix) atomicAdd(&sh.hist[(u[i] >> shift) & dmask], 1u);
+                }
             }
             __syncthreads();
             // thread t owns the 4 bins 4095-4t .. 4092-4t (descending digits);
@@ -295,6 +306,7 @@ __device__ __forceinline__ uint32_t select_row(TkShared& sh, int ncols, int k, K
         uint32_t gtm = 0u, eqm = 0u, mkm = 0u;
 #pragma unroll
         for (int i = 0; i < TK_ITEMS; ++i) {
+            if (i >= nit) break;
             const uint32_t hi = u[i] & mask;
             gtm |= (uint32_t)(u[i] != 0u && hi > prefix) << i;
             eqm |= (uint32_t)(u[i] != 0u && hi == prefix) << i;
@@ -596,7 +608,8 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         // over 2 keys per thread instead of 16).
         // Wave w holds blocks 1024 w .. 1024 w + 1023; it lists its candidates
         // (ascending) in sh.pool[128 w ..] with a wave-level prefix sum and
-        // lane j gathers the scores of its list entries 2j and 2j + 1, so
+        // lane j gathers the scores of list entry j (a list of at most 64) or
+        // of entries 2j and 2j + 1, so
         // thread order then item order is position order and no workgroup-wide
         // step is needed before the positions' selection.  A wave with more
         // than 128 candidates (ties) raises its flag; the selection is then
@@ -629,11 +642,19 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int cb0 = 2 * lane < (int)wtot ? wlist[2 * lane] : -1;
-        const int cb1 = 2 * lane + 1 < (int)wtot ? wlist[2 * lane + 1] : -1;
+        // at most 64 candidates: one block per lane (items 0..7, the passes
+        // below stop after item 7); else two
+        const bool one = wtot <= 64u;
+        const int nit = one ? 8 : TK_ITEMS;
+        const int e0 = one ? lane : 2 * lane;
+        const int cb0 = e0 < (int)wtot ? wlist[e0] : -1;
+        const int cb1 = !one && e0 + 1 < (int)wtot ? wlist[e0 + 1] : -1;
         uint32_t v[TK_ITEMS];
 #pragma unroll
+        for (int i = 8; i < TK_ITEMS; ++i) v[i] = 0u;
+#pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if (h && one) break;
             const int cb = h ? cb1 : cb0;
             const float4* p = (const float4*)(srow + 8 * (cb >= 0 ? cb : 0));
             const float4 v0 = p[0], v1 = p[1];
@@ -655,7 +676,7 @@ __global__ __launch_bounds__(TK_THREADS) void select_full_kernel(SelectFullArgs 
         // largest block maximum) and kth_bin left the histogram clear
         uint32_t m2, v2;
         const uint32_t ni = select_row<1, decltype(rkeys), decltype(remit), true>(sh, TK_SWEEP, a.k, rkeys, remit, 0u,
-                                                                               m2, v2, thr_val, key_max);
+                                                                               m2, v2, thr_val, key_max, nit);
         // the flags were written before the selection's first barrier (its
         // first pass's)
         bool ovf_any = false;
